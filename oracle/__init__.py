@@ -1,0 +1,114 @@
+"""fp64 CPU oracle for causal multi-head attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The product library never loads it and
+shares no code with it.
+
+The arithmetic lives in ``attn_oracle.c`` (plain loops, fp64, the full score
+matrix of each head materialised); this module compiles it with gcc, loads
+it with ctypes and widens inputs to fp64 exactly. Passages followed: the
+"Hand-written Masked Multi-Head Attention CUDA kernel" page, sections 2,
+2.1 and 2.2 (definition, [B,S,H,D] layout, j <= i), and the "Week-4 CUDA
+notes" page, section 2.2 (unfused softmax(QK^T/sqrt(d))V, -inf mask, max
+subtraction).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+BUILD_CMD = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", _LIB, "-lm"]
+
+
+def build(force: bool = True) -> str:
+    """Compile ``liboracle.so`` next to its source (gcc, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        cmd = BUILD_CMD[:-3] + ["-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB)
+            dp = ctypes.POINTER(ctypes.c_double)
+            ip = ctypes.POINTER(ctypes.c_int32)
+            lib.oracle_attn_fwd_f64.argtypes = [dp, dp, dp, dp, dp] + [ctypes.c_int] * 6
+            lib.oracle_attn_fwd_f64.restype = ctypes.c_int
+            lib.oracle_attn_decode_f64.argtypes = [dp, dp, dp, ip, dp] + [ctypes.c_int] * 4
+            lib.oracle_attn_decode_f64.restype = ctypes.c_int
+            lib.oracle_num_threads.argtypes = []
+            lib.oracle_num_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _f64(x) -> np.ndarray:
+    """Exact widening to a C-contiguous float64 array (bf16/fp32 -> fp64 is exact)."""
+    if hasattr(x, "detach"):  # torch tensor
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def attn_fwd(q, k, v, causal: bool = True, return_p: bool = False):
+    """O = softmax(Q K^T / sqrt(D) + M) V in fp64.
+
+    q: [B, S_q, H, D]; k, v: [B, S_kv, H, D]. Returns O [B, S_q, H, D] (fp64
+    numpy) and, with ``return_p``, P [B, H, S_q, S_kv].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, S_q, H, D = q.shape
+    S_kv = k.shape[1]
+    if k.shape != (B, S_kv, H, D) or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    o = np.zeros((B, S_q, H, D), dtype=np.float64)
+    p = np.zeros((B, H, S_q, S_kv), dtype=np.float64) if return_p else None
+    rc = _load().oracle_attn_fwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                     _ptr(p) if p is not None else None,
+                                     B, H, S_q, S_kv, D, int(bool(causal)))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_fwd_f64 rejected the arguments (code {rc})")
+    return (o, p) if return_p else o
+
+
+def attn_decode(q, kcache, vcache, seqlens):
+    """Single-query decode: q [B,1,H,D], caches [B,S_cap,H,D], seqlens int32[B]."""
+    q, kc, vc = _f64(q), _f64(kcache), _f64(vcache)
+    B, _, H, D = q.shape
+    S_cap = kc.shape[1]
+    if hasattr(seqlens, "numpy"):
+        seqlens = seqlens.cpu().numpy()
+    sl = np.ascontiguousarray(seqlens, dtype=np.int32)
+    if sl.shape != (B,):
+        raise ValueError("seqlens must be int32[B]")
+    o = np.zeros((B, 1, H, D), dtype=np.float64)
+    rc = _load().oracle_attn_decode_f64(_ptr(q), _ptr(kc), _ptr(vc),
+                                        sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                        _ptr(o), B, H, S_cap, D)
+    if rc != 0:
+        raise ValueError(f"oracle_attn_decode_f64 rejected the arguments (code {rc})")
+    return o
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())

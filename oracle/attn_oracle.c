@@ -1,0 +1,180 @@
+/*
+ * attn_oracle.c -- fp64 CPU oracle for masked (causal) multi-head attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path links, loads or calls
+ * this file: only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg do. It shares no code, header, table or helper with the HIP library.
+ *
+ * What it computes is the plain definition, written out step by step:
+ *
+ *   S = Q K^T / sqrt(D)                       (all S_q x S_kv entries, fp64)
+ *   S[i][j] = -inf  where the causal mask hides key j from query i
+ *   P = softmax(S) row by row (subtract the row max, exp, divide by the sum)
+ *   O = P V
+ *
+ *   - definition and causal mask M (0 where visible, -inf elsewhere):
+ *     "Hand-written Masked Multi-Head Attention CUDA kernel" page, section 2
+ *     (its "O = AV^T" is read as O = A.V, the product the other pages use);
+ *   - key j visible to query i iff j <= i: same page, section 2.2;
+ *   - the unfused form softmax(QK^T/sqrt(d))V, masked positions set to -inf
+ *     so that exp gives exactly 0, and the subtraction of the row max:
+ *     "Week-4 CUDA notes" page, section 2.2;
+ *   - tensors are [B, S, H, D] row-major: MMHA page, section 2.1.
+ *
+ * Readings where the pages are silent (listed again in the design notes):
+ *   - the diagonal is visible (j <= i);
+ *   - when S_q != S_kv the queries are the LAST S_q positions of the key
+ *     sequence: query i sits at absolute position i + (S_kv - S_q), so key j
+ *     is visible iff j <= i + S_kv - S_q.  Causal with S_q > S_kv is rejected;
+ *   - no clamp of the running max (the MMHA page's section 2.3 clamp is not
+ *     part of the definition);
+ *   - decode: query b attends keys 0 .. len_b-1 of its cache; len_b <= 0 gives
+ *     an all-zero output row and len_b > S_cap is clamped to S_cap.
+ *
+ * The score matrix of one (b, h) is materialised in full (S_q*S_kv doubles),
+ * the three stages run as three separate passes over it, and OpenMP only
+ * splits the rows of a pass between threads; every value is computed by the
+ * same plain loop whatever the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL 1
+#define ORACLE_ENOMEM 2
+
+/* Element (b, s, h, d) of a [B, S, H, D] row-major tensor. */
+static size_t at(long b, long s, long h, long d, long S, long H, long D) {
+    return (size_t)(((b * S + s) * H + h) * D + d);
+}
+
+/*
+ * One (b, h) head: q rows i < S_q of a [*, S_qdim, H, D] tensor, keys/values
+ * j < S_kv of [*, S_kdim, H, D] tensors (S_kdim >= S_kv lets a KV cache of
+ * capacity S_kdim be used with S_kv valid tokens). p_out, when not NULL,
+ * receives the S_q x S_kv probability matrix of this head.
+ */
+static int oracle_head(const double* q, const double* k, const double* v, double* o,
+                       double* p_out, long b, long h, long H, long D,
+                       long S_q, long S_qdim, long S_kv, long S_kdim, int causal,
+                       double* S /* scratch, S_q*S_kv */) {
+    const double scale = 1.0 / sqrt((double)D);
+    const long off = S_kv - S_q; /* absolute position of query i is i + off */
+    long i;
+
+    /* Pass 1: scores S = Q K^T * scale, masked entries set to -inf. */
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < S_q; ++i) {
+        double* row = S + (size_t)i * (size_t)S_kv;
+        for (long j = 0; j < S_kv; ++j) {
+            if (causal && j > i + off) {
+                row[j] = -INFINITY;
+                continue;
+            }
+            double dot = 0.0;
+            for (long d = 0; d < D; ++d)
+                dot += q[at(b, i, h, d, S_qdim, H, D)] * k[at(b, j, h, d, S_kdim, H, D)];
+            row[j] = dot * scale;
+        }
+    }
+
+    /* Pass 2: softmax of each row: subtract the row max, exponentiate
+     * (exp(-inf) is exactly 0), divide by the row sum. */
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < S_q; ++i) {
+        double* row = S + (size_t)i * (size_t)S_kv;
+        double m = -INFINITY;
+        for (long j = 0; j < S_kv; ++j)
+            if (row[j] > m) m = row[j];
+        double l = 0.0;
+        for (long j = 0; j < S_kv; ++j) {
+            row[j] = exp(row[j] - m);
+            l += row[j];
+        }
+        for (long j = 0; j < S_kv; ++j) row[j] = row[j] / l;
+    }
+
+    /* Pass 3: O = P V. */
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < S_q; ++i) {
+        const double* row = S + (size_t)i * (size_t)S_kv;
+        for (long d = 0; d < D; ++d) {
+            double acc = 0.0;
+            for (long j = 0; j < S_kv; ++j) acc += row[j] * v[at(b, j, h, d, S_kdim, H, D)];
+            o[at(b, i, h, d, S_qdim, H, D)] = acc;
+        }
+    }
+
+    if (p_out) {
+        double* dst = p_out + (size_t)(b * H + h) * (size_t)S_q * (size_t)S_kv;
+        memcpy(dst, S, sizeof(double) * (size_t)S_q * (size_t)S_kv);
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Prefill / general forward.
+ *   q, o : [B, S_q, H, D];  k, v : [B, S_kv, H, D];  fp64, row-major.
+ *   p    : optional [B, H, S_q, S_kv] probabilities (NULL to skip).
+ * Returns ORACLE_EINVAL for a non-positive size, causal with S_q > S_kv, or a
+ * causal flag other than 0/1; ORACLE_ENOMEM if the score matrix cannot be
+ * allocated.
+ */
+int oracle_attn_fwd_f64(const double* q, const double* k, const double* v, double* o,
+                        double* p, int B, int H, int S_q, int S_kv, int D, int causal) {
+    if (B <= 0 || H <= 0 || S_q <= 0 || S_kv <= 0 || D <= 0) return ORACLE_EINVAL;
+    if (causal != 0 && causal != 1) return ORACLE_EINVAL;
+    if (causal && S_q > S_kv) return ORACLE_EINVAL;
+    double* S = (double*)malloc(sizeof(double) * (size_t)S_q * (size_t)S_kv);
+    if (!S) return ORACLE_ENOMEM;
+    for (long b = 0; b < B; ++b)
+        for (long h = 0; h < H; ++h)
+            oracle_head(q, k, v, o, p, b, h, H, D, S_q, S_q, S_kv, S_kv, causal, S);
+    free(S);
+    return ORACLE_OK;
+}
+
+/*
+ * Single-query decode against a KV cache.
+ *   q, o            : [B, 1, H, D]
+ *   kcache, vcache  : [B, S_cap, H, D]
+ *   seqlens         : int32[B]; query b sees cache slots 0 .. len_b-1.
+ * len_b <= 0 writes a zero row; len_b > S_cap is treated as S_cap. Slots at
+ * or beyond len_b are never read. This is the forward above with S_q = 1 and
+ * S_kv = len_b (causal or not makes no difference for one query that is the
+ * last position).
+ */
+int oracle_attn_decode_f64(const double* q, const double* kcache, const double* vcache,
+                           const int32_t* seqlens, double* o, int B, int H, int S_cap, int D) {
+    if (B <= 0 || H <= 0 || S_cap <= 0 || D <= 0) return ORACLE_EINVAL;
+    double* S = (double*)malloc(sizeof(double) * (size_t)S_cap);
+    if (!S) return ORACLE_ENOMEM;
+    for (long b = 0; b < B; ++b) {
+        long n = seqlens[b];
+        if (n > S_cap) n = S_cap;
+        for (long h = 0; h < H; ++h) {
+            if (n <= 0) {
+                for (long d = 0; d < D; ++d) o[at(b, 0, h, d, 1, H, D)] = 0.0;
+                continue;
+            }
+            oracle_head(q, kcache, vcache, o, NULL, b, h, H, D, 1, 1, n, S_cap, 1, S);
+        }
+    }
+    free(S);
+    return ORACLE_OK;
+}
+
+/* Threads the OpenMP runtime will use for the passes above (1 without OpenMP). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,285 @@
+"""Pins for the fp64 oracle: it is checked against things other than itself.
+
+Each test names the passage or the mathematical fact it relies on. The
+oracle follows the "Hand-written Masked Multi-Head Attention CUDA kernel"
+page (section 2: A = softmax(QK^T/sqrt(d_k) + M), O = A.V; section 2.1:
+[B,S,H,D] layout; section 2.2: key j visible iff j <= i) and the "Week-4
+CUDA notes" page, section 2.2 (-inf mask gives exp = 0; subtract the max).
+
+What each kind of mistake would trip:
+  dropped or wrong scale, transposed operand, wrong stride  -> library and golden pins
+  diagonal hidden or mask off by one                        -> row-0, golden, masked-zero pins
+  wrong S_q != S_kv alignment                               -> golden bottom-right case
+  missing normalisation / max subtraction overflow          -> row sums, large-logit test
+  decode reading past the length                            -> NaN-filled cache test
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "geometric_weights.json")
+
+
+def rnd(seed, *shape, std=1.0):
+    g = np.random.default_rng(seed)
+    return g.standard_normal(shape) * std
+
+
+def sdpa_f64(q, k, v, causal):
+    """torch's scaled_dot_product_attention on the CPU in float64.
+
+    For causal with S_q != S_kv the mask is passed explicitly as a boolean
+    matrix (visible iff j <= i + S_kv - S_q) because torch's is_causal aligns
+    top-left.
+    """
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k).permute(0, 2, 1, 3)
+    vt = torch.from_numpy(v).permute(0, 2, 1, 3)
+    S_q, S_kv = q.shape[1], k.shape[1]
+    if causal and S_q == S_kv:
+        o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    elif causal:
+        i = torch.arange(S_q)[:, None]
+        j = torch.arange(S_kv)[None, :]
+        mask = j <= i + (S_kv - S_q)
+        o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+    else:
+        o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)
+    return o.permute(0, 2, 1, 3).contiguous().numpy()
+
+
+# --------------------------------------------------------------------------
+# Library special case: torch SDPA in float64
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("B,H,S_q,S_kv,D,causal", [
+    (1, 1, 1, 1, 8, True),
+    (1, 2, 64, 64, 32, True),
+    (2, 3, 37, 37, 16, True),
+    (2, 2, 19, 53, 64, True),      # chunked prefill: queries are the last 19 positions
+    (1, 2, 1, 70, 128, True),      # one query at the end = decode
+    (2, 2, 33, 47, 32, False),
+    (1, 1, 130, 130, 128, True),
+])
+def test_matches_sdpa_float64(B, H, S_q, S_kv, D, causal):
+    q = rnd(1, B, S_q, H, D)
+    k = rnd(2, B, S_kv, H, D)
+    v = rnd(3, B, S_kv, H, D)
+    got = oracle.attn_fwd(q, k, v, causal)
+    ref = sdpa_f64(q, k, v, causal)
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+# --------------------------------------------------------------------------
+# Exact closed forms (tests/golden/geometric_weights.json, written from
+# fractions by tests/golden/make_golden.py, not by the oracle)
+# --------------------------------------------------------------------------
+def test_golden_geometric_weights():
+    doc = json.load(open(GOLDEN))
+    assert "section 2" in doc["citation"]
+    for case in doc["cases"]:
+        q = np.array(case["q"], dtype=np.float64)
+        k = np.array(case["k"], dtype=np.float64)
+        v = np.array(case["v"], dtype=np.float64)
+        exact = np.vectorize(lambda s: float(Fraction(s)))(np.array(case["o_exact"], dtype=object))
+        got = oracle.attn_fwd(q, k, v, case["causal"])
+        assert got.shape == exact.shape
+        np.testing.assert_allclose(got, exact.astype(np.float64), rtol=1e-13, atol=1e-14,
+                                   err_msg=case["name"])
+
+
+def test_two_keys_is_a_logistic_blend():
+    """Two visible keys: weight of key 1 is 1/(1+exp(-(s1-s0))) (sigmoid)."""
+    D = 1  # scale 1
+    q = np.array([[[[0.7]], [[-1.3]]]])              # [1, 2, 1, 1]
+    k = np.array([[[[0.5]], [[2.0]]]])
+    v = np.array([[[[3.0]], [[-5.0]]]])
+    o = oracle.attn_fwd(q, k, v, causal=True)
+    assert o[0, 0, 0, 0] == 3.0
+    w1 = 1.0 / (1.0 + math.exp(-(-1.3 * 2.0 - (-1.3 * 0.5))))
+    assert abs(o[0, 1, 0, 0] - (3.0 * (1 - w1) + -5.0 * w1)) <= 1e-15
+    del D
+
+
+# --------------------------------------------------------------------------
+# Brute force in pure Python, log-sum-exp formulation with exact summation
+# --------------------------------------------------------------------------
+def brute_force(q, k, v, causal):
+    B, S_q, H, D = q.shape
+    S_kv = k.shape[1]
+    off = S_kv - S_q
+    out = np.zeros_like(q)
+    for b in range(B):
+        for h in range(H):
+            for i in range(S_q):
+                vis = [j for j in range(S_kv) if not causal or j <= i + off]
+                s = [math.fsum(q[b, i, h, d] * k[b, j, h, d] for d in range(D)) / math.sqrt(D)
+                     for j in vis]
+                top = max(s)
+                lse = top + math.log(math.fsum(math.exp(x - top) for x in s))
+                w = [math.exp(x - lse) for x in s]
+                for d in range(D):
+                    out[b, i, h, d] = math.fsum(wj * v[b, j, h, d] for wj, j in zip(w, vis))
+    return out
+
+
+@pytest.mark.parametrize("B,H,S_q,S_kv,D,causal", [
+    (1, 1, 5, 5, 3, True), (2, 2, 7, 7, 4, True), (1, 3, 4, 9, 8, True),
+    (2, 1, 6, 6, 5, False), (1, 2, 16, 16, 8, True),
+])
+def test_brute_force_tiny(B, H, S_q, S_kv, D, causal):
+    q = rnd(11, B, S_q, H, D, std=2.0)
+    k = rnd(12, B, S_kv, H, D, std=2.0)
+    v = rnd(13, B, S_kv, H, D)
+    got = oracle.attn_fwd(q, k, v, causal)
+    assert np.max(np.abs(got - brute_force(q, k, v, causal))) <= 1e-13
+
+
+# --------------------------------------------------------------------------
+# Invariants
+# --------------------------------------------------------------------------
+def test_rows_sum_to_one_and_masked_entries_are_exactly_zero():
+    B, H, S_q, S_kv, D = 2, 3, 40, 57, 16
+    q, k, v = rnd(21, B, S_q, H, D, std=3), rnd(22, B, S_kv, H, D, std=3), rnd(23, B, S_kv, H, D)
+    _, p = oracle.attn_fwd(q, k, v, causal=True, return_p=True)
+    assert np.max(np.abs(p.sum(-1) - 1.0)) <= 1e-12
+    i = np.arange(S_q)[:, None]
+    j = np.arange(S_kv)[None, :]
+    masked = np.broadcast_to(j > i + (S_kv - S_q), p.shape)
+    assert np.all(p[masked] == 0.0)
+    assert np.all(p[~masked] > 0.0)
+
+
+def test_row_zero_returns_value_row_zero_exactly():
+    B, H, S, D = 2, 4, 33, 32
+    q, k, v = rnd(31, B, S, H, D), rnd(32, B, S, H, D), rnd(33, B, S, H, D)
+    o = oracle.attn_fwd(q, k, v, causal=True)
+    assert np.array_equal(o[:, 0], v[:, 0])
+
+
+def test_equal_keys_give_prefix_means():
+    """All keys equal -> uniform weights over the visible prefix -> O_i = mean(V_0..V_i)."""
+    B, H, S, D = 1, 2, 50, 8
+    q = rnd(41, B, S, H, D)
+    k = np.broadcast_to(rnd(42, B, 1, H, D), (B, S, H, D)).copy()
+    v = rnd(43, B, S, H, D)
+    o = oracle.attn_fwd(q, k, v, causal=True)
+    prefix = np.cumsum(v, axis=1) / np.arange(1, S + 1)[None, :, None, None]
+    assert np.max(np.abs(o - prefix)) <= 1e-13
+
+
+def test_constant_values_pass_through():
+    B, H, S, D = 1, 2, 31, 16
+    q, k = rnd(51, B, S, H, D, std=4), rnd(52, B, S, H, D, std=4)
+    c = rnd(53, 1, 1, H, D)
+    v = np.broadcast_to(c, (B, S, H, D)).copy()
+    o = oracle.attn_fwd(q, k, v, causal=True)
+    assert np.max(np.abs(o - v)) <= 1e-14
+
+
+def test_shift_of_all_keys_leaves_output_unchanged():
+    """k_j + c for one c: every score of row i moves by q_i.c/sqrt(D); softmax ignores it."""
+    B, H, S, D = 1, 2, 45, 32
+    q, k, v = rnd(61, B, S, H, D), rnd(62, B, S, H, D), rnd(63, B, S, H, D)
+    c = rnd(64, 1, 1, H, D, std=3.0)
+    o1 = oracle.attn_fwd(q, k, v, causal=True)
+    o2 = oracle.attn_fwd(q, k + c, v, causal=True)
+    assert np.max(np.abs(o1 - o2)) <= 1e-12
+
+
+def test_large_logits_stay_finite_and_match_lse_brute_force():
+    """Logits with spreads in the thousands overflow exp unless the row max is subtracted."""
+    B, H, S, D = 1, 1, 12, 4
+    q, k, v = rnd(71, B, S, H, D, std=30), rnd(72, B, S, H, D, std=30), rnd(73, B, S, H, D)
+    o = oracle.attn_fwd(q, k, v, causal=True)
+    assert np.all(np.isfinite(o))
+    assert np.max(np.abs(o - brute_force(q, k, v, True))) <= 1e-12
+
+
+def test_causal_prefix_consistency_is_exact():
+    B, H, S, D = 1, 2, 60, 16
+    q, k, v = rnd(81, B, S, H, D), rnd(82, B, S, H, D), rnd(83, B, S, H, D)
+    full = oracle.attn_fwd(q, k, v, causal=True)
+    for Sp in (1, 17, 59):
+        part = oracle.attn_fwd(q[:, :Sp], k[:, :Sp], v[:, :Sp], causal=True)
+        assert np.array_equal(full[:, :Sp], part)
+
+
+def test_non_causal_key_permutation_invariance():
+    B, H, S_q, S_kv, D = 1, 2, 9, 23, 8
+    q, k, v = rnd(91, B, S_q, H, D), rnd(92, B, S_kv, H, D), rnd(93, B, S_kv, H, D)
+    perm = np.random.default_rng(5).permutation(S_kv)
+    o1 = oracle.attn_fwd(q, k, v, causal=False)
+    o2 = oracle.attn_fwd(q, k[:, perm], v[:, perm], causal=False)
+    assert np.max(np.abs(o1 - o2)) <= 1e-14
+
+
+def test_heads_and_batches_are_independent():
+    B, H, S, D = 2, 3, 20, 8
+    q, k, v = rnd(101, B, S, H, D), rnd(102, B, S, H, D), rnd(103, B, S, H, D)
+    o1 = oracle.attn_fwd(q, k, v, causal=True)
+    k2, v2 = k.copy(), v.copy()
+    k2[1, :, 2] += 5.0
+    v2[1, :, 2] *= -3.0
+    o2 = oracle.attn_fwd(q, k2, v2, causal=True)
+    changed = np.zeros_like(o1, dtype=bool)
+    changed[1, :, 2] = True
+    assert np.array_equal(o1[~changed], o2[~changed])
+    assert not np.allclose(o1[changed], o2[changed])
+
+
+# --------------------------------------------------------------------------
+# Decode: the S_q = 1 special case of the forward, never reading past len
+# --------------------------------------------------------------------------
+def test_decode_equals_forward_with_one_query_and_ignores_slots_past_len():
+    B, H, S_cap, D = 4, 3, 40, 16
+    seqlens = np.array([1, 17, 40, 5], dtype=np.int32)
+    q, kc, vc = rnd(111, B, 1, H, D), rnd(112, B, S_cap, H, D), rnd(113, B, S_cap, H, D)
+    for b in range(B):
+        kc[b, seqlens[b]:] = np.nan
+        vc[b, seqlens[b]:] = np.nan
+    o = oracle.attn_decode(q, kc, vc, seqlens)
+    assert np.all(np.isfinite(o))
+    for b in range(B):
+        n = seqlens[b]
+        ref = oracle.attn_fwd(q[b:b + 1], kc[b:b + 1, :n], vc[b:b + 1, :n], causal=True)
+        assert np.array_equal(o[b:b + 1], ref)
+        ref2 = sdpa_f64(q[b:b + 1], kc[b:b + 1, :n], vc[b:b + 1, :n], causal=False)
+        assert np.max(np.abs(o[b:b + 1] - ref2)) <= 1e-12
+    assert np.array_equal(o[0, 0], vc[0, 0])  # one key: the value row itself
+
+
+def test_decode_empty_and_overlong_lengths():
+    B, H, S_cap, D = 3, 2, 10, 8
+    q, kc, vc = rnd(121, B, 1, H, D), rnd(122, B, S_cap, H, D), rnd(123, B, S_cap, H, D)
+    o = oracle.attn_decode(q, kc, vc, np.array([0, -4, 99], dtype=np.int32))
+    assert np.all(o[0] == 0.0) and np.all(o[1] == 0.0)
+    full = oracle.attn_decode(q, kc, vc, np.array([10, 10, 10], dtype=np.int32))
+    assert np.array_equal(o[2], full[2])
+
+
+def test_rejects_invalid_arguments():
+    q = rnd(1, 1, 4, 1, 8)
+    with pytest.raises(ValueError):
+        oracle.attn_fwd(q, q[:, :2], q[:, :2], causal=True)   # causal with S_q > S_kv
+
+
+# --------------------------------------------------------------------------
+# The workloads themselves (shapes and the decode lengths the recipe fixes)
+# --------------------------------------------------------------------------
+def test_workload_recipe():
+    sl, q, kc, vc = workloads.make_decode(workloads.BF16_DECODE, S_cap=8)
+    assert sl.tolist() == [1764, 1316, 2324, 1626, 376, 361, 133, 372, 1003, 3498, 32, 479,
+                           3036, 3120, 1054, 3810]
+    assert q.dtype == torch.bfloat16 and kc.shape == (16, 8, 32, 128)
+    assert workloads.BF16_S2048.flops() == 34_376_515_584
+    assert workloads.BF16_S4096.flops() == 137_472_507_904
+    assert workloads.FP32_TINY.flops() == 532_480
+    assert workloads.decode_kv_bytes(sl.tolist(), 32, 128, 2, 4096) == 398_196_736 + 262_144

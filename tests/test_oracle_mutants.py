@@ -1,0 +1,91 @@
+"""The oracle's pins must catch plausible mistakes planted in the oracle.
+
+Each case compiles a copy of ``oracle/attn_oracle.c`` with one edit (a
+dropped scale, a diagonal hidden, a transposed layout, ...) into a temporary
+directory, points the oracle module at it and checks that at least one pin
+of ``test_oracle.py`` fails. Runs on the CPU only; the real oracle is never
+modified.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import test_oracle as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
+
+MUTANTS = {
+    "diagonal_hidden": ("if (causal && j > i + off)", "if (causal && j >= i + off)"),
+    "alignment_top_left": ("const long off = S_kv - S_q;", "const long off = 0;"),
+    "alignment_sign": ("const long off = S_kv - S_q;", "const long off = S_q - S_kv;"),
+    "mask_ignored": ("if (causal && j > i + off)", "if (0 && j > i + off)"),
+    "scale_dropped": ("row[j] = dot * scale;", "row[j] = dot;"),
+    "scale_is_1_over_d": ("1.0 / sqrt((double)D)", "1.0 / (double)D"),
+    "values_replaced_by_keys": ("acc += row[j] * v[", "acc += row[j] * k["),
+    "no_normalisation": ("for (long j = 0; j < S_kv; ++j) row[j] = row[j] / l;", ""),
+    "no_max_subtraction": ("row[j] = exp(row[j] - m);", "row[j] = exp(row[j]);"),
+    "layout_bhsd": ("return (size_t)(((b * S + s) * H + h) * D + d);",
+                    "return (size_t)(((b * H + h) * S + s) * D + d);"),
+    "decode_reads_full_cache": ("if (n > S_cap) n = S_cap;", "n = S_cap;"),
+    "query_key_swapped": ("dot += q[at(b, i, h, d, S_qdim, H, D)] * k[at(b, j, h, d, S_kdim, H, D)];",
+                          "dot += q[at(b, i, h, d, S_qdim, H, D)] * q[at(b, j % S_q, h, d, S_qdim, H, D)];"),
+    "max_over_first_key_only": ("if (row[j] > m) m = row[j];", "if (j == 0) m = row[j];"),
+}
+
+PINS = [
+    lambda: pins.test_matches_sdpa_float64(2, 2, 19, 53, 64, True),
+    lambda: pins.test_matches_sdpa_float64(2, 3, 37, 37, 16, True),
+    lambda: pins.test_matches_sdpa_float64(2, 2, 33, 47, 32, False),
+    pins.test_golden_geometric_weights,
+    pins.test_two_keys_is_a_logistic_blend,
+    lambda: pins.test_brute_force_tiny(1, 3, 4, 9, 8, True),
+    pins.test_rows_sum_to_one_and_masked_entries_are_exactly_zero,
+    pins.test_row_zero_returns_value_row_zero_exactly,
+    pins.test_equal_keys_give_prefix_means,
+    pins.test_constant_values_pass_through,
+    pins.test_large_logits_stay_finite_and_match_lse_brute_force,
+    pins.test_decode_equals_forward_with_one_query_and_ignores_slots_past_len,
+    pins.test_decode_empty_and_overlong_lengths,
+]
+
+
+def _compile(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) >= 1, f"mutation anchor for {name} not found"
+    src = tmp_path / f"{name}.c"
+    src.write_text(text.replace(old, new))
+    lib = tmp_path / f"{name}.so"
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", str(src), "-o",
+                    str(lib), "-lm"], check=True)
+    return str(lib)
+
+
+def _failures():
+    failed = 0
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, ValueError):
+            failed += 1
+    return failed
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert _failures() == 0
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path, monkeypatch):
+    real = oracle._load()
+    path = _compile(tmp_path, name, *MUTANTS[name])
+    mutant = ctypes.CDLL(path)
+    for fn in ("oracle_attn_fwd_f64", "oracle_attn_decode_f64", "oracle_num_threads"):
+        f, g = getattr(mutant, fn), getattr(real, fn)
+        f.argtypes, f.restype = g.argtypes, g.restype
+    monkeypatch.setattr(oracle, "_lib", mutant)
+    assert _failures() >= 1, f"no pin catches mutant {name}"

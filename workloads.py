@@ -1,0 +1,144 @@
+"""Seeded synthetic inputs for causal multi-head attention.
+
+This module is shared by the tests, the benchmark and the oracle checks. It
+holds shapes, seeds and random draws only: none of the attention arithmetic
+lives here, so neither the GPU path nor the oracle depends on the other
+through it.
+
+Layout of every tensor is ``[B, S, H, D]`` row-major, the (batch, sequence,
+heads, head_dim) layout the Masked Multi-Head Attention page fixes in its
+section 2.1 (tensors flattened to ``(B*S, H*D)`` rows).
+
+The five workloads:
+
+* ``fp32_tiny``     fp32, B=1, H=2,  S=64,   D=32,  causal, N(0,1)
+* ``fp32_small``    fp32, B=2, H=8,  S=512,  D=64,  causal, N(0,1)
+* ``bf16_s2048``    bf16, B=1, H=32, S=2048, D=128, causal, N(0,1)
+                    (hidden 4096: the LLaMA-7B layer shape of the MMHA page, section 1)
+* ``bf16_s4096``    bf16, B=1, H=32, S=4096, D=128, causal, Q,K ~ N(0, 4^2),
+                    V ~ N(0,1) (logits reach about +-100: stability stress)
+* ``bf16_decode``   bf16 decode, B=16 sequences, one query each, H=32, D=128,
+                    KV-cache capacity 4096, lengths uniform in [1, 4096]
+
+Generator: a torch CPU ``Generator`` seeded with ``1000 + index`` (1001..1005).
+Prefill draws q, k, v in that order as ``randn(B,S,H,D) * std``; decode draws
+the lengths first, then q, the K cache and the V cache. bf16 tensors are the
+round-to-nearest-even cast of the fp32 draw (``Tensor.to(torch.bfloat16)``).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Prefill:
+    name: str
+    dtype: torch.dtype
+    B: int
+    H: int
+    S_q: int
+    S_kv: int
+    D: int
+    causal: bool
+    seed: int
+    qk_std: float = 1.0
+    v_std: float = 1.0
+
+    def flops(self) -> int:
+        """Algorithmic FLOP: 4*B*H*D per visible (query, key) pair.
+
+        Two multiply-adds (QK^T and P.V) per visible pair; masked pairs and the
+        softmax exponentials are not counted.
+        """
+        return 4 * self.B * self.H * self.D * visible_pairs(self.S_q, self.S_kv, self.causal)
+
+
+@dataclass(frozen=True)
+class Decode:
+    name: str
+    dtype: torch.dtype
+    B: int
+    H: int
+    S_cap: int
+    D: int
+    seed: int
+    len_lo: int = 1
+    len_hi: int = 4096
+
+
+def visible_pairs(S_q: int, S_kv: int, causal: bool) -> int:
+    """Number of (i, j) pairs a query sees (bottom-right causal alignment)."""
+    if not causal:
+        return S_q * S_kv
+    off = S_kv - S_q
+    return sum(min(S_kv, i + 1 + off) for i in range(S_q))
+
+
+FP32_TINY = Prefill("fp32_tiny", torch.float32, 1, 2, 64, 64, 32, True, 1001)
+FP32_SMALL = Prefill("fp32_small", torch.float32, 2, 8, 512, 512, 64, True, 1002)
+BF16_S2048 = Prefill("bf16_s2048", torch.bfloat16, 1, 32, 2048, 2048, 128, True, 1003)
+BF16_S4096 = Prefill("bf16_s4096", torch.bfloat16, 1, 32, 4096, 4096, 128, True, 1004,
+                     qk_std=4.0, v_std=1.0)
+BF16_DECODE = Decode("bf16_decode", torch.bfloat16, 16, 32, 4096, 128, 1005)
+
+PREFILL_CONFIGS = (FP32_TINY, FP32_SMALL, BF16_S2048, BF16_S4096)
+
+
+def make_prefill(cfg: Prefill, device: str | torch.device = "cpu"):
+    """Draw (q, k, v) for a prefill workload; CPU draw, then optional copy."""
+    g = torch.Generator().manual_seed(cfg.seed)
+    q = torch.randn(cfg.B, cfg.S_q, cfg.H, cfg.D, generator=g) * cfg.qk_std
+    k = torch.randn(cfg.B, cfg.S_kv, cfg.H, cfg.D, generator=g) * cfg.qk_std
+    v = torch.randn(cfg.B, cfg.S_kv, cfg.H, cfg.D, generator=g) * cfg.v_std
+    out = tuple(t.to(cfg.dtype).contiguous() for t in (q, k, v))
+    if str(device) != "cpu":
+        out = tuple(t.to(device) for t in out)
+    return out
+
+
+def make_prefill_shape(seed: int, dtype: torch.dtype, B: int, H: int, S_q: int, S_kv: int,
+                       D: int, qk_std: float = 1.0, v_std: float = 1.0):
+    """Same recipe as :func:`make_prefill` for an arbitrary (edge-case) shape."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, S_q, H, D, generator=g) * qk_std
+    k = torch.randn(B, S_kv, H, D, generator=g) * qk_std
+    v = torch.randn(B, S_kv, H, D, generator=g) * v_std
+    return tuple(t.to(dtype).contiguous() for t in (q, k, v))
+
+
+def make_decode(cfg: Decode, nan_fill: bool = False, seqlens=None, S_cap: int | None = None,
+                B: int | None = None):
+    """Draw (seqlens, q, kcache, vcache) on the CPU.
+
+    ``seqlens`` is int32[B] drawn uniform in [len_lo, len_hi] unless given.
+    With ``nan_fill`` every cache slot at or beyond a sequence's length holds
+    NaN, so any read past the valid prefix shows up in the output.
+    """
+    B = cfg.B if B is None else B
+    S_cap = cfg.S_cap if S_cap is None else S_cap
+    g = torch.Generator().manual_seed(cfg.seed)
+    drawn = torch.randint(cfg.len_lo, cfg.len_hi + 1, (B,), generator=g, dtype=torch.int32)
+    if seqlens is None:
+        seqlens = drawn
+    else:
+        seqlens = torch.as_tensor(seqlens, dtype=torch.int32)
+    q = torch.randn(B, 1, cfg.H, cfg.D, generator=g).to(cfg.dtype)
+    kc = torch.randn(B, S_cap, cfg.H, cfg.D, generator=g).to(cfg.dtype)
+    vc = torch.randn(B, S_cap, cfg.H, cfg.D, generator=g).to(cfg.dtype)
+    if nan_fill:
+        for b in range(B):
+            n = max(0, min(int(seqlens[b]), S_cap))
+            kc[b, n:] = float("nan")
+            vc[b, n:] = float("nan")
+    return seqlens, q.contiguous(), kc.contiguous(), vc.contiguous()
+
+
+def decode_kv_bytes(seqlens, H: int, D: int, elem_bytes: int, S_cap: int) -> int:
+    """Algorithmic decode traffic: K and V rows of every valid token, plus q and o."""
+    total = 0
+    for n in seqlens:
+        total += max(0, min(int(n), S_cap))
+    B = len(seqlens)
+    return total * H * D * 2 * elem_bytes + 2 * B * H * D * elem_bytes
