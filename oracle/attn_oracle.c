@@ -100,14 +100,18 @@ static int oracle_head(const double* q, const double* k, const double* v, double
         for (long j = 0; j < S_kv; ++j) row[j] = row[j] / l;
     }
 
-    /* Pass 3: O = P V. */
+    /* Pass 3: O = P V. Each output element is the sum over j = 0, 1, ...
+     * S_kv-1 in that order; the j loop is outside the d loop only so that
+     * value rows are read contiguously. */
 #pragma omp parallel for schedule(static)
     for (i = 0; i < S_q; ++i) {
         const double* row = S + (size_t)i * (size_t)S_kv;
-        for (long d = 0; d < D; ++d) {
-            double acc = 0.0;
-            for (long j = 0; j < S_kv; ++j) acc += row[j] * v[at(b, j, h, d, S_kdim, H, D)];
-            o[at(b, i, h, d, S_qdim, H, D)] = acc;
+        double* out = o + at(b, i, h, 0, S_qdim, H, D);
+        for (long d = 0; d < D; ++d) out[d] = 0.0;
+        for (long j = 0; j < S_kv; ++j) {
+            const double pj = row[j];
+            const double* vrow = v + at(b, j, h, 0, S_kdim, H, D);
+            for (long d = 0; d < D; ++d) out[d] += pj * vrow[d];
         }
     }
 

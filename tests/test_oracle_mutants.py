@@ -25,7 +25,7 @@ MUTANTS = {
     "mask_ignored": ("if (causal && j > i + off)", "if (0 && j > i + off)"),
     "scale_dropped": ("row[j] = dot * scale;", "row[j] = dot;"),
     "scale_is_1_over_d": ("1.0 / sqrt((double)D)", "1.0 / (double)D"),
-    "values_replaced_by_keys": ("acc += row[j] * v[", "acc += row[j] * k["),
+    "values_replaced_by_keys": ("const double* vrow = v + at(", "const double* vrow = k + at("),
     "no_normalisation": ("for (long j = 0; j < S_kv; ++j) row[j] = row[j] / l;", ""),
     "no_max_subtraction": ("row[j] = exp(row[j] - m);", "row[j] = exp(row[j]);"),
     "layout_bhsd": ("return (size_t)(((b * S + s) * H + h) * D + d);",
