@@ -1,0 +1,173 @@
+"""Causal multi-head attention for MI355X (gfx950): Python binding of libattn.so.
+
+Argument marshalling only. Every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/attn.h``; this module checks
+tensors (device, dtype, layout), passes their device pointers and the current
+torch stream, and turns status codes into exceptions. There is no CPU or
+PyTorch fallback: if ``libattn.so`` is missing the import fails.
+
+    o = attn_fwd(q, k, v, causal=True)                      # [B, S, H, D]
+    o = attn_decode(q, kcache, vcache, seqlens)             # q [B, 1, H, D]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_F32, ATTN_BF16, ATTN_F16 = 0, 1, 2
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = 0, 1, 2, 3, 4
+
+_DTYPES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_status_name(status)}: {msg}")
+        self.status = status
+
+
+class FwdPlan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("kernel", "block_m", "block_n", "paired", "grid", "threads",
+                                           "lds_bytes", "max_tiles", "min_tiles")]
+
+
+class DecodePlan(ctypes.Structure):
+    _fields_ = [("chunk", ctypes.c_int), ("n_split_max", ctypes.c_int), ("threads", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m causal_head_attention_amd.build` "
+                          "(hipcc, gfx950). There is no fallback implementation.")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i]
+    lib.attn_fwd.restype = i
+    lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
+    lib.attn_decode_workspace_bytes.restype = sz
+    lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, sz]
+    lib.attn_decode.restype = i
+    lib.attn_set_stream.argtypes = [vp]
+    lib.attn_set_stream.restype = i
+    lib.attn_get_stream.argtypes = []
+    lib.attn_get_stream.restype = vp
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [i]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_fwd_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(FwdPlan)]
+    lib.attn_fwd_plan.restype = i
+    lib.attn_decode_plan.argtypes = [i, i, i, i, i, ctypes.POINTER(DecodePlan)]
+    lib.attn_decode_plan.restype = i
+    lib.attn_xcd_remap.argtypes = [i, i]
+    lib.attn_xcd_remap.restype = i
+    return lib
+
+
+lib = _load()
+
+
+def _status_name(status: int) -> str:
+    return lib.attn_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != ATTN_OK:
+        raise AttnError(status, lib.attn_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+    return _DTYPES[t.dtype]
+
+
+def _dev_tensor(name: str, t: torch.Tensor, dim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous ([B, S, H, D] row-major)")
+
+
+def _set_stream(device: torch.device) -> None:
+    _check(lib.attn_set_stream(ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)))
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None,
+             causal: bool = True) -> torch.Tensor:
+    """Fused masked attention forward. q [B,S_q,H,D]; k, v [B,S_kv,H,D]; returns o [B,S_q,H,D]."""
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(n, t, 4)
+    B, S_q, H, D = q.shape
+    S_kv = k.shape[1]
+    if tuple(k.shape) != (B, S_kv, H, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if o is None:
+        o = torch.empty_like(q)
+    else:
+        _dev_tensor("o", o, 4)
+        if tuple(o.shape) != tuple(q.shape) or o.dtype != q.dtype:
+            raise ValueError("o must match q in shape and dtype")
+    _set_stream(q.device)
+    _check(lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, S_q, S_kv, D,
+                        int(bool(causal)), _dtype_code(q)))
+    return o
+
+
+def attn_decode_workspace_bytes(B: int, H: int, S_cap: int, D: int) -> int:
+    return int(lib.attn_decode_workspace_bytes(B, H, S_cap, D))
+
+
+def attn_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, seqlens: torch.Tensor,
+                o: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Single-query decode. q [B,1,H,D]; caches [B,S_cap,H,D]; seqlens int32[B] on the GPU."""
+    for n, t in (("q", q), ("kcache", kcache), ("vcache", vcache)):
+        _dev_tensor(n, t, 4)
+    _dev_tensor("seqlens", seqlens, 1)
+    B, one, H, D = q.shape
+    S_cap = kcache.shape[1]
+    if one != 1 or tuple(kcache.shape) != (B, S_cap, H, D) or tuple(vcache.shape) != tuple(kcache.shape):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, kcache {tuple(kcache.shape)}, "
+                         f"vcache {tuple(vcache.shape)}")
+    if seqlens.dtype != torch.int32 or seqlens.shape[0] != B:
+        raise ValueError("seqlens must be int32[B]")
+    if not (q.dtype == kcache.dtype == vcache.dtype):
+        raise TypeError("q and the caches must share one dtype")
+    if o is None:
+        o = torch.empty_like(q)
+    need = attn_decode_workspace_bytes(B, H, S_cap, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _set_stream(q.device)
+    _check(lib.attn_decode(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), seqlens.data_ptr(),
+                           o.data_ptr(), B, H, S_cap, D, _dtype_code(q), workspace.data_ptr(),
+                           workspace.numel() * workspace.element_size()))
+    return o
+
+
+def attn_fwd_plan(B: int, H: int, S_q: int, S_kv: int, D: int, causal: bool, dtype: int) -> FwdPlan:
+    plan = FwdPlan()
+    _check(lib.attn_fwd_plan(B, H, S_q, S_kv, D, int(bool(causal)), dtype, ctypes.byref(plan)))
+    return plan
+
+
+def attn_decode_plan(B: int, H: int, S_cap: int, D: int, dtype: int) -> DecodePlan:
+    plan = DecodePlan()
+    _check(lib.attn_decode_plan(B, H, S_cap, D, dtype, ctypes.byref(plan)))
+    return plan
+
+
+__all__ = ["attn_fwd", "attn_decode", "attn_decode_workspace_bytes", "attn_fwd_plan", "attn_decode_plan",
+           "AttnError", "ATTN_F32", "ATTN_BF16", "lib", "LIB_PATH"]

@@ -1,0 +1,252 @@
+// attn_api.cpp -- the C ABI of libattn.so: validation, planning, dispatch.
+//
+// Every argument is checked here on the host before any HIP call, so a
+// rejected call has no side effect and the checks can be exercised without a
+// GPU. Launch errors are read back with hipGetLastError right after each
+// launch (the host-launch practice of the depthwise-convolution page,
+// section 3.2); configuration mistakes are caught before they become
+// "invalid configuration" launches ("CUDA first principles" page,
+// section 4.1). An environment switch picks the implementation, as the
+// depthwise-convolution page's section 6.2 suggests for bisecting:
+//   ATTN_ALGO=auto (default) | tile | row
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/attn.h"
+#include "launch.h"
+#include "plan.h"
+
+namespace {
+
+thread_local hipStream_t t_stream = nullptr;
+thread_local std::string t_error;
+
+int fail(int status, const std::string& msg) {
+    t_error = msg;
+    return status;
+}
+
+int ok() {
+    t_error.clear();
+    return ATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte size of a dense tensor, or -1 when it does not fit in 2^62.
+long long tensor_bytes(long long a, long long b, long long c, long long d, long long elem) {
+    const long long lim = (long long)1 << 62;
+    long long n = elem;
+    for (long long x : {a, b, c, d}) {
+        if (x < 0) return -1;
+        if (x != 0 && n > lim / x) return -1;
+        n *= x;
+    }
+    return n;
+}
+
+bool overlap(const void* a, long long na, const void* b, long long nb) {
+    if (!a || !b || na <= 0 || nb <= 0) return false;
+    const uintptr_t x0 = reinterpret_cast<uintptr_t>(a), y0 = reinterpret_cast<uintptr_t>(b);
+    return x0 < y0 + (uintptr_t)nb && y0 < x0 + (uintptr_t)na;
+}
+
+int elem_size(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
+
+enum Algo { kAuto, kTile, kRow };
+
+Algo algo_from_env() {
+    const char* s = std::getenv("ATTN_ALGO");
+    if (!s || !*s || !std::strcmp(s, "auto")) return kAuto;
+    if (!std::strcmp(s, "tile")) return kTile;
+    if (!std::strcmp(s, "row")) return kRow;
+    return kAuto;
+}
+
+// Checks shared by attn_fwd and attn_fwd_plan (sizes and flags only).
+int check_fwd_sizes(int B, int H, int S_q, int S_kv, int D, int causal, int dtype) {
+    if (B < 0 || H < 0 || S_q < 0 || S_kv < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: negative size (B=" + std::to_string(B) + " H=" +
+                                              std::to_string(H) + " S_q=" + std::to_string(S_q) +
+                                              " S_kv=" + std::to_string(S_kv) + ")");
+    if (D <= 0) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: head dim D must be positive");
+    if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: causal must be 0 or 1");
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: dtype " + std::to_string(dtype) +
+                                              " not built (ATTN_F32=0, ATTN_BF16=1)");
+    if (D != 32 && D != 64 && D != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: head dim D=" + std::to_string(D) +
+                                              " not built (32, 64 or 128)");
+    const long long out_elems = (long long)B * H * S_q;
+    if (out_elems == 0) return ATTN_OK;
+    if (S_kv == 0) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: S_kv == 0 leaves the softmax without keys");
+    if (causal && S_q > S_kv)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: causal needs S_q <= S_kv (queries are the last S_q positions)");
+    const int es = elem_size(dtype);
+    if (tensor_bytes(B, S_q, H, D, es) < 0 || tensor_bytes(B, S_kv, H, D, es) < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: tensor size overflows");
+    if ((long long)B * H * S_q > 0x7fffffffLL || (long long)B * H * ((S_q + 127) / 128) > 0x7fffffffLL)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: B*H*S_q exceeds the launch grid");
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_set_stream(void* hip_stream) {
+    t_stream = static_cast<hipStream_t>(hip_stream);
+    return ok();
+}
+
+void* attn_get_stream(void) { return static_cast<void*>(t_stream); }
+
+const char* attn_last_error(void) { return t_error.c_str(); }
+
+const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ATTN_OK";
+        case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG";
+        case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+        case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
+        case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+        default: return "ATTN_UNKNOWN_STATUS";
+    }
+}
+
+int attn_xcd_remap(int x, int n) {
+    if (n <= 0 || x < 0 || x >= n) return -1;
+    return attn::xcd_remap(x, n);
+}
+
+int attn_fwd_plan(int B, int H, int S_q, int S_kv, int D, int causal, int dtype, attn_fwd_plan_t* plan) {
+    if (!plan) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_plan: plan is NULL");
+    std::memset(plan, 0, sizeof(*plan));
+    const int st = check_fwd_sizes(B, H, S_q, S_kv, D, causal, dtype);
+    if (st != ATTN_OK) return st;
+    if ((long long)B * H * S_q == 0) return ok();
+    const Algo algo = algo_from_env();
+    const bool tile = dtype == ATTN_BF16 && algo != kRow;
+    if (tile) {
+        const attn::TileGrid g = attn::tile_grid(B, H, S_q, causal);
+        plan->kernel = 1;
+        plan->block_m = attn::kTileM;
+        plan->block_n = attn::kTileN;
+        plan->paired = g.paired;
+        plan->grid = (int)g.n_items;
+        plan->threads = attn::kTileThreads;
+        plan->lds_bytes = attn::tile_lds_bytes(D);
+        int mx = 0, mn = 1 << 30;
+        for (int p = 0; p < g.items_per_bh; ++p) {
+            const int qa = g.n_qblk - 1 - p;
+            int n = attn::tiles_for_block(qa, S_q, S_kv, causal);
+            if (g.paired && p != qa) n += attn::tiles_for_block(p, S_q, S_kv, causal);
+            mx = n > mx ? n : mx;
+            mn = n < mn ? n : mn;
+        }
+        plan->max_tiles = mx;
+        plan->min_tiles = mn;
+    } else {
+        plan->kernel = 2;
+        plan->block_m = 1;
+        plan->block_n = 64;
+        plan->grid = B * H * S_q;
+        plan->threads = attn::kRowThreads;
+        plan->lds_bytes = D * 4;
+        plan->max_tiles = (S_kv + 63) / 64;
+        plan->min_tiles = causal ? (S_kv - S_q + 1 + 63) / 64 : (S_kv + 63) / 64;
+    }
+    return ok();
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q, int S_kv, int D,
+             int causal, int dtype) {
+    const int st = check_fwd_sizes(B, H, S_q, S_kv, D, causal, dtype);
+    if (st != ATTN_OK) return st;
+    if ((long long)B * H * S_q == 0) return ok();
+    const int es = elem_size(dtype);
+    const long long nq = tensor_bytes(B, S_q, H, D, es), nkv = tensor_bytes(B, S_kv, H, D, es);
+    if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: NULL tensor pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: tensor pointers must be 16-byte aligned");
+    if (overlap(o, nq, q, nq) || overlap(o, nq, k, nkv) || overlap(o, nq, v, nkv))
+        return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: output overlaps an input");
+
+    attn::FwdArgs a{q, k, v, o, B, H, S_q, S_kv, D, causal,
+                    (float)(1.0f / std::sqrt((float)D)) * 1.4426950408889634f};
+    const Algo algo = algo_from_env();
+    hipError_t e;
+    if (dtype == ATTN_BF16 && algo != kRow)
+        e = attn::launch_fwd_tile_bf16(a, t_stream);
+    else
+        e = attn::launch_fwd_row(a, dtype == ATTN_BF16, t_stream);
+    if (e != hipSuccess)
+        return fail(ATTN_ERR_HIP, std::string("attn_fwd: launch failed: ") + hipGetErrorString(e));
+    return ok();
+}
+
+size_t attn_decode_workspace_bytes(int B, int H, int S_cap, int D) {
+    if (B <= 0 || H <= 0 || S_cap <= 0 || D <= 0) return 0;
+    return attn::decode_workspace_floats(B, H, S_cap, D) * sizeof(float);
+}
+
+int attn_decode_plan(int B, int H, int S_cap, int D, int dtype, attn_decode_plan_t* plan) {
+    if (!plan) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_plan: plan is NULL");
+    std::memset(plan, 0, sizeof(*plan));
+    if (B < 0 || H < 0 || S_cap <= 0 || D <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_decode: sizes must be B, H >= 0 and S_cap, D >= 1");
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: dtype " + std::to_string(dtype) + " not built");
+    if (D != 32 && D != 64 && D != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: head dim D=" + std::to_string(D) + " not built");
+    if (tensor_bytes(B, S_cap, H, D, elem_size(dtype)) < 0 ||
+        (long long)attn::decode_n_split_max(S_cap) * H * B > 0x7fffffffLL)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_decode: sizes overflow");
+    plan->chunk = attn::kDecodeChunk;
+    plan->n_split_max = attn::decode_n_split_max(S_cap);
+    plan->threads = attn::kDecodeThreads;
+    plan->workspace_bytes = attn_decode_workspace_bytes(B, H, S_cap, D);
+    return ok();
+}
+
+int attn_decode(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens, void* o, int B,
+                int H, int S_cap, int D, int dtype, void* workspace, size_t workspace_bytes) {
+    attn_decode_plan_t plan;
+    const int st = attn_decode_plan(B, H, S_cap, D, dtype, &plan);
+    if (st != ATTN_OK) return st;
+    if ((long long)B * H == 0) return ok();
+    const int es = elem_size(dtype);
+    const long long nq = tensor_bytes(B, 1, H, D, es), nkv = tensor_bytes(B, S_cap, H, D, es);
+    const long long nsl = (long long)B * 4;
+    if (!q || !kcache || !vcache || !seqlens || !o)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_decode: NULL tensor pointer");
+    if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(o))
+        return fail(ATTN_ERR_INVALID_ARG, "attn_decode: tensor pointers must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_decode: seqlens must be 4-byte aligned");
+    if (!workspace || workspace_bytes < plan.workspace_bytes)
+        return fail(ATTN_ERR_WORKSPACE, "attn_decode: workspace needs " + std::to_string(plan.workspace_bytes) +
+                                            " bytes, got " + std::to_string(workspace_bytes));
+    if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "attn_decode: workspace must be 16-byte aligned");
+    const long long nws = (long long)plan.workspace_bytes;
+    if (overlap(o, nq, q, nq) || overlap(o, nq, kcache, nkv) || overlap(o, nq, vcache, nkv) ||
+        overlap(o, nq, seqlens, nsl) || overlap(o, nq, workspace, nws))
+        return fail(ATTN_ERR_INVALID_ARG, "attn_decode: output overlaps another argument");
+    if (overlap(workspace, nws, q, nq) || overlap(workspace, nws, kcache, nkv) ||
+        overlap(workspace, nws, vcache, nkv) || overlap(workspace, nws, seqlens, nsl))
+        return fail(ATTN_ERR_INVALID_ARG, "attn_decode: workspace overlaps an input");
+
+    attn::DecodeArgs a{q, kcache, vcache, seqlens, o, B, H, S_cap, D,
+                       (float)(1.0f / std::sqrt((float)D)) * 1.4426950408889634f, (float*)workspace};
+    const hipError_t e = attn::launch_decode(a, dtype == ATTN_BF16, t_stream);
+    if (e != hipSuccess)
+        return fail(ATTN_ERR_HIP, std::string("attn_decode: launch failed: ") + hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+// fwd_row.hip -- one wave per query row: the per-query mapping.
+//
+// Serves the fp32 forward (gfx950 has no reduced-precision fp32 matrix
+// path, and fp32 inputs are held to a 1e-4 absolute bound) and, under
+// ATTN_ALGO=row, a bf16 cross-check of the tile kernel. Each iteration takes
+// 64 keys: lane j computes the score of key j0+j (one K row, 16-byte
+// loads), the wave reduces max and sum with cross-lane shuffles, and the
+// lanes switch to owning head dims to accumulate p_j * V[j0+j, :] with
+// coalesced V-row loads.
+//
+// Method: per-query block mapping ("Hand-written Masked Multi-Head
+// Attention CUDA kernel" page, section 2.1); Q row in registers, dot
+// products, warp-level max then exp and sum, never writing scores out
+// (same page, section 2.2; shuffle reduction instead of shared memory and
+// barriers: section 4.1); online softmax with running max and sum and the
+// -inf mask ("Week-4 CUDA notes" page, section 2.2); fp32 accumulation
+// (MMHA page, section 3.3).
+#include <hip/hip_runtime.h>
+
+#include "../launch.h"
+#include "../plan.h"
+
+namespace attn {
+namespace {
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+template <typename T>
+__device__ __forceinline__ T from_f32(float x) { return (T)x; }
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kRowThreads) void fwd_row_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                              const T* __restrict__ V, T* __restrict__ O,
+                                                              int H, int S_q, int S_kv, int causal, float c) {
+    constexpr int DPL = (D + 63) / 64;   // head dims per lane in the P.V phase
+    __shared__ float qs[D];
+    const int lane = threadIdx.x;
+    // flat grid over (b, h, i), i fastest
+    const int i = (int)(blockIdx.x % (unsigned)S_q);
+    const int bh = (int)(blockIdx.x / (unsigned)S_q);
+    const int h = bh % H, b = bh / H;
+    const size_t qoff = ((size_t)((size_t)b * S_q + i) * H + h) * D;
+    for (int d = lane; d < D; d += 64) qs[d] = to_f32(Q[qoff + d]);
+    __syncthreads();
+
+    const int n_keys = causal ? min(S_kv, i + 1 + (S_kv - S_q)) : S_kv;
+    float m_run = -INFINITY, l_run = 0.f;
+    float acc[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+
+    for (int j0 = 0; j0 < n_keys; j0 += 64) {
+        const int j = j0 + lane;
+        float s = -INFINITY;
+        if (j < n_keys) {
+            const T* krow = K + ((size_t)((size_t)b * S_kv + j) * H + h) * D;
+            float dot = 0.f;
+#pragma unroll 8
+            for (int d = 0; d < D; ++d) dot = __builtin_fmaf(qs[d], to_f32(krow[d]), dot);
+            s = dot * c;
+        }
+        const float m_new = fmaxf(m_run, wave_max(s));
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // m_new is finite: key j0 is valid
+        const float pj = __builtin_amdgcn_exp2f(s - m_new);
+        l_run = l_run * alpha + wave_sum(pj);
+        m_run = m_new;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[e] *= alpha;
+        const int nj = min(64, n_keys - j0);
+        for (int jj = 0; jj < nj; ++jj) {
+            const float p = __shfl(pj, jj);
+            const T* vrow = V + ((size_t)((size_t)b * S_kv + j0 + jj) * H + h) * D;
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) {
+                const int d = lane + 64 * e;
+                if (d < D) acc[e] = __builtin_fmaf(p, to_f32(vrow[d]), acc[e]);
+            }
+        }
+    }
+    const float inv = 1.0f / l_run;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+        const int d = lane + 64 * e;
+        if (d < D) O[qoff + d] = from_f32<T>(acc[e] * inv);
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_row(const FwdArgs& a, hipStream_t stream) {
+    const unsigned grid = (unsigned)((long long)a.B * a.H * a.S_q);
+    hipLaunchKernelGGL((fwd_row_kernel<T, D>), dim3(grid), dim3(kRowThreads), 0, stream,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.H, a.S_q, a.S_kv, a.causal,
+                       a.scale_log2);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_row_t(const FwdArgs& a, hipStream_t stream) {
+    switch (a.D) {
+        case 32: return launch_row<T, 32>(a, stream);
+        case 64: return launch_row<T, 64>(a, stream);
+        case 128: return launch_row<T, 128>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_row(const FwdArgs& a, bool dtype_is_bf16, hipStream_t stream) {
+    return dtype_is_bf16 ? launch_row_t<__bf16>(a, stream) : launch_row_t<float>(a, stream);
+}
+
+}  // namespace attn

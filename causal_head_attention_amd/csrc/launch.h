@@ -1,0 +1,39 @@
+// launch.h -- internal launchers (host functions defined next to their kernels).
+// Arguments reaching these have already been validated by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    int B, H, S_q, S_kv, D;
+    int causal;
+    float scale_log2;   // (1/sqrt(D)) * log2(e), fp32
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* kcache;
+    const void* vcache;
+    const int32_t* seqlens;
+    void* o;
+    int B, H, S_cap, D;
+    float scale_log2;
+    float* workspace;   // decode_workspace_floats(B, H, S_cap, D) floats
+};
+
+// MFMA bf16 tile kernel; D in {32, 64, 128}.
+hipError_t launch_fwd_tile_bf16(const FwdArgs& a, hipStream_t stream);
+// Row kernel: one wave per query row; dtype_is_bf16 selects the storage type.
+hipError_t launch_fwd_row(const FwdArgs& a, bool dtype_is_bf16, hipStream_t stream);
+// Split-KV decode (split + combine kernels).
+hipError_t launch_decode(const DecodeArgs& a, bool dtype_is_bf16, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,107 @@
+// plan.h -- launch geometry shared by the host planner and the kernels.
+//
+// Everything here is a pure function of the problem sizes, so the host can
+// compute (and the CPU tests can check) exactly what a kernel will do.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define ATTN_HD __host__ __device__
+#else
+#define ATTN_HD
+#endif
+
+namespace attn {
+
+// ---------------------------------------------------------------------------
+// MFMA bf16 tile kernel (prefill).
+//   A work item is one (b, h, query block of BM rows); with the causal mask,
+//   query blocks r and n-1-r share one workgroup so every workgroup visits
+//   the same number of KV tiles (the causal triangle folded in half).
+//   Eight waves: wave w covers queries 32*(w%4) .. +31 of the block and the
+//   key half w/4 of every BN-key tile.
+// ---------------------------------------------------------------------------
+constexpr int kTileM = 128;     // queries per block
+constexpr int kTileN = 64;      // keys per KV tile
+constexpr int kTileWaves = 8;
+constexpr int kTileThreads = kTileWaves * 64;
+
+constexpr int kNumXcd = 8;      // MI355X: 8 XCDs, workgroups dealt round-robin
+
+// Hardware workgroup x (of n) runs on XCD x % 8. Return a logical id such
+// that each XCD receives a contiguous range of logical ids (so neighbouring
+// work items -- the blocks of one head -- share that XCD's L2).
+ATTN_HD inline int xcd_remap(int x, int n) {
+    if (n <= kNumXcd) return x;
+    const int per = (n + kNumXcd - 1) / kNumXcd;   // ids on the "tall" XCDs
+    int tall = n % kNumXcd;
+    if (tall == 0) tall = kNumXcd;
+    const int xcd = x % kNumXcd;
+    const int local = x / kNumXcd;
+    if (xcd < tall) return xcd * per + local;
+    return tall * per + (xcd - tall) * (per - 1) + local;
+}
+
+// LDS bytes of the tile kernel for head dim D: two stages of (K tile, V^T
+// tile), or the end-of-block exchange of partial accumulators, whichever is
+// larger.
+ATTN_HD constexpr int tile_lds_bytes(int D) {
+    return (2 * 2 * kTileN * D * 2) > (4 * 64 * (D / 2) * 4 + 4 * 2 * 64 * 4)
+               ? (2 * 2 * kTileN * D * 2)
+               : (4 * 64 * (D / 2) * 4 + 4 * 2 * 64 * 4);
+}
+
+// Number of KV tiles query block qb must visit.
+ATTN_HD inline int tiles_for_block(int qb, int S_q, int S_kv, int causal) {
+    const int n_all = (S_kv + kTileN - 1) / kTileN;
+    if (!causal) return n_all;
+    int last_q = (qb + 1) * kTileM - 1;
+    if (last_q > S_q - 1) last_q = S_q - 1;
+    const int last_key = last_q + (S_kv - S_q);
+    const int n = last_key / kTileN + 1;
+    return n < n_all ? n : n_all;
+}
+
+struct TileGrid {
+    int n_qblk;         // query blocks per (b, h)
+    int items_per_bh;   // work items per (b, h)
+    int paired;         // 1: item p runs blocks n-1-p then p
+    long long n_items;  // total workgroups
+};
+
+ATTN_HD inline TileGrid tile_grid(int B, int H, int S_q, int causal) {
+    TileGrid g;
+    g.n_qblk = (S_q + kTileM - 1) / kTileM;
+    g.paired = causal ? 1 : 0;
+    g.items_per_bh = g.paired ? (g.n_qblk + 1) / 2 : g.n_qblk;
+    g.n_items = (long long)B * H * g.items_per_bh;
+    return g;
+}
+
+// ---------------------------------------------------------------------------
+// Row kernel (fp32 path, and the bf16 cross-check path): one wave per query.
+// ---------------------------------------------------------------------------
+constexpr int kRowThreads = 64;
+
+// ---------------------------------------------------------------------------
+// Split-KV decode.
+//   Split kernel: one workgroup per (split, h, b), 4 waves, 64 keys per wave.
+//   Combine kernel: one workgroup per (h, b).
+// ---------------------------------------------------------------------------
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeKeysPerWave = 64;
+constexpr int kDecodeChunk = kDecodeWaves * kDecodeKeysPerWave;   // 256 keys per split
+constexpr int kDecodeThreads = kDecodeWaves * 64;
+
+ATTN_HD inline int decode_n_split_max(int S_cap) {
+    return (S_cap + kDecodeChunk - 1) / kDecodeChunk;
+}
+
+// Workspace: per (b, h, split) one float max, one float sum, D float accumulators.
+ATTN_HD inline size_t decode_workspace_floats(int B, int H, int S_cap, int D) {
+    return (size_t)B * (size_t)H * (size_t)decode_n_split_max(S_cap) * (size_t)(D + 2);
+}
+
+}  // namespace attn

@@ -1,0 +1,187 @@
+/*
+ * attn.h -- C ABI of the gfx950 (MI355X) causal multi-head attention library
+ * (libattn.so).
+ *
+ * Operation. For every batch b and head h:
+ *
+ *     O = softmax(Q K^T / sqrt(D) + M) V
+ *
+ * with M the causal mask (0 where key j is visible to query i, -inf
+ * elsewhere). This is the masked multi-head attention of the "Hand-written
+ * Masked Multi-Head Attention CUDA kernel" page, section 2 (the page's
+ * "O = AV^T" is read as O = A.V), computed the fused way that page's
+ * section 2.2 and the "Week-4 CUDA notes" page, section 2.2 describe: the
+ * score matrix never reaches device memory and the softmax is the one-pass
+ * online form (running max and running sum).
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are dense, row-major [B, S, H, D] (batch, position, head,
+ *    head_dim): MMHA page, section 2.1. Every pointer is a DEVICE pointer
+ *    that stays owned by the caller; the library allocates no device memory
+ *    and keeps no state besides a per-thread stream and error message.
+ *  - Calls are asynchronous: they enqueue kernels on the calling thread's
+ *    stream (attn_set_stream; default: the null stream) and return. A fault
+ *    inside a kernel surfaces at the caller's next synchronisation.
+ *  - Every entry point returns an attn_status_t. Arguments are validated on
+ *    the host before any HIP call; a rejected call touches no memory and
+ *    launches nothing. attn_last_error() then holds a readable reason.
+ *    No C++ exception crosses this boundary and nothing aborts the process.
+ *  - Data pointers must be 16-byte aligned (the kernels move 128-bit
+ *    vectors: "Week-4 CUDA notes" page, section 1.2), the output must not
+ *    overlap any input, and a pointer may be NULL only when its tensor has
+ *    no elements.
+ *  - Causal visibility (MMHA page, section 2.2: key j visible iff j <= i)
+ *    with S_q <= S_kv places the S_q queries at the END of the key sequence:
+ *    query i is at absolute position i + (S_kv - S_q) and sees keys
+ *    j <= i + S_kv - S_q. With S_q == S_kv this is exactly j <= i.
+ *  - Arithmetic: scores, softmax and accumulation in fp32 whatever the
+ *    storage type (MMHA page, section 3.3); the scale 1/sqrt(D) is an fp32
+ *    value. bf16 results are rounded to nearest even.
+ */
+#ifndef ATTN_GFX950_H
+#define ATTN_GFX950_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. ATTN_F16 is reserved and currently returns ATTN_ERR_UNSUPPORTED. */
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_F16 = 2 } attn_dtype_t;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = 1, /* bad size, pointer, alignment, aliasing or flag  */
+    ATTN_ERR_UNSUPPORTED = 2, /* valid request outside what is built (D, dtype)  */
+    ATTN_ERR_WORKSPACE = 3,   /* decode workspace missing or too small           */
+    ATTN_ERR_HIP = 4          /* the HIP runtime reported an error at launch     */
+} attn_status_t;
+
+/*
+ * attn_fwd -- fused masked multi-head attention forward (prefill).
+ * Definition: MMHA page, section 2; fusion of QK^T, mask, softmax and P.V
+ * in one kernel: MMHA page, sections 2.2 and 3, and "Week-4 CUDA notes"
+ * page, section 2.2 (online softmax).
+ *
+ *   q : [B, S_q,  H, D]   k, v : [B, S_kv, H, D]   o : [B, S_q, H, D]
+ *   All four have element type `dtype` (ATTN_F32 or ATTN_BF16).
+ *   D must be 32, 64 or 128 (else ATTN_ERR_UNSUPPORTED).
+ *   causal: 1 applies the mask above (requires S_q <= S_kv), 0 lets every
+ *   query see all S_kv keys. Any other value is ATTN_ERR_INVALID_ARG.
+ *   B, H or S_q equal to 0 is a valid empty call (nothing is launched);
+ *   S_kv == 0 with a non-empty output is ATTN_ERR_INVALID_ARG (no keys to
+ *   attend to). Negative sizes are ATTN_ERR_INVALID_ARG.
+ *   o may not overlap q, k or v; q, k and v may alias each other.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q,
+             int S_kv, int D, int causal, int dtype);
+
+/*
+ * attn_decode_workspace_bytes -- device workspace attn_decode needs for
+ * these sizes (per-split partial max, sum and D accumulators, fp32).
+ * Returns 0 for invalid or empty sizes.
+ */
+size_t attn_decode_workspace_bytes(int B, int H, int S_cap, int D);
+
+/*
+ * attn_decode -- single-query (GEMV-shaped) masked attention against a KV
+ * cache: the per-query mapping of the MMHA page, section 2.1, with the
+ * keys split across workgroups and the per-split partial softmax states
+ * merged afterwards (rows spanning several blocks need one common
+ * normaliser: "Week-4 CUDA notes" page, section 2.2).
+ *
+ *   q, o            : [B, 1, H, D]
+ *   kcache, vcache  : [B, S_cap, H, D]
+ *   seqlens         : DEVICE int32[B]; query b attends cache slots
+ *                     0 .. seqlens[b]-1 (it is the last position, so the
+ *                     causal mask admits all of them). It is read on the
+ *                     device only: a value <= 0 produces an all-zero output
+ *                     row and a value > S_cap is treated as S_cap. Slots at
+ *                     or beyond the length are never read.
+ *   workspace       : DEVICE buffer of at least
+ *                     attn_decode_workspace_bytes(B, H, S_cap, D) bytes,
+ *                     16-byte aligned; contents on entry are ignored and on
+ *                     return are unspecified. Calls that share a workspace
+ *                     must be ordered on one stream.
+ *   dtype           : ATTN_F32 or ATTN_BF16 for q, caches and o.
+ *   D must be 32, 64 or 128. B == 0 or H == 0 is a valid empty call;
+ *   S_cap must be >= 1. o may not overlap any other argument.
+ * A too-small or NULL workspace returns ATTN_ERR_WORKSPACE.
+ */
+int attn_decode(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens,
+                void* o, int B, int H, int S_cap, int D, int dtype, void* workspace,
+                size_t workspace_bytes);
+
+/*
+ * attn_set_stream -- set the HIP stream (a hipStream_t passed as void*) that
+ * later calls from THIS thread enqueue on; NULL selects the null stream.
+ * attn_get_stream returns the current thread's stream.
+ */
+int attn_set_stream(void* hip_stream);
+void* attn_get_stream(void);
+
+/* Reason for the last non-OK status returned on this thread ("" if none).
+ * The pointer stays valid until the next call into the library on this thread. */
+const char* attn_last_error(void);
+
+/* Static name of a status code ("ATTN_OK", ...). */
+const char* attn_status_string(int status);
+
+/*
+ * Launch-plan introspection (host only, no HIP call): how attn_fwd would
+ * split the work. Lets the tiling and causal load-balance rules be tested
+ * without a GPU. Returns the same status attn_fwd would return for these
+ * sizes (pointer checks excluded).
+ *   kernel      : 0 none (empty call), 1 MFMA bf16 tile kernel, 2 row kernel
+ *   block_m     : queries per work item phase (tile kernel), 1 (row kernel)
+ *   block_n     : keys per KV tile
+ *   paired      : 1 when each work item runs query block r and n-1-r
+ *   grid        : workgroups launched
+ *   threads     : threads per workgroup
+ *   lds_bytes   : LDS per workgroup
+ *   max_tiles   : largest number of KV tiles one work item visits
+ *   min_tiles   : smallest number of KV tiles one work item visits
+ */
+typedef struct {
+    int kernel;
+    int block_m;
+    int block_n;
+    int paired;
+    int grid;
+    int threads;
+    int lds_bytes;
+    int max_tiles;
+    int min_tiles;
+} attn_fwd_plan_t;
+
+int attn_fwd_plan(int B, int H, int S_q, int S_kv, int D, int causal, int dtype,
+                  attn_fwd_plan_t* plan);
+
+/*
+ * Decode plan: keys per split, number of split workgroups along the cache
+ * (grid.x), and the workspace it needs. Host only.
+ */
+typedef struct {
+    int chunk;
+    int n_split_max;
+    int threads;
+    size_t workspace_bytes;
+} attn_decode_plan_t;
+
+int attn_decode_plan(int B, int H, int S_cap, int D, int dtype, attn_decode_plan_t* plan);
+
+/*
+ * Workgroup-id remap used by the tile kernel: hardware workgroup x of n runs
+ * on XCD x % 8; the remap gives each XCD a contiguous range of logical work
+ * items so the items of one head share that XCD's L2. A bijection on
+ * [0, n). Exposed so the host tests can check it.
+ */
+int attn_xcd_remap(int x, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_GFX950_H */

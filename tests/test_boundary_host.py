@@ -1,0 +1,183 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+Every argument check in attn_api.cpp runs before any HIP call, so invalid
+calls can be exercised here with fake device addresses: a rejected call
+launches nothing and touches no memory.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import causal_head_attention_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+L = attn.lib
+A = 0x10000  # fake, 16-byte aligned "device" addresses (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_header_symbols_are_exported():
+    names = declared_functions()
+    assert {"attn_fwd", "attn_decode", "attn_decode_workspace_bytes", "attn_set_stream",
+            "attn_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in include/attn.h but not exported by libattn.so"
+
+
+def fwd(q=A, k=A + 0x100000, v=A + 0x200000, o=A + 0x300000, B=1, H=2, S_q=64, S_kv=64, D=128, causal=1,
+        dtype=attn.ATTN_BF16):
+    return L.attn_fwd(q, k, v, o, B, H, S_q, S_kv, D, causal, dtype)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(B=-1), attn.ATTN_ERR_INVALID_ARG, "negative"),
+    (dict(S_kv=-5), attn.ATTN_ERR_INVALID_ARG, "negative"),
+    (dict(D=0), attn.ATTN_ERR_INVALID_ARG, "head dim"),
+    (dict(D=48), attn.ATTN_ERR_UNSUPPORTED, "D=48"),
+    (dict(D=256), attn.ATTN_ERR_UNSUPPORTED, "D=256"),
+    (dict(dtype=attn.ATTN_F16), attn.ATTN_ERR_UNSUPPORTED, "dtype"),
+    (dict(dtype=7), attn.ATTN_ERR_UNSUPPORTED, "dtype"),
+    (dict(causal=2), attn.ATTN_ERR_INVALID_ARG, "causal"),
+    (dict(S_q=65, S_kv=64), attn.ATTN_ERR_INVALID_ARG, "S_q <= S_kv"),
+    (dict(S_kv=0), attn.ATTN_ERR_INVALID_ARG, "S_kv == 0"),
+    (dict(q=0), attn.ATTN_ERR_INVALID_ARG, "NULL"),
+    (dict(o=0), attn.ATTN_ERR_INVALID_ARG, "NULL"),
+    (dict(k=A + 0x100008), attn.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(o=A + 0x10), attn.ATTN_ERR_INVALID_ARG, "overlaps"),          # o inside q
+    (dict(o=A + 0x200000 - 0x10), attn.ATTN_ERR_INVALID_ARG, "overlaps"),  # o runs into v
+    (dict(B=1 << 30, H=1 << 20, S_q=1 << 10, S_kv=1 << 10), attn.ATTN_ERR_INVALID_ARG, "overflow"),
+    (dict(B=1 << 20, H=1 << 12, S_q=1 << 12, S_kv=1 << 12), attn.ATTN_ERR_INVALID_ARG, "launch grid"),
+])
+def test_fwd_rejections(kw, status, needle):
+    assert fwd(**kw) == status
+    msg = L.attn_last_error().decode()
+    assert needle in msg, msg
+
+
+def test_fwd_empty_calls_are_ok_and_launch_nothing():
+    # B, H or S_q == 0: valid, nothing to compute (NULL pointers allowed)
+    for kw in (dict(B=0), dict(H=0), dict(S_q=0)):
+        assert fwd(q=0, k=0, v=0, o=0, **kw) == attn.ATTN_OK
+    assert L.attn_last_error().decode() == ""
+
+
+def test_non_causal_allows_more_queries_than_keys_in_validation():
+    p = attn.attn_fwd_plan(1, 2, 100, 50, 64, False, attn.ATTN_BF16)
+    assert p.kernel == 1 and p.paired == 0
+
+
+def test_status_strings():
+    assert L.attn_status_string(0) == b"ATTN_OK"
+    assert L.attn_status_string(3) == b"ATTN_ERR_WORKSPACE"
+    assert L.attn_status_string(99) == b"ATTN_UNKNOWN_STATUS"
+
+
+def test_stream_is_per_thread_setting():
+    import threading
+    assert L.attn_set_stream(ctypes.c_void_p(0x1234)) == 0
+    assert L.attn_get_stream() == 0x1234
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(L.attn_get_stream()))
+    t.start()
+    t.join()
+    assert seen == [None]
+    L.attn_set_stream(None)
+
+
+# ---------------------------------------------------------------------------
+# Launch plans: the causal triangle folded so every workgroup gets equal work
+# ---------------------------------------------------------------------------
+def test_plan_bf16_s2048():
+    p = attn.attn_fwd_plan(1, 32, 2048, 2048, 128, True, attn.ATTN_BF16)
+    assert (p.kernel, p.block_m, p.block_n, p.paired, p.threads) == (1, 128, 64, 1, 512)
+    assert p.grid == 32 * 8                 # 16 query blocks per head, paired
+    assert p.max_tiles == p.min_tiles == 34  # (2r+2) + (2(15-r)+2) for every r
+    assert p.lds_bytes <= 160 * 1024 // 2    # two workgroups fit in one CU's LDS
+
+
+def test_plan_bf16_s4096_and_odd_block_counts():
+    p = attn.attn_fwd_plan(1, 32, 4096, 4096, 128, True, attn.ATTN_BF16)
+    assert p.grid == 32 * 16 and p.max_tiles == p.min_tiles == 66
+    p = attn.attn_fwd_plan(2, 3, 1000, 1000, 64, True, attn.ATTN_BF16)   # 8 blocks (last ragged)
+    assert p.grid == 2 * 3 * 4 and p.paired == 1
+    p = attn.attn_fwd_plan(1, 1, 640, 640, 64, True, attn.ATTN_BF16)     # 5 blocks: middle one alone
+    assert p.grid == 3 and (p.max_tiles, p.min_tiles) == (12, 6)
+
+
+def test_plan_non_causal_and_fp32():
+    p = attn.attn_fwd_plan(2, 8, 512, 512, 64, False, attn.ATTN_BF16)
+    assert p.paired == 0 and p.grid == 2 * 8 * 4 and p.max_tiles == p.min_tiles == 8
+    p = attn.attn_fwd_plan(2, 8, 512, 512, 64, True, attn.ATTN_F32)
+    assert p.kernel == 2 and p.grid == 2 * 8 * 512
+
+
+def test_plan_env_switch(monkeypatch):
+    monkeypatch.setenv("ATTN_ALGO", "row")
+    assert attn.attn_fwd_plan(1, 32, 2048, 2048, 128, True, attn.ATTN_BF16).kernel == 2
+    monkeypatch.setenv("ATTN_ALGO", "tile")
+    assert attn.attn_fwd_plan(1, 32, 2048, 2048, 128, True, attn.ATTN_BF16).kernel == 1
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 15, 16, 17, 63, 64, 100, 255, 256, 257, 512, 1000, 4099])
+def test_xcd_remap_is_a_bijection_with_contiguous_ranges(n):
+    ids = [L.attn_xcd_remap(x, n) for x in range(n)]
+    assert sorted(ids) == list(range(n))
+    if n >= 16:
+        # workgroups on one XCD (x % 8 equal) get one contiguous range of logical ids
+        for xcd in range(8):
+            mine = sorted(ids[x] for x in range(xcd, n, 8))
+            assert mine == list(range(mine[0], mine[0] + len(mine)))
+    assert L.attn_xcd_remap(n, n) == -1
+
+
+# ---------------------------------------------------------------------------
+# Decode boundary
+# ---------------------------------------------------------------------------
+def test_decode_workspace_and_plan():
+    assert attn.attn_decode_workspace_bytes(16, 32, 4096, 128) == 16 * 32 * 16 * 130 * 4
+    assert attn.attn_decode_workspace_bytes(0, 32, 4096, 128) == 0
+    p = attn.attn_decode_plan(16, 32, 4096, 128, attn.ATTN_BF16)
+    assert (p.chunk, p.n_split_max) == (256, 16)
+    assert attn.attn_decode_plan(1, 1, 257, 64, attn.ATTN_F32).n_split_max == 2
+
+
+def dec(q=A, kc=A + 0x100000, vc=A + 0x200000, sl=A + 0x300000, o=A + 0x310000, B=2, H=2, S_cap=100,
+        D=128, dtype=attn.ATTN_BF16, ws=A + 0x400000, wsb=None):
+    if wsb is None:
+        wsb = attn.attn_decode_workspace_bytes(B, H, S_cap, D)
+    return L.attn_decode(q, kc, vc, sl, o, B, H, S_cap, D, dtype, ws, wsb)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=0), attn.ATTN_ERR_WORKSPACE),
+    (dict(wsb=16), attn.ATTN_ERR_WORKSPACE),
+    (dict(S_cap=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(D=96), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=attn.ATTN_F16), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(sl=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(sl=A + 0x300002), attn.ATTN_ERR_INVALID_ARG),
+    (dict(o=A + 0x100000), attn.ATTN_ERR_INVALID_ARG),         # o on the K cache
+    (dict(ws=A + 0x200000), attn.ATTN_ERR_INVALID_ARG),        # workspace on the V cache
+    (dict(q=A + 8), attn.ATTN_ERR_INVALID_ARG),
+])
+def test_decode_rejections(kw, status):
+    assert dec(**kw) == status, L.attn_last_error()
+
+
+def test_decode_empty_call():
+    assert dec(q=0, kc=0, vc=0, sl=0, o=0, ws=0, B=0, wsb=0) == attn.ATTN_OK
+
+
+def test_binding_rejects_host_tensors():
+    q = torch.zeros(1, 4, 1, 32)
+    with pytest.raises(ValueError):
+        attn.attn_fwd(q, q, q)

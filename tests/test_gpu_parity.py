@@ -1,0 +1,247 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle.
+
+Bars (written here, applied per output tensor):
+  fp32 storage : max |gpu - oracle| <= 1e-4
+  bf16 storage : max |gpu - oracle| <= 2e-2  AND  ||gpu - oracle||_2 / ||oracle||_2 <= 1e-2
+The oracle receives exactly the values the GPU receives (bf16 widened to
+fp64), so input rounding is not counted as error.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+FP32_ATOL = 1e-4
+BF16_ATOL = 2e-2
+BF16_RELL2 = 1e-2
+
+
+def say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def attn():
+    import causal_head_attention_amd as m
+    return m
+
+
+def check(got: torch.Tensor, ref: np.ndarray, dtype: torch.dtype, what: str = ""):
+    g = got.detach().float().cpu().double().numpy()
+    assert g.shape == ref.shape, what
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    err = np.abs(g - ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    if dtype == torch.float32:
+        assert max_abs <= FP32_ATOL, f"{what}: max abs err {max_abs:.3e} > {FP32_ATOL}"
+        return max_abs, None
+    den = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(g - ref) / den) if den > 0 else float(np.linalg.norm(g - ref))
+    assert max_abs <= BF16_ATOL, f"{what}: max abs err {max_abs:.3e} > {BF16_ATOL}"
+    assert rel <= BF16_RELL2, f"{what}: rel L2 err {rel:.3e} > {BF16_RELL2}"
+    return max_abs, rel
+
+
+# ---------------------------------------------------------------------------
+# The workloads at their full sizes, in the configuration the benchmark times
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", workloads.PREFILL_CONFIGS, ids=lambda c: c.name)
+def test_prefill_workload(attn, cfg):
+    say(f"prefill {cfg.name} B={cfg.B} H={cfg.H} S={cfg.S_q} D={cfg.D} {cfg.dtype}")
+    q, k, v = workloads.make_prefill(cfg)
+    o = attn.attn_fwd(q.cuda(), k.cuda(), v.cuda(), causal=cfg.causal)
+    torch.cuda.synchronize()
+    ref = oracle.attn_fwd(q, k, v, cfg.causal)
+    max_abs, rel = check(o, ref, cfg.dtype, cfg.name)
+    say(f"  {cfg.name}: max abs {max_abs:.3e} rel L2 {rel}")
+
+
+def test_decode_workload(attn):
+    cfg = workloads.BF16_DECODE
+    say(f"decode {cfg.name} B={cfg.B} H={cfg.H} S_cap={cfg.S_cap} D={cfg.D} (NaN past each length)")
+    seqlens, q, kc, vc = workloads.make_decode(cfg, nan_fill=True)
+    o = attn.attn_decode(q.cuda(), kc.cuda(), vc.cuda(), seqlens.cuda())
+    torch.cuda.synchronize()
+    ref = np.zeros((cfg.B, 1, cfg.H, cfg.D))
+    for b in range(cfg.B):
+        n = int(seqlens[b])
+        ref[b:b + 1] = oracle.attn_decode(q[b:b + 1], kc[b:b + 1, :n], vc[b:b + 1, :n],
+                                          np.array([n], dtype=np.int32))
+    max_abs, rel = check(o, ref, cfg.dtype, cfg.name)
+    say(f"  decode: max abs {max_abs:.3e} rel L2 {rel:.3e}")
+
+
+# ---------------------------------------------------------------------------
+# Edge shapes: ragged tails, one row, S_q != S_kv, every head dim, both dtypes
+# ---------------------------------------------------------------------------
+EDGE = [
+    # B, H, S_q, S_kv, D, causal
+    (1, 1, 1, 1, 128, True),
+    (1, 2, 7, 7, 64, True),
+    (2, 3, 63, 63, 128, True),
+    (1, 2, 65, 65, 32, True),
+    (1, 1, 127, 127, 128, True),
+    (2, 1, 129, 129, 64, True),
+    (1, 2, 1000, 1000, 128, True),
+    (1, 2, 200, 300, 128, True),     # queries are the last 200 of 300 positions
+    (2, 2, 129, 77, 64, False),      # more queries than keys, no mask
+    (1, 3, 257, 257, 128, False),
+    (1, 1, 1, 513, 128, True),       # one query at the end
+    (3, 5, 33, 95, 32, True),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("shape", EDGE, ids=lambda s: "x".join(map(str, s)))
+def test_edge_shapes(attn, shape, dtype):
+    B, H, S_q, S_kv, D, causal = shape
+    say(f"edge {shape} {dtype}")
+    q, k, v = workloads.make_prefill_shape(7, dtype, B, H, S_q, S_kv, D)
+    o = attn.attn_fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal)
+    torch.cuda.synchronize()
+    check(o, oracle.attn_fwd(q, k, v, causal), dtype, str(shape))
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 300, 300, 128, True), (2, 1, 130, 200, 64, True),
+                                   (1, 1, 77, 77, 32, False)], ids=lambda s: "x".join(map(str, s)))
+def test_bf16_row_kernel_cross_check(attn, shape, monkeypatch):
+    """ATTN_ALGO=row runs the per-query kernel on bf16: both kernels meet the bar."""
+    B, H, S_q, S_kv, D, causal = shape
+    q, k, v = workloads.make_prefill_shape(9, torch.bfloat16, B, H, S_q, S_kv, D)
+    ref = oracle.attn_fwd(q, k, v, causal)
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    monkeypatch.setenv("ATTN_ALGO", "row")
+    assert attn.attn_fwd_plan(B, H, S_q, S_kv, D, causal, attn.ATTN_BF16).kernel == 2
+    o_row = attn.attn_fwd(qc, kc, vc, causal=causal)
+    monkeypatch.setenv("ATTN_ALGO", "tile")
+    o_tile = attn.attn_fwd(qc, kc, vc, causal=causal)
+    torch.cuda.synchronize()
+    check(o_row, ref, torch.bfloat16, "row")
+    check(o_tile, ref, torch.bfloat16, "tile")
+
+
+# ---------------------------------------------------------------------------
+# Invariants the definition fixes exactly
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_identity_values_expose_probabilities(attn, dtype, D):
+    """V = I (S_kv = D) makes O = P: masked entries exactly 0, rows sum to 1."""
+    S = D
+    g = torch.Generator().manual_seed(100 + D)
+    q = (torch.randn(1, S, 2, D, generator=g) * 2).to(dtype)
+    k = (torch.randn(1, S, 2, D, generator=g) * 2).to(dtype)
+    v = torch.eye(D).reshape(1, S, 1, D).expand(1, S, 2, D).contiguous().to(dtype)
+    o = attn.attn_fwd(q.cuda(), k.cuda(), v.cuda(), causal=True).float().cpu()
+    i = torch.arange(S)[:, None]
+    j = torch.arange(D)[None, :]
+    masked = (j > i).expand(2, S, D).permute(1, 0, 2)[None]
+    assert torch.all(o[masked] == 0.0)
+    tol = 1e-4 if dtype == torch.float32 else 2e-2
+    assert torch.max(torch.abs(o.sum(-1) - 1.0)) <= tol
+    check(o.to(dtype).cuda(), oracle.attn_fwd(q, k, v, True), dtype, "V=I")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_row_zero_is_value_row_zero_bitwise(attn, dtype):
+    q, k, v = workloads.make_prefill_shape(11, dtype, 2, 4, 300, 300, 128, qk_std=4.0)
+    o = attn.attn_fwd(q.cuda(), k.cuda(), v.cuda(), causal=True).cpu()
+    assert torch.equal(o[:, 0], v[:, 0])
+
+
+def test_deterministic_across_runs(attn):
+    q, k, v = (t.cuda() for t in workloads.make_prefill_shape(12, torch.bfloat16, 1, 8, 2048, 2048, 128))
+    o1 = attn.attn_fwd(q, k, v, causal=True)
+    o2 = attn.attn_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_guard_bands_untouched(attn):
+    """NaN around every input and a sentinel around the output: an out-of-bounds
+    read would poison the output, an out-of-bounds write would change a guard."""
+    B, H, S, D = 1, 3, 129, 128
+    q, k, v = workloads.make_prefill_shape(13, torch.bfloat16, B, H, S, S, D)
+    n = q.numel()
+    pad = 4096
+
+    def guarded(t, fill):
+        buf = torch.full((n + 2 * pad,), fill, dtype=t.dtype, device="cuda")
+        view = buf[pad:pad + n].view(t.shape)
+        view.copy_(t.cuda())
+        return buf, view
+
+    _, qg = guarded(q, float("nan"))
+    _, kg = guarded(k, float("nan"))
+    _, vg = guarded(v, float("nan"))
+    obuf, og = guarded(torch.zeros_like(q), 1234.0)
+    attn.attn_fwd(qg, kg, vg, og, causal=True)
+    torch.cuda.synchronize()
+    assert torch.all(obuf[:pad] == 1234.0) and torch.all(obuf[pad + n:] == 1234.0)
+    check(og, oracle.attn_fwd(q, k, v, True), torch.bfloat16, "guarded")
+
+
+# ---------------------------------------------------------------------------
+# Decode edge cases
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("D", [64, 128, 32])
+def test_decode_lengths(attn, dtype, D):
+    S_cap = 600
+    lens = [1, S_cap, 0, -3, S_cap + 5, 255, 256, 257, 511, 513, 64, 2]
+    B, H = len(lens), 3
+    g = torch.Generator().manual_seed(200 + D)
+    q = torch.randn(B, 1, H, D, generator=g).to(dtype)
+    kc = torch.randn(B, S_cap, H, D, generator=g).to(dtype)
+    vc = torch.randn(B, S_cap, H, D, generator=g).to(dtype)
+    for b, n in enumerate(lens):
+        n = max(0, min(n, S_cap))
+        kc[b, n:] = float("nan")
+        vc[b, n:] = float("nan")
+    sl = torch.tensor(lens, dtype=torch.int32)
+    o = attn.attn_decode(q.cuda(), kc.cuda(), vc.cuda(), sl.cuda()).cpu()
+    assert torch.all(o[2] == 0) and torch.all(o[3] == 0)
+    assert torch.equal(o[0, 0], vc[0, 0])                # one key: its value row, bitwise
+    ref = oracle.attn_decode(q, kc, vc, sl.numpy())
+    check(o.cuda(), ref, dtype, f"decode D={D}")
+
+
+def test_decode_matches_forward_with_one_query(attn):
+    """attn_decode row b equals attn_fwd(S_q = 1, S_kv = len_b) on the same data."""
+    B, H, S_cap, D = 4, 4, 700, 128
+    lens = [700, 1, 333, 257]
+    g = torch.Generator().manual_seed(300)
+    q = torch.randn(B, 1, H, D, generator=g).bfloat16().cuda()
+    kc = torch.randn(B, S_cap, H, D, generator=g).bfloat16().cuda()
+    vc = torch.randn(B, S_cap, H, D, generator=g).bfloat16().cuda()
+    o = attn.attn_decode(q, kc, vc, torch.tensor(lens, dtype=torch.int32).cuda())
+    for b, n in enumerate(lens):
+        of = attn.attn_fwd(q[b:b + 1], kc[b:b + 1, :n].contiguous(), vc[b:b + 1, :n].contiguous(), causal=True)
+        d = (of.float() - o[b:b + 1].float()).abs().max().item()
+        assert d <= 2e-2, (b, n, d)
+
+
+# ---------------------------------------------------------------------------
+# Error paths through the binding on a live device
+# ---------------------------------------------------------------------------
+def test_error_paths_on_device(attn):
+    q = torch.zeros(1, 8, 2, 128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(attn.AttnError) as e:
+        attn.attn_fwd(q, q, q, q, causal=True)            # output aliases the inputs
+    assert e.value.status == attn.ATTN_ERR_INVALID_ARG
+    sl = torch.ones(1, dtype=torch.int32, device="cuda")
+    qd = torch.zeros(1, 1, 2, 128, dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros(1, 16, 2, 128, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(attn.AttnError) as e:
+        attn.attn_decode(qd, kc, kc, sl, workspace=ws)
+    assert e.value.status == attn.ATTN_ERR_WORKSPACE
