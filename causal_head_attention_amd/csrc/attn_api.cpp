@@ -92,6 +92,11 @@ int check_fwd_sizes(int B, int H, int S_q, int S_kv, int D, int causal, int dtyp
         return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: tensor size overflows");
     if ((long long)B * H * S_q > 0x7fffffffLL || (long long)B * H * ((S_q + 127) / 128) > 0x7fffffffLL)
         return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: B*H*S_q exceeds the launch grid");
+    // the kernels address one head's rows with 32-bit byte offsets
+    const long long S_max = (S_q > S_kv ? S_q : S_kv) + 128;
+    if (S_max * H * D * es > 0x7fffffffLL)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: one batch entry spans more than 2 GiB "
+                                          "((S + 128) * H * D * elem_size); split the batch");
     return ATTN_OK;
 }
 

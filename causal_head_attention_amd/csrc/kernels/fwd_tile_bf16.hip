@@ -2,7 +2,7 @@
 //
 // One workgroup (8 waves) owns one (b, h, block of 128 queries); with the
 // causal mask it owns two blocks, r and n-1-r, run one after the other so
-// every workgroup walks the same number of KV tiles. For each 64-key tile:
+// every workgroup walks the same number of KV tiles. Per 64-key tile:
 //
 //   K tile  : HBM -> registers -> LDS  (row-major, 16-byte chunks XOR-swizzled)
 //   V tile  : HBM -> registers -> transposed in registers -> LDS as V^T
@@ -11,9 +11,13 @@
 //   softmax : online (running max, running sum) in fp32, base-2 exponent
 //   O^T    += V^T . P^T          v_mfma_f32_32x32x16_bf16, P rounded to bf16
 //
-// and the next tile's HBM loads are in flight while the current one is
-// computed (double-buffered LDS, one barrier per tile). The score matrix
-// never leaves registers.
+// Software pipeline, one barrier per tile: in iteration t a wave computes
+// the scores of tile t+1 on the matrix cores while it runs the softmax of
+// tile t on the vector ALUs, then accumulates P(t) V(t). K tiles are staged
+// two tiles ahead and V tiles one ahead (double-buffered LDS for each), so
+// HBM/L2 latency overlaps a whole iteration. Loads go through per-head
+// buffer descriptors: rows past the end read as zeros, with no branches.
+// The score matrix never leaves registers.
 //
 // Method: fused QK^T + mask + softmax + P.V with the score row kept on chip
 // and K tiles staged in shared memory ("Hand-written Masked Multi-Head
@@ -90,71 +94,104 @@ struct TileCfg {
     static constexpr int LDS = tile_lds_bytes(D);
 };
 
-// Issue the HBM loads of KV tile `tile0` into registers.
-// Waves 0-3 load K (row-major 16-byte chunks), waves 4-7 load V (KR keys x
-// 8 head dims each, to be transposed).
+// Buffer resource for the rows of one (b, h) head inside a [B, S, H, D]
+// tensor: base at (b, 0, h, 0), valid bytes up to the end of row S-1. A load
+// whose offset lies past the last row returns zeros and a store there is
+// dropped, so ragged tails need neither branches nor clamped addresses.
 template <int D>
-__device__ __forceinline__ void load_tile(u32x4_t (&pre)[TileCfg<D>::NPRE], const __bf16* __restrict__ K,
-                                          const __bf16* __restrict__ V, int b, int h, int H, int S_kv,
-                                          int tile0, int tid) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const __bf16* base, int b, int h, int S, int H) {
+    const __bf16* p = base + ((size_t)b * S * H + h) * D;
+    const int bytes = ((S - 1) * H + 1) * D * 2;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, bytes, 0x00020000);
+}
+
+// Byte offset of 16-byte chunk `ch` of token `tok` in a head's rows.
+template <int D>
+__device__ __forceinline__ int tok_off(int tok, int ch, int H) {
+    return (tok * H * D + 8 * ch) * 2;
+}
+
+// Loader roles: waves 0-3 stage K tiles (row-major 16-byte chunks), waves
+// 4-7 stage V tiles (KR keys x 8 head dims per thread, transposed on store).
+template <int D>
+__device__ __forceinline__ void load_k(u32x4_t (&pre)[TileCfg<D>::NPRE], __amdgpu_buffer_rsrc_t rk, int H,
+                                       int tile0, int tid) {
     using C = TileCfg<D>;
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-    if (tid < 256) {
 #pragma unroll
-        for (int it = 0; it < C::NPRE; ++it) {
-            const int ci = tid + 256 * it;
-            const int row = ci / C::KCH, ch = ci % C::KCH;
-            const int key = tile0 + row;
-            pre[it] = zero;
-            if (key < S_kv)
-                pre[it] = *(const u32x4_t*)(K + ((size_t)((size_t)b * S_kv + key) * H + h) * D + 8 * ch);
-        }
-    } else {
-        const int u = tid - 256;
-        const int c8 = u % (D / 8), kq = u / (D / 8);
+    for (int it = 0; it < C::NPRE; ++it) {
+        const int ci = tid + 256 * it;
+        const int row = ci / C::KCH, ch = ci % C::KCH;
+        pre[it] = __builtin_amdgcn_raw_buffer_load_b128(rk, tok_off<D>(tile0 + row, ch, H), 0, 0);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void load_v(u32x4_t (&pre)[TileCfg<D>::NPRE], __amdgpu_buffer_rsrc_t rv, int H,
+                                       int tile0, int tid) {
+    using C = TileCfg<D>;
+    const int u = tid - 256;
+    const int c8 = u % (D / 8), kq = u / (D / 8);
 #pragma unroll
-        for (int kk = 0; kk < C::KR; ++kk) {
-            const int key = tile0 + kq * C::KR + kk;
-            pre[kk] = zero;
-            if (key < S_kv)
-                pre[kk] = *(const u32x4_t*)(V + ((size_t)((size_t)b * S_kv + key) * H + h) * D + 8 * c8);
+    for (int kk = 0; kk < C::KR; ++kk)
+        pre[kk] = __builtin_amdgcn_raw_buffer_load_b128(rv, tok_off<D>(tile0 + kq * C::KR + kk, c8, H), 0, 0);
+}
+
+template <int D>
+__device__ __forceinline__ void store_k(const u32x4_t (&pre)[TileCfg<D>::NPRE], char* kst, int tid) {
+    using C = TileCfg<D>;
+#pragma unroll
+    for (int it = 0; it < C::NPRE; ++it) {
+        const int ci = tid + 256 * it;
+        const int row = ci / C::KCH, ch = ci % C::KCH;
+        *(u32x4_t*)(kst + k_lds_off<D>(row, ch)) = pre[it];
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void store_v(const u32x4_t (&pre)[TileCfg<D>::NPRE], char* vt, int tid) {
+    using C = TileCfg<D>;
+    const int u = tid - 256;
+    const int c8 = u % (D / 8), kq = u / (D / 8);
+    const int key0 = kq * C::KR;
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+        const int d = 8 * c8 + dd;
+        char* dst = vt + vt_lds_off(d, key0);
+        if constexpr (C::KR == 4) {
+            u32x2_t w;
+            w[0] = half_of(pre[0], dd) | (half_of(pre[1], dd) << 16);
+            w[1] = half_of(pre[2], dd) | (half_of(pre[3], dd) << 16);
+            *(u32x2_t*)dst = w;
+        } else if constexpr (C::KR == 2) {
+            *(unsigned*)dst = half_of(pre[0], dd) | (half_of(pre[1], dd) << 16);
+        } else {
+            *(unsigned short*)dst = (unsigned short)half_of(pre[0], dd);
         }
     }
 }
 
-// Write the prefetched registers of one tile into LDS stage `stage`.
+// S^T (32 keys of this wave's half tile x 32 queries) = K . Q^T
 template <int D>
-__device__ __forceinline__ void store_tile(const u32x4_t (&pre)[TileCfg<D>::NPRE], char* stage, int tid) {
+__device__ __forceinline__ f32x16_t qk_tile(const char* kst, int half, int l32, int g,
+                                            const bf16x8_t (&qf)[TileCfg<D>::KS]) {
     using C = TileCfg<D>;
-    if (tid < 256) {
+    f32x16_t s;
 #pragma unroll
-        for (int it = 0; it < C::NPRE; ++it) {
-            const int ci = tid + 256 * it;
-            const int row = ci / C::KCH, ch = ci % C::KCH;
-            *(u32x4_t*)(stage + k_lds_off<D>(row, ch)) = pre[it];
-        }
-    } else {
-        char* vt = stage + C::K_BYTES;
-        const int u = tid - 256;
-        const int c8 = u % (D / 8), kq = u / (D / 8);
-        const int key0 = kq * C::KR;
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    const char* krow = kst + (32 * half + swap_bits23(l32)) * (D * 2);
 #pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-            const int d = 8 * c8 + dd;
-            char* dst = vt + vt_lds_off(d, key0);
-            if constexpr (C::KR == 4) {
-                u32x2_t w;
-                w[0] = half_of(pre[0], dd) | (half_of(pre[1], dd) << 16);
-                w[1] = half_of(pre[2], dd) | (half_of(pre[3], dd) << 16);
-                *(u32x2_t*)dst = w;
-            } else if constexpr (C::KR == 2) {
-                *(unsigned*)dst = half_of(pre[0], dd) | (half_of(pre[1], dd) << 16);
-            } else {
-                *(unsigned short*)dst = (unsigned short)half_of(pre[0], dd);
-            }
-        }
+    for (int ks = 0; ks < C::KS; ++ks) {
+        const bf16x8_t a = *(const bf16x8_t*)(krow + 16 * ((2 * ks + g) ^ (l32 % C::KCH)));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
     }
+    return s;
 }
+
+// Row maxima are only re-based when they grow by more than 2^kLazy: until
+// then probabilities are taken against a stale maximum (at most 2^kLazy,
+// far from fp32/bf16 overflow) and the accumulators are left alone. The
+// final O = acc / l is the same quantity either way.
+constexpr float kLazy = 8.0f;
 
 template <int D>
 __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
@@ -163,6 +200,9 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
     int n_qblk, int items_per_bh, int paired) {
     using C = TileCfg<D>;
     __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+    // stages: K tiles at [0, 2*K_BYTES), V^T tiles at [2*K_BYTES, 4*K_BYTES)
+    auto kst = [&](int i) { return lds + i * C::K_BYTES; };
+    auto vst = [&](int i) { return lds + (2 + i) * C::K_BYTES; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -171,6 +211,7 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
     const int g = lane >> 5;
     const int wq = wave & 3;     // query sub-block of this wave
     const int half = wave >> 2;  // key half of every tile
+    const bool k_loader = tid < 256;
     const int off = S_kv - S_q;  // absolute position of query i is i + off
 
     const int item = xcd_remap(blockIdx.x, gridDim.x);
@@ -179,6 +220,11 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
     const int b = bh / H, h = bh % H;
     const int qb_first = n_qblk - 1 - p;
     const int nphase = (paired && p != qb_first) ? 2 : 1;
+
+    const __amdgpu_buffer_rsrc_t rq = head_rsrc<D>(Q, b, h, S_q, H);
+    const __amdgpu_buffer_rsrc_t rk = head_rsrc<D>(K, b, h, S_kv, H);
+    const __amdgpu_buffer_rsrc_t rv = head_rsrc<D>(V, b, h, S_kv, H);
+    const __amdgpu_buffer_rsrc_t ro = head_rsrc<D>((const __bf16*)O, b, h, S_q, H);
 
     for (int phase = 0; phase < nphase; ++phase) {
         const int qb = phase == 0 ? qb_first : p;
@@ -189,88 +235,94 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
         const int q_last = (q0 + 31 < S_q ? q0 + 31 : S_q - 1);
         const int key_last = causal ? q_last + off : S_kv - 1;   // last key any row of the wave sees
         const int lane_key_limit = causal ? qi + off : S_kv - 1; // last key this lane sees
+        // wave-uniform: does this wave have visible keys in tile t?
+        auto active = [&](int t) {
+            const int kb = t * kTileN + 32 * half;
+            return wave_has_rows && kb <= key_last && kb < S_kv;
+        };
 
         // Q^T fragments (B operand): lane holds query qi, head dims 16*ks + 8*g .. +7.
         bf16x8_t qf[C::KS];
-        {
-            const bool ok = qi < S_q;
-            const __bf16* qrow = Q + ((size_t)((size_t)b * S_q + (ok ? qi : 0)) * H + h) * D;
 #pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-                u32x4_t x = {0u, 0u, 0u, 0u};
-                if (ok) x = *(const u32x4_t*)(qrow + 16 * ks + 8 * g);
-                qf[ks] = __builtin_bit_cast(bf16x8_t, x);
-            }
-        }
+        for (int ks = 0; ks < C::KS; ++ks)
+            qf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rq, tok_off<D>(qi, 2 * ks + g, H), 0, 0));
 
         f32x16_t acc[C::DB];
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-        float m_run = -INFINITY;   // running max of (score * c) for query qi
+        float m_ref = -INFINITY;   // reference maximum of (score * c) for query qi
         float l_run = 0.f;         // this lane's share of the running sum
 
+        // Prologue: tile 0 (K and V) staged; S(0) computed while K(1) lands.
         u32x4_t pre[C::NPRE];
-        load_tile<D>(pre, K, V, b, h, H, S_kv, 0, tid);
-        store_tile<D>(pre, lds, tid);
+        if (k_loader) {
+            load_k<D>(pre, rk, H, 0, tid);
+            store_k<D>(pre, kst(0), tid);
+        } else {
+            load_v<D>(pre, rv, H, 0, tid);
+            store_v<D>(pre, vst(0), tid);
+        }
+        __syncthreads();
+        if (k_loader && nt > 1) load_k<D>(pre, rk, H, kTileN, tid);
+        // unconditional: every path into the loop has then waited for the Q
+        // loads, so the loop body never waits on them (or on the prefetch)
+        f32x16_t s_cur = qk_tile<D>(kst(0), half, l32, g, qf);
+        if (k_loader && nt > 1) store_k<D>(pre, kst(1), tid);
         __syncthreads();
 
         for (int t = 0; t < nt; ++t) {
-            const bool more = t + 1 < nt;
-            if (more) load_tile<D>(pre, K, V, b, h, H, S_kv, (t + 1) * kTileN, tid);
+            // (a) HBM loads: K two tiles ahead, V one tile ahead
+            const bool ld_k = k_loader && t + 2 < nt;
+            const bool ld_v = !k_loader && t + 1 < nt;
+            if (ld_k) load_k<D>(pre, rk, H, (t + 2) * kTileN, tid);
+            if (ld_v) load_v<D>(pre, rv, H, (t + 1) * kTileN, tid);
 
-            const char* stage = lds + (t & 1) * C::STAGE;
-            const int kb_local = 32 * half;
-            const int kbase = t * kTileN + kb_local;   // first key of this wave's half tile
-            if (wave_has_rows && kbase <= key_last && kbase < S_kv) {
-                // ---- S^T = K . Q^T over this wave's 32 keys x 32 queries
-                f32x16_t s;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[r] = 0.f;
-                const char* krow = stage + (kb_local + swap_bits23(l32)) * (D * 2);
-#pragma unroll
-                for (int ks = 0; ks < C::KS; ++ks) {
-                    const bf16x8_t a = *(const bf16x8_t*)(krow + 16 * ((2 * ks + g) ^ (l32 % C::KCH)));
-                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
-                }
-                // ---- mask: only where the tile crosses the diagonal or the key end
+            // (b) next tile's scores on the matrix cores ...
+            f32x16_t s_next;
+            if (t + 1 < nt && active(t + 1)) s_next = qk_tile<D>(kst((t + 1) & 1), half, l32, g, qf);
+
+            // ... while this tile's softmax runs on the vector ALUs
+            if (active(t)) {
+                const int kbase = t * kTileN + 32 * half;
                 const bool need_mask = (causal && kbase + 31 > q0 + off) || (kbase + 32 > S_kv);
                 if (need_mask) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = kbase + 16 * (r >> 3) + 8 * g + (r & 7);
-                        if (key > lane_key_limit || key >= S_kv) s[r] = -INFINITY;
+                        if (key > lane_key_limit || key >= S_kv) s_cur[r] = -INFINITY;
                     }
                 }
-                // ---- online softmax (base 2: exp(x*scale) = 2^(x*scale*log2 e))
-                float mx = s[0];
+                float mx = s_cur[0];
 #pragma unroll
-                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float m_new = fmaxf(m_run, mx * c);
-                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-                float pr[16];
-                float rs = 0.f;
+                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
+                mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+                if (__builtin_amdgcn_ballot_w64(mx > m_ref + kLazy)) {
+                    const float m_new = fmaxf(m_ref, mx);
+                    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+                    l_run *= alpha;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -m_use));
-                    rs += pr[r];
+                    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+                    m_ref = m_new;
                 }
-                l_run = l_run * alpha + rs;
-                m_run = m_new;
-#pragma unroll
-                for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+                const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+                // P is rounded to bf16 for the P.V product; the row sum adds up
+                // the same rounded values, so the weights that multiply V are
+                // exactly normalised (a near one-hot row returns its V row)
                 bf16x8_t pb[2];
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) pb[s2][i] = (__bf16)pr[8 * s2 + i];
-                // ---- O^T += V^T . P^T
-                const char* vt = stage + C::K_BYTES;
+                    for (int i = 0; i < 8; ++i) {
+                        pb[s2][i] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[8 * s2 + i], c, -m_use));
+                        l_run += (float)pb[s2][i];
+                    }
+                // (c) O^T += V^T . P^T
+                const char* vt = vst(t & 1);
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db) {
                     const int d = 32 * db + l32;
@@ -283,15 +335,18 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
                     }
                 }
             }
-            if (more) store_tile<D>(pre, lds + ((t + 1) & 1) * C::STAGE, tid);
+            // (d) land the prefetched tiles in the stages read two iterations ago
+            if (ld_k) store_k<D>(pre, kst(t & 1), tid);
+            if (ld_v) store_v<D>(pre, vst((t + 1) & 1), tid);
             __syncthreads();
+            s_cur = s_next;
         }
 
         // ---- merge the two key halves (waves wq and wq+4) through LDS
         float* xf = (float*)lds;
         float* slot = xf + wq * (64 * (C::DB * 16 + 2));
         if (half == 1) {
-            slot[lane] = m_run;
+            slot[lane] = m_ref;
             slot[64 + lane] = l_run;
 #pragma unroll
             for (int db = 0; db < C::DB; ++db)
@@ -302,30 +357,29 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
         if (half == 0 && wave_has_rows) {
             const float m1 = slot[lane];
             const float l1 = slot[64 + lane];
-            const float m = fmaxf(m_run, m1);
+            const float m = fmaxf(m_ref, m1);
             const float mu = (m == -INFINITY) ? 0.f : m;
-            const float a0 = __builtin_amdgcn_exp2f(m_run - mu);
+            const float a0 = __builtin_amdgcn_exp2f(m_ref - mu);
             const float a1 = __builtin_amdgcn_exp2f(m1 - mu);
             float l = a0 * l_run + a1 * l1;
             l += __shfl_xor(l, 32);
             const float inv = 1.0f / l;
-            if (qi < S_q) {
-                __bf16* orow = O + ((size_t)((size_t)b * S_q + qi) * H + h) * D;
 #pragma unroll
-                for (int db = 0; db < C::DB; ++db)
+            for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        __bf16 ob[4];
+                for (int j = 0; j < 4; ++j) {
+                    __bf16 ob[4];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int r = 4 * j + e;
-                            const float x1 = slot[128 + (db * 16 + r) * 64 + lane];
-                            ob[e] = (__bf16)((a0 * acc[db][r] + a1 * x1) * inv);
-                        }
-                        // lane holds head dims 32*db + 8*j + 4*g .. +3 of its query
-                        *(u32x2_t*)(orow + 32 * db + 8 * j + 4 * g) = __builtin_bit_cast(u32x2_t, ob);
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * j + e;
+                        const float x1 = slot[128 + (db * 16 + r) * 64 + lane];
+                        ob[e] = (__bf16)((a0 * acc[db][r] + a1 * x1) * inv);
                     }
-            }
+                    // lane holds head dims 32*db + 8*j + 4*g .. +3 of its query;
+                    // rows past S_q fall outside the descriptor and are dropped
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, ob), ro,
+                                                          (qi * H * D + 32 * db + 8 * j + 4 * g) * 2, 0, 0);
+                }
         }
         __syncthreads();
     }
