@@ -26,8 +26,12 @@ SOURCES = [
 ]
 
 ARCH = "gfx950"
-# Packed fp32 VALU forms are switched off for every device pass.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed fp32 VALU forms are switched off for every device pass. MFMA
+# accumulators are kept in ordinary VGPRs: the softmax rescale touches them
+# with vector instructions, and accumulators in AGPRs would be copied in and
+# out of the loop.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 

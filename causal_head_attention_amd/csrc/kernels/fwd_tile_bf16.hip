@@ -4,7 +4,7 @@
 // causal mask it owns two blocks, r and n-1-r, run one after the other so
 // every workgroup walks the same number of KV tiles. Per 64-key tile:
 //
-//   K tile  : HBM -> registers -> LDS  (row-major, 16-byte chunks XOR-swizzled)
+//   K tile  : HBM -> registers -> LDS  (row-major, rows padded by 16 bytes)
 //   V tile  : HBM -> registers -> transposed in registers -> LDS as V^T
 //   S^T     = K . Q^T            v_mfma_f32_32x32x16_bf16, fp32 accumulate
 //   mask    : only on tiles that cross the diagonal or the ragged key end
@@ -57,24 +57,12 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 __device__ __forceinline__ int swap_bits23(int x) {
     return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
-}
-
-// Byte offset of 16-byte chunk `ch` of K-tile row `row` (D/8 chunks per row).
-// The XOR makes the 32 lanes that read one chunk column (rows
-// swap_bits23(lane)) hit 32 different chunk positions.
-template <int D>
-__device__ __forceinline__ int k_lds_off(int row, int ch) {
-    constexpr int KCH = D / 8;
-    return row * (D * 2) + 16 * (ch ^ (swap_bits23(row & 31) % KCH));
-}
-
-// Byte offset of element (d, key) of the V^T tile (64 keys = 8 chunks per row).
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
-__device__ __forceinline__ int vt_lds_off(int d, int key) {
-    return d * 128 + 16 * ((key >> 3) ^ vt_swz(d)) + 2 * (key & 7);
 }
 
 __device__ __forceinline__ unsigned half_of(u32x4_t x, int e) {
@@ -82,16 +70,29 @@ __device__ __forceinline__ unsigned half_of(u32x4_t x, int e) {
     return (x[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
 }
 
+// LDS layout of one stage (padded rows instead of XOR swizzles, so every
+// MFMA operand read is a base register plus an immediate offset):
+//   K tile : 64 rows of D bf16, row stride 2*D + 16 bytes. Key r of the tile
+//            sits in LDS row (r & ~31) | swap_bits23(r & 31), so the lane that
+//            reads LDS row 32*half + lane%32 gets key swap_bits23(lane%32)
+//            and 8 (or 16) consecutive lanes read 8 (16) consecutive rows:
+//            with the 16-byte pad those fall in distinct banks.
+//   V^T    : D rows of 64 keys, row stride 144 bytes (consecutive head dims
+//            -> consecutive rows -> distinct banks for the P.V reads).
 template <int D>
 struct TileCfg {
     static constexpr int KCH = D / 8;            // 16-byte chunks per K row
     static constexpr int KS = D / 16;            // MFMA k-steps for S^T
     static constexpr int DB = D / 32;            // 32-row blocks of O^T
     static constexpr int KR = D / 32;            // keys per V-transposer thread
+    static constexpr int NKQ = kTileN / KR;      // key groups per V tile
     static constexpr int NPRE = D / 32;          // 16-byte prefetch registers per thread
-    static constexpr int K_BYTES = kTileN * D * 2;
-    static constexpr int STAGE = 2 * K_BYTES;    // K tile + V^T tile
+    static constexpr int KROW = 2 * D + 16;
+    static constexpr int VROW = 2 * kTileN + 16;
+    static constexpr int K_BYTES = kTileN * KROW;
+    static constexpr int V_BYTES = D * VROW;
     static constexpr int LDS = tile_lds_bytes(D);
+    static_assert(2 * (K_BYTES + V_BYTES) <= LDS, "stages fit");
 };
 
 // Buffer resource for the rows of one (b, h) head inside a [B, S, H, D]
@@ -111,29 +112,42 @@ __device__ __forceinline__ int tok_off(int tok, int ch, int H) {
     return (tok * H * D + 8 * ch) * 2;
 }
 
-// Loader roles: waves 0-3 stage K tiles (row-major 16-byte chunks), waves
-// 4-7 stage V tiles (KR keys x 8 head dims per thread, transposed on store).
+// Descriptor for the rows of one KV tile: the head's descriptor moved to the
+// tile's first token, its range shortened to match (zero once past the end).
+// All operands are wave-uniform, so this is scalar work; the per-lane offsets
+// then stay loop-invariant.
 template <int D>
-__device__ __forceinline__ void load_k(u32x4_t (&pre)[TileCfg<D>::NPRE], __amdgpu_buffer_rsrc_t rk, int H,
-                                       int tile0, int tid) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const __bf16* base, int b, int h, int S, int H,
+                                                            int tile0) {
+    const __bf16* p = base + ((size_t)b * S * H + h) * D + (size_t)tile0 * H * D;
+    const int bytes = ((S - 1) * H + 1) * D * 2 - tile0 * H * D * 2;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, bytes > 0 ? bytes : 0, 0x00020000);
+}
+
+// Loader roles: waves 0-3 stage K tiles (16 lanes per key row), waves 4-7
+// stage V tiles: thread (c8, kq) loads KR keys x 8 head dims and writes them
+// transposed, so the 16-lane groups of one LDS store fill one 128-byte V^T row.
+template <int D>
+__device__ __forceinline__ void load_k(u32x4_t (&pre)[TileCfg<D>::NPRE], __amdgpu_buffer_rsrc_t rt, int H,
+                                       int tid) {
     using C = TileCfg<D>;
 #pragma unroll
     for (int it = 0; it < C::NPRE; ++it) {
         const int ci = tid + 256 * it;
         const int row = ci / C::KCH, ch = ci % C::KCH;
-        pre[it] = __builtin_amdgcn_raw_buffer_load_b128(rk, tok_off<D>(tile0 + row, ch, H), 0, 0);
+        pre[it] = __builtin_amdgcn_raw_buffer_load_b128(rt, tok_off<D>(row, ch, H), 0, 0);
     }
 }
 
 template <int D>
-__device__ __forceinline__ void load_v(u32x4_t (&pre)[TileCfg<D>::NPRE], __amdgpu_buffer_rsrc_t rv, int H,
-                                       int tile0, int tid) {
+__device__ __forceinline__ void load_v(u32x4_t (&pre)[TileCfg<D>::NPRE], __amdgpu_buffer_rsrc_t rt, int H,
+                                       int tid) {
     using C = TileCfg<D>;
     const int u = tid - 256;
-    const int c8 = u % (D / 8), kq = u / (D / 8);
+    const int kq = u % C::NKQ, c8 = u / C::NKQ;
 #pragma unroll
     for (int kk = 0; kk < C::KR; ++kk)
-        pre[kk] = __builtin_amdgcn_raw_buffer_load_b128(rv, tok_off<D>(tile0 + kq * C::KR + kk, c8, H), 0, 0);
+        pre[kk] = __builtin_amdgcn_raw_buffer_load_b128(rt, tok_off<D>(kq * C::KR + kk, c8, H), 0, 0);
 }
 
 template <int D>
@@ -143,7 +157,8 @@ __device__ __forceinline__ void store_k(const u32x4_t (&pre)[TileCfg<D>::NPRE], 
     for (int it = 0; it < C::NPRE; ++it) {
         const int ci = tid + 256 * it;
         const int row = ci / C::KCH, ch = ci % C::KCH;
-        *(u32x4_t*)(kst + k_lds_off<D>(row, ch)) = pre[it];
+        const int lrow = (row & ~31) | swap_bits23(row & 31);
+        *(u32x4_t*)(kst + lrow * C::KROW + 16 * ch) = pre[it];
     }
 }
 
@@ -151,12 +166,11 @@ template <int D>
 __device__ __forceinline__ void store_v(const u32x4_t (&pre)[TileCfg<D>::NPRE], char* vt, int tid) {
     using C = TileCfg<D>;
     const int u = tid - 256;
-    const int c8 = u % (D / 8), kq = u / (D / 8);
-    const int key0 = kq * C::KR;
+    const int kq = u % C::NKQ, c8 = u / C::NKQ;
+    char* base = vt + 8 * c8 * C::VROW + 2 * C::KR * kq;
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
-        const int d = 8 * c8 + dd;
-        char* dst = vt + vt_lds_off(d, key0);
+        char* dst = base + dd * C::VROW;
         if constexpr (C::KR == 4) {
             u32x2_t w;
             w[0] = half_of(pre[0], dd) | (half_of(pre[1], dd) << 16);
@@ -170,18 +184,17 @@ __device__ __forceinline__ void store_v(const u32x4_t (&pre)[TileCfg<D>::NPRE], 
     }
 }
 
-// S^T (32 keys of this wave's half tile x 32 queries) = K . Q^T
+// S^T (32 keys of this wave's half tile x 32 queries) = K . Q^T; `krow` is
+// this lane's K row (chunk g) in the stage.
 template <int D>
-__device__ __forceinline__ f32x16_t qk_tile(const char* kst, int half, int l32, int g,
-                                            const bf16x8_t (&qf)[TileCfg<D>::KS]) {
+__device__ __forceinline__ f32x16_t qk_tile(const char* krow, const bf16x8_t (&qf)[TileCfg<D>::KS]) {
     using C = TileCfg<D>;
     f32x16_t s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
-    const char* krow = kst + (32 * half + swap_bits23(l32)) * (D * 2);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8_t a = *(const bf16x8_t*)(krow + 16 * ((2 * ks + g) ^ (l32 % C::KCH)));
+        const bf16x8_t a = *(const bf16x8_t*)(krow + 32 * ks);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
     }
     return s;
@@ -200,9 +213,9 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
     int n_qblk, int items_per_bh, int paired) {
     using C = TileCfg<D>;
     __shared__ __attribute__((aligned(16))) char lds[C::LDS];
-    // stages: K tiles at [0, 2*K_BYTES), V^T tiles at [2*K_BYTES, 4*K_BYTES)
+    // stages: K0 K1 V0 V1
     auto kst = [&](int i) { return lds + i * C::K_BYTES; };
-    auto vst = [&](int i) { return lds + (2 + i) * C::K_BYTES; };
+    auto vst = [&](int i) { return lds + 2 * C::K_BYTES + i * C::V_BYTES; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -213,6 +226,9 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
     const int half = wave >> 2;  // key half of every tile
     const bool k_loader = tid < 256;
     const int off = S_kv - S_q;  // absolute position of query i is i + off
+    // per-lane operand offsets inside a stage (the k-steps / blocks are immediates)
+    const int k_lane = (32 * half + l32) * C::KROW + 16 * g;
+    const int v_lane = l32 * C::VROW + 16 * (4 * half + g);
 
     const int item = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = item / items_per_bh;
@@ -222,8 +238,6 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
     const int nphase = (paired && p != qb_first) ? 2 : 1;
 
     const __amdgpu_buffer_rsrc_t rq = head_rsrc<D>(Q, b, h, S_q, H);
-    const __amdgpu_buffer_rsrc_t rk = head_rsrc<D>(K, b, h, S_kv, H);
-    const __amdgpu_buffer_rsrc_t rv = head_rsrc<D>(V, b, h, S_kv, H);
     const __amdgpu_buffer_rsrc_t ro = head_rsrc<D>((const __bf16*)O, b, h, S_q, H);
 
     for (int phase = 0; phase < nphase; ++phase) {
@@ -235,11 +249,6 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
         const int q_last = (q0 + 31 < S_q ? q0 + 31 : S_q - 1);
         const int key_last = causal ? q_last + off : S_kv - 1;   // last key any row of the wave sees
         const int lane_key_limit = causal ? qi + off : S_kv - 1; // last key this lane sees
-        // wave-uniform: does this wave have visible keys in tile t?
-        auto active = [&](int t) {
-            const int kb = t * kTileN + 32 * half;
-            return wave_has_rows && kb <= key_last && kb < S_kv;
-        };
 
         // Q^T fragments (B operand): lane holds query qi, head dims 16*ks + 8*g .. +7.
         bf16x8_t qf[C::KS];
@@ -259,45 +268,42 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
         // Prologue: tile 0 (K and V) staged; S(0) computed while K(1) lands.
         u32x4_t pre[C::NPRE];
         if (k_loader) {
-            load_k<D>(pre, rk, H, 0, tid);
+            load_k<D>(pre, tile_rsrc<D>(K, b, h, S_kv, H, 0), H, tid);
             store_k<D>(pre, kst(0), tid);
         } else {
-            load_v<D>(pre, rv, H, 0, tid);
+            load_v<D>(pre, tile_rsrc<D>(V, b, h, S_kv, H, 0), H, tid);
             store_v<D>(pre, vst(0), tid);
         }
         __syncthreads();
-        if (k_loader && nt > 1) load_k<D>(pre, rk, H, kTileN, tid);
+        if (k_loader && nt > 1) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_kv, H, kTileN), H, tid);
         // unconditional: every path into the loop has then waited for the Q
         // loads, so the loop body never waits on them (or on the prefetch)
-        f32x16_t s_cur = qk_tile<D>(kst(0), half, l32, g, qf);
+        f32x16_t sa = qk_tile<D>(kst(0) + k_lane, qf), sb;
         if (k_loader && nt > 1) store_k<D>(pre, kst(1), tid);
         __syncthreads();
 
-        for (int t = 0; t < nt; ++t) {
+        // One tile: s_c holds S(t); S(t+1) goes to s_n.
+        auto step = [&](int t, f32x16_t& s_c, f32x16_t& s_n) {
             // (a) HBM loads: K two tiles ahead, V one tile ahead
             const bool ld_k = k_loader && t + 2 < nt;
             const bool ld_v = !k_loader && t + 1 < nt;
-            if (ld_k) load_k<D>(pre, rk, H, (t + 2) * kTileN, tid);
-            if (ld_v) load_v<D>(pre, rv, H, (t + 1) * kTileN, tid);
+            if (ld_k) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_kv, H, (t + 2) * kTileN), H, tid);
+            if (ld_v) load_v<D>(pre, tile_rsrc<D>(V, b, h, S_kv, H, (t + 1) * kTileN), H, tid);
 
-            // (b) next tile's scores on the matrix cores ...
-            f32x16_t s_next;
-            if (t + 1 < nt && active(t + 1)) s_next = qk_tile<D>(kst((t + 1) & 1), half, l32, g, qf);
-
-            // ... while this tile's softmax runs on the vector ALUs
-            if (active(t)) {
-                const int kbase = t * kTileN + 32 * half;
-                const bool need_mask = (causal && kbase + 31 > q0 + off) || (kbase + 32 > S_kv);
-                if (need_mask) {
+            const int kbase = t * kTileN + 32 * half;   // first key of this wave's half tile
+            if (wave_has_rows && kbase <= key_last && kbase < S_kv) {
+                // (b) mask: only where the tile crosses the diagonal or the key end
+                if ((causal && kbase + 31 > q0 + off) || (kbase + 32 > S_kv)) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = kbase + 16 * (r >> 3) + 8 * g + (r & 7);
-                        if (key > lane_key_limit || key >= S_kv) s_cur[r] = -INFINITY;
+                        if (key > lane_key_limit || key >= S_kv) s_c[r] = -INFINITY;
                     }
                 }
-                float mx = s_cur[0];
+                // (c) row max (one exchange with the partner lane l^32), lazy re-base
+                float mx = s_c[0];
 #pragma unroll
-                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
+                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_c[r]);
                 mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
                 if (__builtin_amdgcn_ballot_w64(mx > m_ref + kLazy)) {
                     const float m_new = fmaxf(m_ref, mx);
@@ -310,36 +316,57 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
                     m_ref = m_new;
                 }
                 const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+                // V^T operands of this tile (read early: their LDS latency then
+                // overlaps the exponentials below)
+                const char* vt = vst(t & 1) + v_lane;
+                bf16x8_t va[C::DB][2];
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) va[db][s2] = *(const bf16x8_t*)(vt + 32 * db * C::VROW + 32 * s2);
+                // (d) next tile's scores on the matrix cores, interleaved with
+                // this tile's exponentials on the vector ALUs
+                s_n = qk_tile<D>(kst((t + 1) & 1) + k_lane, qf);
                 // P is rounded to bf16 for the P.V product; the row sum adds up
                 // the same rounded values, so the weights that multiply V are
                 // exactly normalised (a near one-hot row returns its V row)
                 bf16x8_t pb[2];
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
+                for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        pb[s2][i] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[8 * s2 + i], c, -m_use));
-                        l_run += (float)pb[s2][i];
-                    }
-                // (c) O^T += V^T . P^T
-                const char* vt = vst(t & 1);
+                    for (int i = 0; i < 8; ++i)
+                        pb[s2][i] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_c[8 * s2 + i], c, -m_use));
+                    // row sum of the rounded values: one v_dot2 (x 1.0) per pair
 #pragma unroll
-                for (int db = 0; db < C::DB; ++db) {
-                    const int d = 32 * db + l32;
-                    const char* vrow = vt + d * 128;
-                    const int sw = vt_swz(d);
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) {
-                        const bf16x8_t a = *(const bf16x8_t*)(vrow + 16 * ((4 * half + 2 * s2 + g) ^ sw));
-                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s2], acc[db], 0, 0, 0);
+                    for (int i = 0; i < 4; ++i) {
+                        const bf16x2_t pair = {pb[s2][2 * i], pb[s2][2 * i + 1]};
+                        l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, l_run, false);
                     }
                 }
+                // (e) O^T += V^T . P^T
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2)
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][s2], pb[s2], acc[db], 0, 0, 0);
+                // schedule: all K and V operand reads first, then the S(t+1)
+                // MFMAs each followed by a slice of the softmax VALU work,
+                // then the P.V MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, C::KS, 0);
+#pragma unroll
+                for (int i = 0; i < C::KS; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                }
             }
-            // (d) land the prefetched tiles in the stages read two iterations ago
+            // (f) land the prefetched tiles in the stages read one iteration ago
             if (ld_k) store_k<D>(pre, kst(t & 1), tid);
             if (ld_v) store_v<D>(pre, vst((t + 1) & 1), tid);
             __syncthreads();
-            s_cur = s_next;
+        };
+        for (int t = 0; t < nt; t += 2) {
+            step(t, sa, sb);
+            if (t + 1 < nt) step(t + 1, sb, sa);
         }
 
         // ---- merge the two key halves (waves wq and wq+4) through LDS

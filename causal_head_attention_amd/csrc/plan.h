@@ -20,8 +20,8 @@ namespace attn {
 //   A work item is one (b, h, query block of BM rows); with the causal mask,
 //   query blocks r and n-1-r share one workgroup so every workgroup visits
 //   the same number of KV tiles (the causal triangle folded in half).
-//   Eight waves: wave w covers queries 32*(w%4) .. +31 of the block and the
-//   key half w/4 of every BN-key tile.
+//   Eight waves, two per SIMD: wave w covers queries 32*(w%4) .. +31 of the
+//   block and the key half w/4 of every 64-key tile.
 // ---------------------------------------------------------------------------
 constexpr int kTileM = 128;     // queries per block
 constexpr int kTileN = 64;      // keys per KV tile
@@ -44,13 +44,14 @@ ATTN_HD inline int xcd_remap(int x, int n) {
     return tall * per + (xcd - tall) * (per - 1) + local;
 }
 
-// LDS bytes of the tile kernel for head dim D: two stages of (K tile, V^T
-// tile), or the end-of-block exchange of partial accumulators, whichever is
-// larger.
+// LDS bytes of the tile kernel for head dim D: two stages of (K tile with
+// rows padded to 2*D+16 bytes, V^T tile with rows of 2*kTileN+16 bytes), or
+// the end-of-block exchange of the partial softmax states of four waves
+// (64 lanes x (2 + D/2) floats each), whichever is larger.
 ATTN_HD constexpr int tile_lds_bytes(int D) {
-    return (2 * 2 * kTileN * D * 2) > (4 * 64 * (D / 2) * 4 + 4 * 2 * 64 * 4)
-               ? (2 * 2 * kTileN * D * 2)
-               : (4 * 64 * (D / 2) * 4 + 4 * 2 * 64 * 4);
+    return (2 * (kTileN * (2 * D + 16) + D * (2 * kTileN + 16))) > (4 * 64 * (2 + D / 2) * 4)
+               ? (2 * (kTileN * (2 * D + 16) + D * (2 * kTileN + 16)))
+               : (4 * 64 * (2 + D / 2) * 4);
 }
 
 // Number of KV tiles query block qb must visit.
