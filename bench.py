@@ -3,9 +3,11 @@
 One step is one pass of the whole path over resident synthetic inputs:
   1. attn_fwd   on bf16 B=1, H=32, S=2048, D=128, causal  (prefill)
   2. attn_decode on bf16 B=16, H=32, D=128, KV capacity 4096, lengths U[1,4096]
-Each kernel call is bracketed by HIP events recorded on the stream it is
-launched on (torch's current stream), and a 512 MiB fill runs before each
-call so neither finds its inputs in L2 or the 256 MB Infinity Cache.
+Each call is timed by two hipEvents that the library attaches to its first
+and last kernel dispatch (attn_set_timing_events -> hipExtLaunchKernelGGL on
+torch's current stream), so the interval is the kernels' device time, and a
+512 MiB fill runs before each call so neither finds its inputs in L2 or the
+256 MB Infinity Cache.
 
 `value` is the prefill rate: algorithmic causal FLOP (4*B*H*D per visible
 query-key pair) / mean prefill kernel time. The decode rate (K and V bytes
@@ -13,7 +15,7 @@ of the valid tokens plus q and o / mean decode time) is reported beside it.
 The CPU baseline is the fp64 oracle on the full prefill workload, timed on
 the host cores (test infrastructure, not part of the product path).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--warm]
 Only one GPU is supported; --gpus > 1 exits with a message.
 """
 from __future__ import annotations
@@ -58,12 +60,44 @@ def measured_traffic(kernel: str, src: str):
     return ent.get("bytes_per_launch")
 
 
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch has already loaded."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.rt = ctypes.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            h = self.ct.c_void_p()
+            if self.rt.hipEventCreate(self.ct.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(h.value)
+        return out
+
+    def ms(self, a, b) -> float:
+        v = self.ct.c_float()
+        if self.rt.hipEventElapsedTime(self.ct.byref(v), self.ct.c_void_p(a), self.ct.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return v.value
+
+    def destroy(self, hs):
+        for h in hs:
+            self.rt.hipEventDestroy(self.ct.c_void_p(h))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm", action="store_true", help="also time 20 back-to-back calls without the flush")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one device copy of MIB MiB (reference for HBM counters)")
     args = ap.parse_args()
@@ -101,46 +135,51 @@ def main() -> int:
     flops = pc.flops()
     dec_bytes = workloads.decode_kv_bytes(seqlens_h.tolist(), dc.H, dc.D, 2, dc.S_cap)
 
-    def step(evs):
-        flush.zero_()
-        evs[0].record()
-        attn.attn_fwd(q, k, v, o, causal=True)
-        evs[1].record()
-        flush.zero_()
-        evs[2].record()
-        attn.attn_decode(qd, kc, vc, seqlens, od, ws)
-        evs[3].record()
+    hev = HipEvents()
 
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(4)]  # noqa: E731
+    def step(evs):
+        # events are attached to the kernels themselves (hipExtLaunchKernelGGL),
+        # so each interval is the call's device time on its own stream
+        flush.zero_()
+        attn.attn_set_timing_events(evs[0], evs[1])
+        attn.attn_fwd(q, k, v, o, causal=True)
+        flush.zero_()
+        attn.attn_set_timing_events(evs[2], evs[3])
+        attn.attn_decode(qd, kc, vc, seqlens, od, ws)
+
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
-        step(mk())
-    torch.cuda.synchronize()
+        evs = hev.create(4)
+        step(evs)
+        torch.cuda.synchronize()
+        hev.destroy(evs)
 
     log(f"timing {args.steps} steps")
-    events = [mk() for _ in range(args.steps)]
+    events = [hev.create(4) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for evs in events:
         step(evs)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
-    dec_ms = [e[2].elapsed_time(e[3]) for e in events]
+    fwd_ms = [hev.ms(e[0], e[1]) for e in events]
+    dec_ms = [hev.ms(e[2], e[3]) for e in events]
+    for e in events:
+        hev.destroy(e)
 
-    # warm-cache figures (no flush), reported for context only
+    # warm-cache figures (no flush), for context only
     warm_f, warm_d = [], []
-    for _ in range(20):
-        e = mk()
-        e[0].record()
-        attn.attn_fwd(q, k, v, o, causal=True)
-        e[1].record()
-        e[2].record()
-        attn.attn_decode(qd, kc, vc, seqlens, od, ws)
-        e[3].record()
-        torch.cuda.synchronize()
-        warm_f.append(e[0].elapsed_time(e[1]))
-        warm_d.append(e[2].elapsed_time(e[3]))
+    if args.warm:
+        for _ in range(20):
+            e = hev.create(4)
+            attn.attn_set_timing_events(e[0], e[1])
+            attn.attn_fwd(q, k, v, o, causal=True)
+            attn.attn_set_timing_events(e[2], e[3])
+            attn.attn_decode(qd, kc, vc, seqlens, od, ws)
+            torch.cuda.synchronize()
+            warm_f.append(hev.ms(e[0], e[1]))
+            warm_d.append(hev.ms(e[2], e[3]))
+            hev.destroy(e)
 
     if args.copy_calibration:
         n = args.copy_calibration << 20
@@ -212,8 +251,11 @@ def main() -> int:
                                 "mean_call_us": round(dec_mean * 1e3, 2),
                                 "median_call_us": round(statistics.median(dec_ms) * 1e3, 2),
                                 "note": "one call = split kernel + combine kernel"}},
-        "warm_cache": {"prefill_tflops": round(flops / (statistics.median(warm_f) * 1e-3) / 1e12, 2),
-                       "decode_gbs": round(dec_bytes / (statistics.median(warm_d) * 1e-3) / 1e9, 1)},
+        "warm_cache": ({"prefill_tflops": round(flops / (statistics.median(warm_f) * 1e-3) / 1e12, 2),
+                        "decode_gbs": round(dec_bytes / (statistics.median(warm_d) * 1e-3) / 1e9, 1)}
+                       if warm_f else None),
+        "timing": "hipEvents attached to the first/last kernel dispatch of each call (start->end of the "
+                  "kernels, no queueing gaps); 512 MiB fill before every call",
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         "cpu_baseline": cpu,
         "parity": parity,

@@ -41,6 +41,9 @@ class DecodePlan(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
+_lib = None
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run `python -m causal_head_attention_amd.build` "
@@ -55,6 +58,8 @@ def _load() -> ctypes.CDLL:
     lib.attn_decode.restype = i
     lib.attn_set_stream.argtypes = [vp]
     lib.attn_set_stream.restype = i
+    lib.attn_set_timing_events.argtypes = [vp, vp]
+    lib.attn_set_timing_events.restype = i
     lib.attn_get_stream.argtypes = []
     lib.attn_get_stream.restype = vp
     lib.attn_last_error.argtypes = []
@@ -70,16 +75,27 @@ def _load() -> ctypes.CDLL:
     return lib
 
 
-lib = _load()
+def load() -> ctypes.CDLL:
+    """Load libattn.so (once). Raises ImportError if it is not built: no fallback exists."""
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+
+def __getattr__(name):  # module attribute `lib` loads the library on first use
+    if name == "lib":
+        return load()
+    raise AttributeError(name)
 
 
 def _status_name(status: int) -> str:
-    return lib.attn_status_string(status).decode()
+    return load().attn_status_string(status).decode()
 
 
 def _check(status: int) -> None:
     if status != ATTN_OK:
-        raise AttnError(status, lib.attn_last_error().decode())
+        raise AttnError(status, load().attn_last_error().decode())
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -100,7 +116,7 @@ def _dev_tensor(name: str, t: torch.Tensor, dim: int) -> None:
 
 
 def _set_stream(device: torch.device) -> None:
-    _check(lib.attn_set_stream(ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)))
+    _check(load().attn_set_stream(ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)))
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None,
@@ -121,13 +137,13 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor 
         if tuple(o.shape) != tuple(q.shape) or o.dtype != q.dtype:
             raise ValueError("o must match q in shape and dtype")
     _set_stream(q.device)
-    _check(lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, S_q, S_kv, D,
+    _check(load().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, S_q, S_kv, D,
                         int(bool(causal)), _dtype_code(q)))
     return o
 
 
 def attn_decode_workspace_bytes(B: int, H: int, S_cap: int, D: int) -> int:
-    return int(lib.attn_decode_workspace_bytes(B, H, S_cap, D))
+    return int(load().attn_decode_workspace_bytes(B, H, S_cap, D))
 
 
 def attn_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, seqlens: torch.Tensor,
@@ -151,23 +167,29 @@ def attn_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, seq
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _set_stream(q.device)
-    _check(lib.attn_decode(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), seqlens.data_ptr(),
+    _check(load().attn_decode(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), seqlens.data_ptr(),
                            o.data_ptr(), B, H, S_cap, D, _dtype_code(q), workspace.data_ptr(),
                            workspace.numel() * workspace.element_size()))
     return o
 
 
+def attn_set_timing_events(start: int | None, stop: int | None) -> None:
+    """Arm two hipEvent_t handles for the next attn_fwd / attn_decode call on this thread."""
+    _check(load().attn_set_timing_events(ctypes.c_void_p(start or 0), ctypes.c_void_p(stop or 0)))
+
+
 def attn_fwd_plan(B: int, H: int, S_q: int, S_kv: int, D: int, causal: bool, dtype: int) -> FwdPlan:
     plan = FwdPlan()
-    _check(lib.attn_fwd_plan(B, H, S_q, S_kv, D, int(bool(causal)), dtype, ctypes.byref(plan)))
+    _check(load().attn_fwd_plan(B, H, S_q, S_kv, D, int(bool(causal)), dtype, ctypes.byref(plan)))
     return plan
 
 
 def attn_decode_plan(B: int, H: int, S_cap: int, D: int, dtype: int) -> DecodePlan:
     plan = DecodePlan()
-    _check(lib.attn_decode_plan(B, H, S_cap, D, dtype, ctypes.byref(plan)))
+    _check(load().attn_decode_plan(B, H, S_cap, D, dtype, ctypes.byref(plan)))
     return plan
 
 
 __all__ = ["attn_fwd", "attn_decode", "attn_decode_workspace_bytes", "attn_fwd_plan", "attn_decode_plan",
+           "attn_set_timing_events",
            "AttnError", "ATTN_F32", "ATTN_BF16", "lib", "LIB_PATH"]

@@ -25,6 +25,14 @@ namespace {
 
 thread_local hipStream_t t_stream = nullptr;
 thread_local std::string t_error;
+thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;   // for the next call only
+
+// Take (and clear) the timing events armed for this call.
+void take_events(hipEvent_t& start, hipEvent_t& stop) {
+    start = t_ev_start;
+    stop = t_ev_stop;
+    t_ev_start = t_ev_stop = nullptr;
+}
 
 int fail(int status, const std::string& msg) {
     t_error = msg;
@@ -111,6 +119,12 @@ int attn_set_stream(void* hip_stream) {
 
 void* attn_get_stream(void) { return static_cast<void*>(t_stream); }
 
+int attn_set_timing_events(void* start, void* stop) {
+    t_ev_start = static_cast<hipEvent_t>(start);
+    t_ev_stop = static_cast<hipEvent_t>(stop);
+    return ok();
+}
+
 const char* attn_last_error(void) { return t_error.c_str(); }
 
 const char* attn_status_string(int status) {
@@ -171,6 +185,8 @@ int attn_fwd_plan(int B, int H, int S_q, int S_kv, int D, int causal, int dtype,
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q, int S_kv, int D,
              int causal, int dtype) {
+    hipEvent_t ev_start, ev_stop;
+    take_events(ev_start, ev_stop);
     const int st = check_fwd_sizes(B, H, S_q, S_kv, D, causal, dtype);
     if (st != ATTN_OK) return st;
     if ((long long)B * H * S_q == 0) return ok();
@@ -183,7 +199,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H,
         return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: output overlaps an input");
 
     attn::FwdArgs a{q, k, v, o, B, H, S_q, S_kv, D, causal,
-                    (float)(1.0f / std::sqrt((float)D)) * 1.4426950408889634f};
+                    (float)(1.0f / std::sqrt((float)D)) * 1.4426950408889634f, ev_start, ev_stop};
     const Algo algo = algo_from_env();
     hipError_t e;
     if (dtype == ATTN_BF16 && algo != kRow)
@@ -221,6 +237,8 @@ int attn_decode_plan(int B, int H, int S_cap, int D, int dtype, attn_decode_plan
 
 int attn_decode(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens, void* o, int B,
                 int H, int S_cap, int D, int dtype, void* workspace, size_t workspace_bytes) {
+    hipEvent_t ev_start, ev_stop;
+    take_events(ev_start, ev_stop);
     attn_decode_plan_t plan;
     const int st = attn_decode_plan(B, H, S_cap, D, dtype, &plan);
     if (st != ATTN_OK) return st;
@@ -247,7 +265,8 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
         return fail(ATTN_ERR_INVALID_ARG, "attn_decode: workspace overlaps an input");
 
     attn::DecodeArgs a{q, kcache, vcache, seqlens, o, B, H, S_cap, D,
-                       (float)(1.0f / std::sqrt((float)D)) * 1.4426950408889634f, (float*)workspace};
+                       (float)(1.0f / std::sqrt((float)D)) * 1.4426950408889634f, (float*)workspace, ev_start,
+                       ev_stop};
     const hipError_t e = attn::launch_decode(a, dtype == ATTN_BF16, t_stream);
     if (e != hipSuccess)
         return fail(ATTN_ERR_HIP, std::string("attn_decode: launch failed: ") + hipGetErrorString(e));

@@ -212,13 +212,13 @@ template <typename T, int D>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
     const int nsm = decode_n_split_max(a.S_cap);
     const unsigned grid1 = (unsigned)((long long)nsm * a.H * a.B);
-    hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(grid1), dim3(kDecodeThreads), 0, stream, (const T*)a.q,
-                       (const T*)a.kcache, (const T*)a.vcache, a.seqlens, a.workspace, a.H, a.S_cap, nsm,
-                       a.scale_log2);
+    hipExtLaunchKernelGGL((decode_split_kernel<T, D>), dim3(grid1), dim3(kDecodeThreads), 0, stream, a.ev_start,
+                          nullptr, 0, (const T*)a.q, (const T*)a.kcache, (const T*)a.vcache, a.seqlens, a.workspace,
+                          a.H, a.S_cap, nsm, a.scale_log2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)(a.H * a.B)), dim3(128), 0, stream,
-                       (const float*)a.workspace, a.seqlens, (T*)a.o, a.H, a.S_cap, nsm);
+    hipExtLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)(a.H * a.B)), dim3(128), 0, stream, nullptr,
+                          a.ev_stop, 0, (const float*)a.workspace, a.seqlens, (T*)a.o, a.H, a.S_cap, nsm);
     return hipGetLastError();
 }
 

@@ -99,9 +99,9 @@ __global__ __launch_bounds__(kRowThreads) void fwd_row_kernel(const T* __restric
 template <typename T, int D>
 hipError_t launch_row(const FwdArgs& a, hipStream_t stream) {
     const unsigned grid = (unsigned)((long long)a.B * a.H * a.S_q);
-    hipLaunchKernelGGL((fwd_row_kernel<T, D>), dim3(grid), dim3(kRowThreads), 0, stream,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.H, a.S_q, a.S_kv, a.causal,
-                       a.scale_log2);
+    hipExtLaunchKernelGGL((fwd_row_kernel<T, D>), dim3(grid), dim3(kRowThreads), 0, stream, a.ev_start, a.ev_stop,
+                          0, (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.H, a.S_q, a.S_kv, a.causal,
+                          a.scale_log2);
     return hipGetLastError();
 }
 

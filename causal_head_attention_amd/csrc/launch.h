@@ -2,6 +2,7 @@
 // Arguments reaching these have already been validated by the C ABI layer.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -16,6 +17,8 @@ struct FwdArgs {
     int B, H, S_q, S_kv, D;
     int causal;
     float scale_log2;   // (1/sqrt(D)) * log2(e), fp32
+    hipEvent_t ev_start;   // optional: recorded when the first kernel starts
+    hipEvent_t ev_stop;    // optional: recorded when the last kernel ends
 };
 
 struct DecodeArgs {
@@ -27,6 +30,8 @@ struct DecodeArgs {
     int B, H, S_cap, D;
     float scale_log2;
     float* workspace;   // decode_workspace_floats(B, H, S_cap, D) floats
+    hipEvent_t ev_start;   // optional: recorded when the split kernel starts
+    hipEvent_t ev_stop;    // optional: recorded when the combine kernel ends
 };
 
 // MFMA bf16 tile kernel; D in {32, 64, 128}.

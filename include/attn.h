@@ -122,6 +122,17 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
 int attn_set_stream(void* hip_stream);
 void* attn_get_stream(void);
 
+/*
+ * attn_set_timing_events -- arm two HIP events (hipEvent_t passed as void*,
+ * created by the caller, either may be NULL) for the NEXT attn_fwd or
+ * attn_decode call on this thread: `start` is recorded when that call's first
+ * kernel starts executing and `stop` when its last kernel finishes, so
+ * hipEventElapsedTime(start, stop) is the call's device time without the
+ * queueing gaps around it. The events are used once; the next call (whatever
+ * its status) disarms them. Measurement plumbing, not part of the operation.
+ */
+int attn_set_timing_events(void* start, void* stop);
+
 /* Reason for the last non-OK status returned on this thread ("" if none).
  * The pointer stays valid until the next call into the library on this thread. */
 const char* attn_last_error(void);

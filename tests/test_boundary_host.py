@@ -181,3 +181,11 @@ def test_binding_rejects_host_tensors():
     q = torch.zeros(1, 4, 1, 32)
     with pytest.raises(ValueError):
         attn.attn_fwd(q, q, q)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: without libattn.so the first call raises ImportError."""
+    monkeypatch.setattr(attn, "LIB_PATH", str(tmp_path / "libattn.so"))
+    monkeypatch.setattr(attn, "_lib", None)
+    with pytest.raises(ImportError):
+        attn.load()
