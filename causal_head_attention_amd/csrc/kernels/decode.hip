@@ -1,13 +1,15 @@
 // decode.hip -- single-query attention against a KV cache, split along the keys.
 //
-// Split kernel: workgroup (split, h, b) takes keys [256*split, 256*split+256)
-// of sequence b (clipped to its length; workgroups past the length exit at
-// once). Each of its 4 waves streams 64 keys: a key's head vector is one
-// contiguous row, read by D*sizeof(T)/16 lanes with 16-byte loads, so a wave
-// load instruction covers several keys and every load of the wave is issued
-// before the first score is needed. Scores are reduced across the lanes of a
-// key with shuffles, the wave's softmax state (max, sum, D accumulators) is
-// merged across waves in LDS, and the workgroup writes one partial state.
+// Split kernel: workgroup (split, b) takes keys [64*split, 64*split+64) of
+// sequence b (clipped to its length; workgroups past the length exit at
+// once) for ALL heads. The cache is [B, S_cap, H, D], so one token's H head
+// rows are one contiguous span: each wave owns a group of heads whose rows
+// for one token are read by one 16-byte-per-lane load instruction, and the
+// eight waves of the workgroup together sweep whole token rows. A head's
+// D elements sit in one group of D*sizeof(T)/16 lanes ("a row"), so the dot
+// product reduces with DPP inside the row and the head's softmax state (max,
+// sum, D accumulators) lives in that row; one partial state per (b, h,
+// split) goes to the workspace.
 // Combine kernel: per (b, h), rescale each split's partial state to the
 // common maximum, add, divide by the common sum. Splits are merged in a
 // fixed order, so results do not change from run to run.
@@ -19,7 +21,8 @@
 // blocks ("Week-4 CUDA notes" page, section 2.2); partial reductions in
 // the wave, final reduction per block (MMHA page, section 1); grouping
 // work of irregular length instead of letting it diverge ("CUDA first
-// principles" page, section 4.4).
+// principles" page, section 4.4); contiguous, coalesced loads ("CUDA first
+// principles" page, section 3.2).
 #include <hip/hip_runtime.h>
 
 #include "../launch.h"
@@ -29,6 +32,7 @@ namespace attn {
 namespace {
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 template <typename T>
 struct Elem;
@@ -51,7 +55,46 @@ struct Elem<__bf16> {
     }
 };
 
+constexpr int kNonTemporal = 2;   // buffer-load cache policy: nt
+
 __device__ __forceinline__ int clamp_len(int n, int S_cap) { return n < 0 ? 0 : (n > S_cap ? S_cap : n); }
+
+// DPP lane moves inside 16-lane rows (gfx9 encodings).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kQuadSwap1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7-i within 8
+constexpr int kRowMirror = 0x140;      // lane i <-> 15-i within 16
+
+// Sum over groups of N consecutive lanes (N = 4, 8, 16 or 32); every lane of
+// the group gets the total.
+template <int N>
+__device__ __forceinline__ float row_sum(float x) {
+    x += dpp<kQuadSwap1>(x);
+    x += dpp<kQuadSwap2>(x);
+    if constexpr (N >= 8) x += dpp<kRowHalfMirror>(x);
+    if constexpr (N >= 16) x += dpp<kRowMirror>(x);
+    if constexpr (N >= 32) x += __shfl_xor(x, 16);
+    return x;
+}
+
+template <typename T, int D>
+struct DecCfg {
+    static constexpr int E = Elem<T>::PER16;     // elements per 16-byte chunk
+    static constexpr int LPH = D / E;            // lanes per head row
+    static constexpr int HPI = 64 / LPH;         // heads per wave load instruction
+};
+
+// Descriptor over sequence b's cache rows ([S_cap, H, D] slice); reads past
+// the slice return zeros.
+template <typename T, int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const T* base, int b, int S_cap, int H) {
+    const T* p = base + (size_t)b * S_cap * H * D;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, S_cap * H * D * (int)sizeof(T), 0x00020000);
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(const T* __restrict__ q,
@@ -60,165 +103,195 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(const T* _
                                                                       const int32_t* __restrict__ seqlens,
                                                                       float* __restrict__ ws, int H, int S_cap,
                                                                       int n_split_max, float c) {
-    constexpr int E = Elem<T>::PER16;                // elements per 16-byte chunk
-    constexpr int LPK = D / E;                       // lanes per key
-    constexpr int KPI = 64 / LPK;                    // keys per wave load instruction
-    constexpr int NIT = kDecodeKeysPerWave / KPI;    // load instructions per wave
-    constexpr int NB = NIT < 16 ? NIT : 16;          // loads in flight per batch
-    static_assert(NIT % NB == 0, "batching");
-
-    __shared__ float sm[kDecodeWaves], sl[kDecodeWaves];
-    __shared__ float sacc[kDecodeWaves][D];
+    using C = DecCfg<T, D>;
+    constexpr int E = C::E, LPH = C::LPH, HPI = C::HPI;
+    constexpr bool kBf16 = sizeof(T) == 2;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int split = (int)(blockIdx.x % (unsigned)n_split_max);
-    const int bh = (int)(blockIdx.x / (unsigned)n_split_max);
-    const int h = bh % H, b = bh / H;
+    const int b = (int)(blockIdx.x / (unsigned)n_split_max);
     const int len = clamp_len(seqlens[b], S_cap);
-    if (split * kDecodeChunk >= len) return;   // uniform for the whole workgroup
+    const int k0 = split * kDecodeChunk;
+    if (k0 >= len) return;   // uniform for the whole workgroup
+    const int k1 = min(len, k0 + kDecodeChunk);
+    const int sub = lane % LPH, hl = lane / LPH;
+    const __amdgpu_buffer_rsrc_t rk = seq_rsrc<T, D>(kc, b, S_cap, H);
+    const __amdgpu_buffer_rsrc_t rv = seq_rsrc<T, D>(vc, b, S_cap, H);
+    const int key_bytes = H * D * (int)sizeof(T);
+    const int n_groups = (H + HPI - 1) / HPI;
 
-    const int kend = min(len, (split + 1) * kDecodeChunk);
-    const int kstart = split * kDecodeChunk + wave * kDecodeKeysPerWave;
-    const int sub = lane % LPK, kl = lane / LPK;
+    for (int grp = wave; grp < n_groups; grp += kDecodeWaves) {
+        const int h = grp * HPI + hl;
+        const bool h_ok = h < H;
+        const int lane_off = ((h_ok ? h : 0) * D + E * sub) * (int)sizeof(T);
 
-    float qv[E];
-    {
-        const u32x4_t x = *(const u32x4_t*)(q + ((size_t)b * H + h) * D + E * sub);
+        // this row's query chunk; bf16 stays packed (exact) for v_dot2 and the
+        // scale is applied to the reduced score
+        const u32x4_t qx = *(const u32x4_t*)(q + ((size_t)b * H + (h_ok ? h : 0)) * D + E * sub);
+        float qf[E];
+        if constexpr (!kBf16) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) qv[e] = Elem<T>::get(x, e) * c;
-    }
+            for (int e = 0; e < E; ++e) qf[e] = Elem<T>::get(qx, e);
+        }
 
-    float m_run = -INFINITY, l_run = 0.f, acc[E];
+        float m_run = -INFINITY, l_run = 0.f, acc[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+        for (int e = 0; e < E; ++e) acc[e] = 0.f;
 
+        for (int kb = k0; kb < k1; kb += kDecodeBatch) {
+            u32x4_t kr[kDecodeBatch], vr[kDecodeBatch];
 #pragma unroll
-    for (int bt = 0; bt < NIT / NB; ++bt) {
-        u32x4_t kr[NB], vr[NB];
-        const u32x4_t zero = {0u, 0u, 0u, 0u};
+            for (int it = 0; it < kDecodeBatch; ++it) {
+                const int off = lane_off + (kb + it) * key_bytes;
+                // read-once stream: non-temporal, so the loads do not allocate
+                // in the caches (and do not evict whatever is resident there)
+                kr[it] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kNonTemporal);
+                vr[it] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, kNonTemporal);
+            }
+            float s[kDecodeBatch];
 #pragma unroll
-        for (int it = 0; it < NB; ++it) {
-            const int key = kstart + (bt * NB + it) * KPI + kl;
-            kr[it] = zero;
-            vr[it] = zero;
-            if (key < kend) {
-                const size_t off = ((size_t)((size_t)b * S_cap + key) * H + h) * D + E * sub;
-                kr[it] = *(const u32x4_t*)(kc + off);
-                vr[it] = *(const u32x4_t*)(vc + off);
+            for (int it = 0; it < kDecodeBatch; ++it) {
+                float d = 0.f;
+                if constexpr (kBf16) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        // scalar copies first (bit-casting a vector-element lvalue
+                        // reads element 0 with this compiler)
+                        const unsigned kw = kr[it][w], qw = qx[w];
+                        d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kw),
+                                                            __builtin_bit_cast(bf16x2_t, qw), d, false);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) d = __builtin_fmaf(qf[e], Elem<T>::get(kr[it], e), d);
+                }
+                d = row_sum<LPH>(d) * c;
+                s[it] = (kb + it < k1) ? d : -INFINITY;
+            }
+            // slots past the length may hold anything (even NaN): their
+            // probability is 0, and their values must not reach the sums
+            if (kb + kDecodeBatch > k1) {
+                const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int it = 0; it < kDecodeBatch; ++it)
+                    if (kb + it >= k1) vr[it] = zero;
+            }
+            float mx = s[0];
+#pragma unroll
+            for (int it = 1; it < kDecodeBatch; ++it) mx = fmaxf(mx, s[it]);
+            const float m_new = fmaxf(m_run, mx);   // finite: key kb < k1 is valid
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] *= alpha;
+            m_run = m_new;
+            if constexpr (kBf16) {
+                // pairs of keys: P rounded to bf16, V pairs packed per head dim,
+                // one v_dot2 per (pair, dim); the sum adds the same rounded P
+#pragma unroll
+                for (int it = 0; it < kDecodeBatch; it += 2) {
+                    const bf16x2_t pp = {(__bf16)__builtin_amdgcn_exp2f(s[it] - m_new),
+                                         (__bf16)__builtin_amdgcn_exp2f(s[it + 1] - m_new)};
+                    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const unsigned va = (vr[it][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                        const unsigned vb = (vr[it + 1][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                        acc[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, va | (vb << 16)), pp,
+                                                                 acc[e], false);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int it = 0; it < kDecodeBatch; ++it) {
+                    const float p = __builtin_amdgcn_exp2f(s[it] - m_new);
+                    l_run += p;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(p, Elem<T>::get(vr[it], e), acc[e]);
+                }
             }
         }
-        float s[NB];
+        // one partial record per (b, h, split): [max, sum, D accumulators]
+        if (h_ok) {
+            float* rec = ws + (((size_t)b * H + h) * n_split_max + split) * (D + 2);
+            if (sub == 0) {
+                rec[0] = m_run;
+                rec[1] = l_run;
+            }
 #pragma unroll
-        for (int it = 0; it < NB; ++it) {
-            float d = 0.f;
-#pragma unroll
-            for (int e = 0; e < E; ++e) d = __builtin_fmaf(qv[e], Elem<T>::get(kr[it], e), d);
-#pragma unroll
-            for (int m = LPK / 2; m >= 1; m >>= 1) d += __shfl_xor(d, m);
-            const int key = kstart + (bt * NB + it) * KPI + kl;
-            s[it] = key < kend ? d : -INFINITY;
+            for (int e = 0; e < E; ++e) rec[2 + E * sub + e] = acc[e];
         }
-        float mx = s[0];
-#pragma unroll
-        for (int it = 1; it < NB; ++it) mx = fmaxf(mx, s[it]);
-#pragma unroll
-        for (int m = LPK; m < 64; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        float ls = 0.f, part[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) part[e] = 0.f;
-#pragma unroll
-        for (int it = 0; it < NB; ++it) {
-            const float p = __builtin_amdgcn_exp2f(s[it] - m_use);
-            ls += p;
-#pragma unroll
-            for (int e = 0; e < E; ++e) part[e] = __builtin_fmaf(p, Elem<T>::get(vr[it], e), part[e]);
-        }
-        l_run = l_run * alpha + ls;
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = acc[e] * alpha + part[e];
-        m_run = m_new;
-    }
-    // sum over the key groups of the wave (lanes with equal `sub`)
-#pragma unroll
-    for (int m = LPK; m < 64; m <<= 1) {
-        l_run += __shfl_xor(l_run, m);
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] += __shfl_xor(acc[e], m);
-    }
-    if (lane == 0) {
-        sm[wave] = m_run;
-        sl[wave] = l_run;
-    }
-    if (kl == 0) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) sacc[wave][E * sub + e] = acc[e];
-    }
-    __syncthreads();
-
-    float* rec = ws + ((size_t)bh * n_split_max + split) * (D + 2);
-    float M = sm[0];
-#pragma unroll
-    for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, sm[w]);   // finite: wave 0 has a valid key
-    float wt[kDecodeWaves];
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) wt[w] = __builtin_amdgcn_exp2f(sm[w] - M);
-    for (int d = tid; d < D; d += kDecodeThreads) {
-        float a = 0.f;
-#pragma unroll
-        for (int w = 0; w < kDecodeWaves; ++w) a = __builtin_fmaf(wt[w], sacc[w][d], a);
-        rec[2 + d] = a;
-    }
-    if (tid == 0) {
-        float L = 0.f;
-#pragma unroll
-        for (int w = 0; w < kDecodeWaves; ++w) L = __builtin_fmaf(wt[w], sl[w], L);
-        rec[0] = M;
-        rec[1] = L;
     }
 }
 
+// Combine: one workgroup per (b, h). The split maxima and sums are read in
+// parallel (one split per thread), reduced in LDS, and every thread then
+// owns one head dim and adds the rescaled accumulators of all splits.
 template <typename T, int D>
-__global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ ws,
-                                                             const int32_t* __restrict__ seqlens,
-                                                             T* __restrict__ o, int H, int S_cap, int n_split_max) {
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const float* __restrict__ ws,
+                                                                         const int32_t* __restrict__ seqlens,
+                                                                         T* __restrict__ o, int H, int S_cap,
+                                                                         int n_split_max) {
+    __shared__ float w_s[kDecodeMaxSplits];
+    __shared__ float red[kCombineThreads / 64];
     const int bh = blockIdx.x;
     const int b = bh / H;
-    const int d = threadIdx.x;
-    if (d >= D) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int len = clamp_len(seqlens[b], S_cap);
-    T* out = o + (size_t)bh * D;   // [B, 1, H, D]: (b, h) row is bh
+    T* out = o + (size_t)bh * D;   // [B, 1, H, D]: the (b, h) row is bh
     if (len == 0) {
-        out[d] = (T)0.f;
+        for (int d = tid; d < D; d += kCombineThreads) out[d] = (T)0.f;
         return;
     }
     const int ns = (len + kDecodeChunk - 1) / kDecodeChunk;
     const float* rec = ws + (size_t)bh * n_split_max * (D + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, rec[(size_t)s * (D + 2)]);
-    float L = 0.f, a = 0.f;
-    for (int s = 0; s < ns; ++s) {
-        const float* r = rec + (size_t)s * (D + 2);
-        const float w = __builtin_amdgcn_exp2f(r[0] - M);
-        L = __builtin_fmaf(w, r[1], L);
-        a = __builtin_fmaf(w, r[2 + d], a);
+    // common maximum
+    float m = -INFINITY;
+    for (int s = tid; s < ns; s += kCombineThreads) m = fmaxf(m, rec[(size_t)s * (D + 2)]);
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) m = fmaxf(m, __shfl_xor(m, x));
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    float M = red[0];
+#pragma unroll
+    for (int w = 1; w < kCombineThreads / 64; ++w) M = fmaxf(M, red[w]);
+    __syncthreads();
+    // per-split weights and the common sum
+    float L = 0.f;
+    for (int s = tid; s < ns; s += kCombineThreads) {
+        const float w = __builtin_amdgcn_exp2f(rec[(size_t)s * (D + 2)] - M);
+        w_s[s] = w;
+        L = __builtin_fmaf(w, rec[(size_t)s * (D + 2) + 1], L);
     }
-    out[d] = (T)(a / L);
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) L += __shfl_xor(L, x);
+    if (lane == 0) red[wave] = L;
+    __syncthreads();
+    float Lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < kCombineThreads / 64; ++w) Lt += red[w];
+    const float inv = 1.0f / Lt;
+    for (int d = tid; d < D; d += kCombineThreads) {
+        float a = 0.f;
+#pragma unroll 8
+        for (int s = 0; s < ns; ++s) a = __builtin_fmaf(w_s[s], rec[(size_t)s * (D + 2) + 2 + d], a);
+        out[d] = (T)(a * inv);
+    }
 }
 
 template <typename T, int D>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
     const int nsm = decode_n_split_max(a.S_cap);
-    const unsigned grid1 = (unsigned)((long long)nsm * a.H * a.B);
+    const unsigned grid1 = (unsigned)((long long)nsm * a.B);
     hipExtLaunchKernelGGL((decode_split_kernel<T, D>), dim3(grid1), dim3(kDecodeThreads), 0, stream, a.ev_start,
                           nullptr, 0, (const T*)a.q, (const T*)a.kcache, (const T*)a.vcache, a.seqlens, a.workspace,
                           a.H, a.S_cap, nsm, a.scale_log2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipExtLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)(a.H * a.B)), dim3(128), 0, stream, nullptr,
-                          a.ev_stop, 0, (const float*)a.workspace, a.seqlens, (T*)a.o, a.H, a.S_cap, nsm);
+    hipExtLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)(a.H * a.B)), dim3(kCombineThreads), 0,
+                          stream, nullptr, a.ev_stop, 0, (const float*)a.workspace, a.seqlens, (T*)a.o, a.H,
+                          a.S_cap, nsm);
     return hipGetLastError();
 }
 

@@ -88,13 +88,17 @@ constexpr int kRowThreads = 64;
 
 // ---------------------------------------------------------------------------
 // Split-KV decode.
-//   Split kernel: one workgroup per (split, h, b), 4 waves, 64 keys per wave.
+//   Split kernel: one workgroup per (split, b) covering ALL heads of keys
+//   [64*split, 64*split+64): each wave owns a group of heads, each load
+//   instruction reads one token's rows of those heads (contiguous bytes).
 //   Combine kernel: one workgroup per (h, b).
 // ---------------------------------------------------------------------------
-constexpr int kDecodeWaves = 4;
-constexpr int kDecodeKeysPerWave = 64;
-constexpr int kDecodeChunk = kDecodeWaves * kDecodeKeysPerWave;   // 256 keys per split
+constexpr int kDecodeWaves = 8;
+constexpr int kDecodeChunk = 64;          // keys per split
+constexpr int kDecodeBatch = 16;          // keys whose loads are in flight together
 constexpr int kDecodeThreads = kDecodeWaves * 64;
+constexpr int kCombineThreads = 128;
+constexpr int kDecodeMaxSplits = 16384;  // S_cap up to 16384 * 64 = 1,048,576 tokens
 
 ATTN_HD inline int decode_n_split_max(int S_cap) {
     return (S_cap + kDecodeChunk - 1) / kDecodeChunk;
