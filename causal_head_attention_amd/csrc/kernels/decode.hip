@@ -225,16 +225,22 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(const T* _
     }
 }
 
-// Combine: one workgroup per (b, h). The split maxima and sums are read in
-// parallel (one split per thread), reduced in LDS, and every thread then
-// owns one head dim and adds the rescaled accumulators of all splits.
+// Combine: one workgroup per (b, h). The split maxima are read in parallel
+// (one split per thread) and reduced; each split's weight exp2(m_s - M) goes
+// to LDS with the common sum. Then thread (part, d) adds the weighted
+// accumulators of head dim d for the splits s = part, part + P, ... with all
+// of its loads issued before the first add, and the P parts are summed in
+// LDS. Fixed order throughout, so the result is deterministic.
 template <typename T, int D>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const float* __restrict__ ws,
                                                                          const int32_t* __restrict__ seqlens,
                                                                          T* __restrict__ o, int H, int S_cap,
                                                                          int n_split_max) {
+    constexpr int P = kCombineThreads / D;        // split parts
+    constexpr int PER = 16;                       // loads in flight per thread per round
     __shared__ float w_s[kDecodeMaxSplits];
     __shared__ float red[kCombineThreads / 64];
+    __shared__ float part_acc[P][D];
     const int bh = blockIdx.x;
     const int b = bh / H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -271,12 +277,29 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const f
     float Lt = 0.f;
 #pragma unroll
     for (int w = 0; w < kCombineThreads / 64; ++w) Lt += red[w];
-    const float inv = 1.0f / Lt;
-    for (int d = tid; d < D; d += kCombineThreads) {
-        float a = 0.f;
-#pragma unroll 8
-        for (int s = 0; s < ns; ++s) a = __builtin_fmaf(w_s[s], rec[(size_t)s * (D + 2) + 2 + d], a);
-        out[d] = (T)(a * inv);
+    // weighted accumulators: thread (part, d)
+    const int d = tid % D, part = tid / D;
+    float a = 0.f;
+    for (int s0 = part; s0 < ns; s0 += P * PER) {
+        float x[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int s = s0 + j * P;
+            x[j] = s < ns ? rec[(size_t)s * (D + 2) + 2 + d] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int s = s0 + j * P;
+            if (s < ns) a = __builtin_fmaf(w_s[s], x[j], a);
+        }
+    }
+    part_acc[part][d] = a;
+    __syncthreads();
+    if (tid < D) {
+        float t = 0.f;
+#pragma unroll
+        for (int q = 0; q < P; ++q) t += part_acc[q][tid];
+        out[tid] = (T)(t / Lt);
     }
 }
 

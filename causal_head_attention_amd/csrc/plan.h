@@ -97,7 +97,7 @@ constexpr int kDecodeWaves = 8;
 constexpr int kDecodeChunk = 64;          // keys per split
 constexpr int kDecodeBatch = 16;          // keys whose loads are in flight together
 constexpr int kDecodeThreads = kDecodeWaves * 64;
-constexpr int kCombineThreads = 128;
+constexpr int kCombineThreads = 512;
 constexpr int kDecodeMaxSplits = 16384;  // S_cap up to 16384 * 64 = 1,048,576 tokens
 
 ATTN_HD inline int decode_n_split_max(int S_cap) {
