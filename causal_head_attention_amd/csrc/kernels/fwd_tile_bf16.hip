@@ -316,14 +316,6 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
                     m_ref = m_new;
                 }
                 const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-                // V^T operands of this tile (read early: their LDS latency then
-                // overlaps the exponentials below)
-                const char* vt = vst(t & 1) + v_lane;
-                bf16x8_t va[C::DB][2];
-#pragma unroll
-                for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) va[db][s2] = *(const bf16x8_t*)(vt + 32 * db * C::VROW + 32 * s2);
                 // (d) next tile's scores on the matrix cores, interleaved with
                 // this tile's exponentials on the vector ALUs
                 s_n = qk_tile<D>(kst((t + 1) & 1) + k_lane, qf);
@@ -343,21 +335,35 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
                         l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, l_run, false);
                     }
                 }
-                // (e) O^T += V^T . P^T
+                // (e) O^T += V^T . P^T; the V^T operands are read once the
+                // S(t+1) operands are consumed, so both sets share registers
+                const char* vt = vst(t & 1) + v_lane;
+                bf16x8_t va[C::DB][2];
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) va[db][s2] = *(const bf16x8_t*)(vt + 32 * db * C::VROW + 32 * s2);
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db)
 #pragma unroll
                     for (int s2 = 0; s2 < 2; ++s2)
                         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][s2], pb[s2], acc[db], 0, 0, 0);
-                // schedule: all K and V operand reads first, then the S(t+1)
-                // MFMAs each followed by a slice of the softmax VALU work,
-                // then the P.V MFMAs
+                // schedule: all K operand reads first, then the S(t+1) MFMAs
+                // each followed by a slice of the softmax VALU work, then the
+                // V^T operand reads and the P.V MFMAs
                 __builtin_amdgcn_sched_group_barrier(0x100, C::KS, 0);
 #pragma unroll
-                for (int i = 0; i < C::KS; ++i) {
+                for (int i = 0; i < C::KS / 2; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
                 }
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::DB, 0);
+#pragma unroll
+                for (int i = 0; i < C::KS / 2; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::DB, 0);
             }
             // (f) land the prefetched tiles in the stages read one iteration ago
             if (ld_k) store_k<D>(pre, kst(t & 1), tid);
