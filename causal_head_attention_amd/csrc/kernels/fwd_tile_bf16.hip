@@ -335,6 +335,10 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
                         l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, l_run, false);
                     }
                 }
+                // The two waves sharing a SIMD run the same program in step; a
+                // raised issue priority from here to the barrier lets one wave's
+                // P.V MFMAs run while the other still works on its softmax.
+                __builtin_amdgcn_s_setprio(2);
                 // (e) O^T += V^T . P^T; the V^T operands are read once the
                 // S(t+1) operands are consumed, so both sets share registers
                 const char* vt = vst(t & 1) + v_lane;
@@ -368,6 +372,7 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
             // (f) land the prefetched tiles in the stages read one iteration ago
             if (ld_k) store_k<D>(pre, kst(t & 1), tid);
             if (ld_v) store_v<D>(pre, vst((t + 1) & 1), tid);
+            __builtin_amdgcn_s_setprio(0);
             __syncthreads();
         };
         for (int t = 0; t < nt; t += 2) {
