@@ -200,6 +200,13 @@ __device__ __forceinline__ f32x16_t qk_tile(const char* krow, const bf16x8_t (&q
     return s;
 }
 
+// Workgroup barrier that only orders LDS traffic: unlike __syncthreads it
+// does not wait for this wave's global loads and stores, so loads issued for
+// the next block and the output stores stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Row maxima are only re-based when they grow by more than 2^kLazy: until
 // then probabilities are taken against a stale maximum (at most 2^kLazy,
 // far from fp32/bf16 overflow) and the accumulators are left alone. The
@@ -240,6 +247,23 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
     const __amdgpu_buffer_rsrc_t rq = head_rsrc<D>(Q, b, h, S_q, H);
     const __amdgpu_buffer_rsrc_t ro = head_rsrc<D>((const __bf16*)O, b, h, S_q, H);
 
+    // The loads that open a query block: its Q^T fragments (B operand: lane
+    // holds query qi, head dims 16*ks + 8*g .. +7) and tile 0 of K and V.
+    // They are issued before the previous block's merge, so their latency
+    // overlaps it.
+    bf16x8_t qf[C::KS];
+    u32x4_t pre[C::NPRE];
+    auto issue_block = [&](int qb) {
+        const int qi = qb * kTileM + 32 * wq + l32;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+            qf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rq, tok_off<D>(qi, 2 * ks + g, H), 0, 0));
+        if (k_loader) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_kv, H, 0), H, tid);
+        else load_v<D>(pre, tile_rsrc<D>(V, b, h, S_kv, H, 0), H, tid);
+    };
+    issue_block(qb_first);
+
     for (int phase = 0; phase < nphase; ++phase) {
         const int qb = phase == 0 ? qb_first : p;
         const int nt = tiles_for_block(qb, S_q, S_kv, causal);
@@ -250,13 +274,6 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
         const int key_last = causal ? q_last + off : S_kv - 1;   // last key any row of the wave sees
         const int lane_key_limit = causal ? qi + off : S_kv - 1; // last key this lane sees
 
-        // Q^T fragments (B operand): lane holds query qi, head dims 16*ks + 8*g .. +7.
-        bf16x8_t qf[C::KS];
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-            qf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     rq, tok_off<D>(qi, 2 * ks + g, H), 0, 0));
-
         f32x16_t acc[C::DB];
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
@@ -266,14 +283,8 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
         float l_run = 0.f;         // this lane's share of the running sum
 
         // Prologue: tile 0 (K and V) staged; S(0) computed while K(1) lands.
-        u32x4_t pre[C::NPRE];
-        if (k_loader) {
-            load_k<D>(pre, tile_rsrc<D>(K, b, h, S_kv, H, 0), H, tid);
-            store_k<D>(pre, kst(0), tid);
-        } else {
-            load_v<D>(pre, tile_rsrc<D>(V, b, h, S_kv, H, 0), H, tid);
-            store_v<D>(pre, vst(0), tid);
-        }
+        if (k_loader) store_k<D>(pre, kst(0), tid);
+        else store_v<D>(pre, vst(0), tid);
         __syncthreads();
         if (k_loader && nt > 1) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_kv, H, kTileN), H, tid);
         // unconditional: every path into the loop has then waited for the Q
@@ -380,6 +391,9 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
             if (t + 1 < nt) step(t + 1, sb, sa);
         }
 
+        // the next block's opening loads run under this block's merge
+        if (phase + 1 < nphase) issue_block(p);
+
         // ---- merge the two key halves (waves wq and wq+4) through LDS
         float* xf = (float*)lds;
         float* slot = xf + wq * (64 * (C::DB * 16 + 2));
@@ -391,7 +405,7 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) slot[128 + (db * 16 + r) * 64 + lane] = acc[db][r];
         }
-        __syncthreads();
+        lds_barrier();
         if (half == 0 && wave_has_rows) {
             const float m1 = slot[lane];
             const float l1 = slot[64 + lane];
@@ -419,7 +433,7 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
                                                           (qi * H * D + 32 * db + 8 * j + 4 * g) * 2, 0, 0);
                 }
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
