@@ -91,7 +91,62 @@ class HipEvents:
             self.rt.hipEventDestroy(self.ct.c_void_p(h))
 
 
+def traffic_from_counters(fetch_csv: str, write_csv: str, copy_mib: int = 256) -> dict:
+    """Turn two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch) of `bench.py --copy-calibration MIB` into HBM bytes per launch.
+
+    Each counter is scaled by what it reads for the calibration copy (the
+    largest `__amd_rocclr_copyBuffer` dispatch: copy_mib MiB read and written).
+    The result is keyed by the SHA-256 of the kernel sources it was taken on."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    copy_kib = copy_mib * 1024.0
+    f_scale = copy_kib / max(fetch["__amd_rocclr_copyBuffer"])
+    w_scale = copy_kib / max(write["__amd_rocclr_copyBuffer"])
+
+    def mean_of(vals, key):
+        xs = [v for name, v in vals.items() if key in name]
+        assert len(xs) == 1, f"{key}: {len(xs)} kernels match"
+        return statistics.fmean(xs[0])
+
+    out = {"note": (f"HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each "
+                    f"scaled by what the counter reads for a {copy_mib} MiB device copy: FETCH_SIZE x {f_scale:.5f}, "
+                    f"WRITE_SIZE x {w_scale:.5f}.")}
+    rows = []
+    prefill = {"fetch_kib": mean_of(fetch, "fwd_tile_bf16_kernelILi128"),
+               "write_kib": mean_of(write, "fwd_tile_bf16_kernelILi128")}
+    split = {"fetch_kib": mean_of(fetch, "decode_split_kernelIDF16bLi128"),
+             "write_kib": mean_of(write, "decode_split_kernelIDF16bLi128")}
+    comb = {"fetch_kib": mean_of(fetch, "decode_combine_kernelIDF16bLi128"),
+            "write_kib": mean_of(write, "decode_combine_kernelIDF16bLi128")}
+    pb = round((prefill["fetch_kib"] * f_scale + prefill["write_kib"] * w_scale) * 1024)
+    db = round(((split["fetch_kib"] + comb["fetch_kib"]) * f_scale + (split["write_kib"] + comb["write_kib"]) * w_scale)
+               * 1024)
+    out["fwd_tile_bf16"] = {"bytes_per_launch": pb, "algorithmic_bytes": 4 * 2048 * 32 * 128 * 2,
+                            "counters_kib": prefill, "source_sha256": sha256(TILE_SRC)}
+    out["decode"] = {"bytes_per_launch": db, "counters_kib": {"split": split, "combine": comb},
+                     "source_sha256": sha256(DECODE_SRC), "note": "one call = split + combine kernels"}
+    out["scales"] = {"fetch": f_scale, "write": w_scale}
+    return out
+
+
 def main() -> int:
+    if len(sys.argv) >= 2 and sys.argv[1] == "--traffic-from":
+        # bench.py --traffic-from FETCH_CSV WRITE_CSV: write profiles/traffic.json
+        doc = traffic_from_counters(sys.argv[2], sys.argv[3])
+        json.dump(doc, open(TRAFFIC_JSON, "w"), indent=1)
+        print(json.dumps(doc, indent=1))
+        return 0
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
