@@ -207,6 +207,16 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// The value lane l^32 holds (v_permlane32_swap: the two half-waves trade
+// registers, no LDS round trip).
+__device__ __forceinline__ float partner_lane(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto pr = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    // lanes 0-31 find the upper half's value in the second result, lanes 32-63 in the first
+    const unsigned lo = pr[0], hi = pr[1];
+    return __builtin_bit_cast(float, (__lane_id() < 32) ? hi : lo);
+}
+
 // Row maxima are only re-based when they grow by more than 2^kLazy: until
 // then probabilities are taken against a stale maximum (at most 2^kLazy,
 // far from fp32/bf16 overflow) and the accumulators are left alone. The
@@ -315,7 +325,7 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
                 float mx = s_c[0];
 #pragma unroll
                 for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_c[r]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+                mx = fmaxf(mx, partner_lane(mx)) * c;   // row max over both half-waves
                 if (__builtin_amdgcn_ballot_w64(mx > m_ref + kLazy)) {
                     const float m_new = fmaxf(m_ref, mx);
                     const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -346,10 +356,6 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
                         l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, l_run, false);
                     }
                 }
-                // The two waves sharing a SIMD run the same program in step; a
-                // raised issue priority from here to the barrier lets one wave's
-                // P.V MFMAs run while the other still works on its softmax.
-                __builtin_amdgcn_s_setprio(2);
                 // (e) O^T += V^T . P^T; the V^T operands are read once the
                 // S(t+1) operands are consumed, so both sets share registers
                 const char* vt = vst(t & 1) + v_lane;
@@ -383,7 +389,6 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
             // (f) land the prefetched tiles in the stages read one iteration ago
             if (ld_k) store_k<D>(pre, kst(t & 1), tid);
             if (ld_v) store_v<D>(pre, vst((t + 1) & 1), tid);
-            __builtin_amdgcn_s_setprio(0);
             __syncthreads();
         };
         for (int t = 0; t < nt; t += 2) {
@@ -414,7 +419,7 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
             const float a0 = __builtin_amdgcn_exp2f(m_ref - mu);
             const float a1 = __builtin_amdgcn_exp2f(m1 - mu);
             float l = a0 * l_run + a1 * l1;
-            l += __shfl_xor(l, 32);
+            l += partner_lane(l);
             const float inv = 1.0f / l;
 #pragma unroll
             for (int db = 0; db < C::DB; ++db)
