@@ -6,7 +6,9 @@ link step writes ``causal_head_attention_amd/libattn.so``.
 """
 from __future__ import annotations
 
+import json
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -43,25 +45,58 @@ def hipcc() -> str:
     return exe
 
 
-def _compile(src: str) -> str:
+RESOURCES = os.path.join(BUILD_DIR, "kernel_resources.json")
+_REMARK = re.compile(r"remark:\s+(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]|"
+                     r"SGPRs Spill|VGPRs Spill|LDS Size \[bytes/block\]):\s+(\S+)")
+
+
+def _resources(text: str) -> dict:
+    """Per-kernel register, scratch, spill and LDS figures from hipcc's
+    kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for m in _REMARK.finditer(text):
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[key.split(" [")[0]] = int(val)
+    return out
+
+
+def _compile(src: str) -> tuple[str, dict]:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    hip = src.endswith(".hip")
+    lang = ["-x", "hip", "-Rpass-analysis=kernel-resource-usage"] if hip else []
     cmd = [hipcc()] + COMMON + DEVICE_FLAGS + lang + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)"
-    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln and ln.strip()]
+    text = r.stdout + r.stderr
+    noise = ("'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)",
+             "[-Rpass-analysis=kernel-resource-usage]")
+    # keep real diagnostics; drop the resource remarks and their source excerpts
+    msgs = [ln for ln in text.splitlines() if ln.strip() and not any(n in ln for n in noise)
+            and not re.match(r"^\s*(\d+\s*)?[|^]", ln)]
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n" + "\n".join(msgs))
     if msgs:
         print("\n".join(msgs), file=sys.stderr)
-    return obj
+    return obj, _resources(text)
 
 
 def build(jobs: int = 4) -> str:
     """Compile every HIP/C++ source for gfx950 and link ``libattn.so``."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        done = list(ex.map(_compile, SOURCES))
+    objs = [o for o, _ in done]
+    res = {}
+    for _, r in done:
+        res.update(r)
+    with open(RESOURCES, "w") as f:
+        json.dump(res, f, indent=1, sort_keys=True)
+    for name, r in res.items():
+        if r.get("ScratchSize", 0) or r.get("VGPRs Spill", 0):
+            print(f"warning: {name} uses {r.get('ScratchSize')} B/lane of scratch "
+                  f"({r.get('VGPRs Spill')} VGPRs spilled)", file=sys.stderr)
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     subprocess.run(cmd, check=True, capture_output=True, text=True)

@@ -191,3 +191,18 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(attn, "_lib", None)
     with pytest.raises(ImportError):
         attn.load()
+
+
+def test_kernels_use_no_scratch():
+    """Every kernel keeps its state in registers and LDS: a register array
+    indexed at run time, or a spill, would move it to scratch memory (a
+    several-fold slowdown). The figures come from hipcc's resource report,
+    which the build writes next to its objects."""
+    import json
+    path = os.path.join(ROOT, "_build", "kernel_resources.json")
+    if not os.path.exists(path):
+        pytest.skip("no build report (build the library first)")
+    res = json.load(open(path))
+    assert any("fwd_tile_bf16_kernel" in k for k in res), "report lists the tile kernel"
+    bad = {k: v for k, v in res.items() if v.get("ScratchSize", 0) or v.get("VGPRs Spill", 0)}
+    assert not bad, bad
