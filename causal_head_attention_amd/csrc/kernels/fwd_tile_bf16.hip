@@ -11,6 +11,11 @@
 //   softmax : online (running max, running sum) in fp32, base-2 exponent
 //   O^T    += V^T . P^T          v_mfma_f32_32x32x16_bf16, P rounded to bf16
 //
+// A block walks its KV tiles from the diagonal down to tile 0 (the online
+// softmax does not depend on the order). The workgroups of one head then
+// reach a given tile at different times, the one with the shortest block
+// first, so only one of them waits for its first fetch from HBM.
+//
 // Software pipeline, one barrier per tile: in iteration t a wave computes
 // the scores of tile t+1 on the matrix cores while it runs the softmax of
 // tile t on the vector ALUs, then accumulates P(t) V(t). K tiles are staged
@@ -269,8 +274,9 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
         for (int ks = 0; ks < C::KS; ++ks)
             qf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
                                                      rq, tok_off<D>(qi, 2 * ks + g, H), 0, 0));
-        if (k_loader) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_kv, H, 0), H, tid);
-        else load_v<D>(pre, tile_rsrc<D>(V, b, h, S_kv, H, 0), H, tid);
+        const int first = (tiles_for_block(qb, S_q, S_kv, causal) - 1) * kTileN;   // tiles run backwards
+        if (k_loader) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_kv, H, first), H, tid);
+        else load_v<D>(pre, tile_rsrc<D>(V, b, h, S_kv, H, first), H, tid);
     };
     issue_block(qb_first);
 
@@ -296,7 +302,9 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
         if (k_loader) store_k<D>(pre, kst(0), tid);
         else store_v<D>(pre, vst(0), tid);
         __syncthreads();
-        if (k_loader && nt > 1) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_kv, H, kTileN), H, tid);
+        // step u works on KV tile nt-1-u: the diagonal tile first
+        auto tile_of = [&](int u) { return nt - 1 - u; };
+        if (k_loader && nt > 1) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_kv, H, tile_of(1) * kTileN), H, tid);
         // unconditional: every path into the loop has then waited for the Q
         // loads, so the loop body never waits on them (or on the prefetch)
         f32x16_t sa = qk_tile<D>(kst(0) + k_lane, qf), sb;
@@ -308,11 +316,17 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
             // (a) HBM loads: K two tiles ahead, V one tile ahead
             const bool ld_k = k_loader && t + 2 < nt;
             const bool ld_v = !k_loader && t + 1 < nt;
-            if (ld_k) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_kv, H, (t + 2) * kTileN), H, tid);
-            if (ld_v) load_v<D>(pre, tile_rsrc<D>(V, b, h, S_kv, H, (t + 1) * kTileN), H, tid);
+            if (ld_k) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_kv, H, tile_of(t + 2) * kTileN), H, tid);
+            if (ld_v) load_v<D>(pre, tile_rsrc<D>(V, b, h, S_kv, H, tile_of(t + 1) * kTileN), H, tid);
 
-            const int kbase = t * kTileN + 32 * half;   // first key of this wave's half tile
-            if (wave_has_rows && kbase <= key_last && kbase < S_kv) {
+            const int kbase = tile_of(t) * kTileN + 32 * half;   // first key of this wave's half tile
+            const bool work = wave_has_rows && kbase <= key_last && kbase < S_kv;
+            // a wave skips the tiles whose keys all lie past its last query (the
+            // first ones in this order); the first tile it does see still needs
+            // its scores from here
+            if (!work && t + 1 < nt && wave_has_rows && kbase - kTileN <= key_last && kbase - kTileN < S_kv)
+                s_n = qk_tile<D>(kst((t + 1) & 1) + k_lane, qf);
+            if (work) {
                 // (b) mask: only where the tile crosses the diagonal or the key end
                 if ((causal && kbase + 31 > q0 + off) || (kbase + 32 > S_kv)) {
 #pragma unroll
