@@ -10,7 +10,7 @@ it with ctypes and widens inputs to fp64 exactly. Passages followed: the
 "Hand-written Masked Multi-Head Attention CUDA kernel" page, sections 2,
 2.1 and 2.2 (definition, [B,S,H,D] layout, j <= i), and the "Week-4 CUDA
 notes" page, section 2.2 (unfused softmax(QK^T/sqrt(d))V, -inf mask, max
-subtraction).
+subtraction; the running sum whose log is the log-sum-exp output).
 """
 from __future__ import annotations
 
@@ -53,6 +53,8 @@ def _load():
             lib.oracle_attn_fwd_f64.restype = ctypes.c_int
             lib.oracle_attn_decode_f64.argtypes = [dp, dp, dp, ip, dp] + [ctypes.c_int] * 4
             lib.oracle_attn_decode_f64.restype = ctypes.c_int
+            lib.oracle_attn_fwd_kvcache_f64.argtypes = [dp, dp, dp, ip, dp, dp] + [ctypes.c_int] * 6
+            lib.oracle_attn_fwd_kvcache_f64.restype = ctypes.c_int
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
             _lib = lib
@@ -108,6 +110,35 @@ def attn_decode(q, kcache, vcache, seqlens):
     if rc != 0:
         raise ValueError(f"oracle_attn_decode_f64 rejected the arguments (code {rc})")
     return o
+
+
+def attn_fwd_kvcache(q, kcache, vcache, seqlens=None, causal: bool = True):
+    """Chunk of queries against a KV cache with per-entry lengths, plus log-sum-exp.
+
+    q [B,S_q,H,D]; caches [B,S_cap,H,D]; seqlens int32[B] or None (all S_cap rows).
+    Returns (O [B,S_q,H,D], LSE [B,H,S_q]) as fp64 numpy arrays; rows that see no
+    key are 0 with LSE -inf.
+    """
+    q, kc, vc = _f64(q), _f64(kcache), _f64(vcache)
+    B, S_q, H, D = q.shape
+    S_cap = kc.shape[1]
+    if kc.shape != (B, S_cap, H, D) or vc.shape != kc.shape:
+        raise ValueError("shape mismatch")
+    sl = None
+    if seqlens is not None:
+        if hasattr(seqlens, "numpy"):
+            seqlens = seqlens.cpu().numpy()
+        sl = np.ascontiguousarray(seqlens, dtype=np.int32)
+        if sl.shape != (B,):
+            raise ValueError("seqlens must be int32[B]")
+    o = np.zeros((B, S_q, H, D), dtype=np.float64)
+    lse = np.zeros((B, H, S_q), dtype=np.float64)
+    rc = _load().oracle_attn_fwd_kvcache_f64(
+        _ptr(q), _ptr(kc), _ptr(vc), sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if sl is not None else None,
+        _ptr(o), _ptr(lse), B, H, S_q, S_cap, D, int(bool(causal)))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_fwd_kvcache_f64 rejected the arguments (code {rc})")
+    return o, lse
 
 
 def num_threads() -> int:

@@ -29,7 +29,12 @@
  *   - no clamp of the running max (the MMHA page's section 2.3 clamp is not
  *     part of the definition);
  *   - decode: query b attends keys 0 .. len_b-1 of its cache; len_b <= 0 gives
- *     an all-zero output row and len_b > S_cap is clamped to S_cap.
+ *     an all-zero output row and len_b > S_cap is clamped to S_cap;
+ *   - KV-cache prefill: entry b of a cache holds len_b valid rows and its S_q
+ *     queries are the last S_q positions (query i at len_b - S_q + i); a
+ *     query that sees no key at all gets a zero output row;
+ *   - the log-sum-exp of a row is ln(sum_j exp(S[i][j])) over its visible
+ *     keys (the log of the softmax denominator), -inf for a row with none.
  *
  * The score matrix of one (b, h) is materialised in full (S_q*S_kv doubles),
  * the three stages run as three separate passes over it, and OpenMP only
@@ -61,7 +66,7 @@ static size_t at(long b, long s, long h, long d, long S, long H, long D) {
  * receives the S_q x S_kv probability matrix of this head.
  */
 static int oracle_head(const double* q, const double* k, const double* v, double* o,
-                       double* p_out, long b, long h, long H, long D,
+                       double* p_out, double* lse_out, long b, long h, long H, long D,
                        long S_q, long S_qdim, long S_kv, long S_kdim, int causal,
                        double* S /* scratch, S_q*S_kv */) {
     const double scale = 1.0 / sqrt((double)D);
@@ -85,19 +90,26 @@ static int oracle_head(const double* q, const double* k, const double* v, double
     }
 
     /* Pass 2: softmax of each row: subtract the row max, exponentiate
-     * (exp(-inf) is exactly 0), divide by the row sum. */
+     * (exp(-inf) is exactly 0), divide by the row sum. The log-sum-exp of
+     * the row is m + ln(l). A row with no visible key is all zeros. */
 #pragma omp parallel for schedule(static)
     for (i = 0; i < S_q; ++i) {
         double* row = S + (size_t)i * (size_t)S_kv;
         double m = -INFINITY;
         for (long j = 0; j < S_kv; ++j)
             if (row[j] > m) m = row[j];
+        if (m == -INFINITY) {
+            for (long j = 0; j < S_kv; ++j) row[j] = 0.0;
+            if (lse_out) lse_out[(size_t)(b * H + h) * (size_t)S_q + (size_t)i] = -INFINITY;
+            continue;
+        }
         double l = 0.0;
         for (long j = 0; j < S_kv; ++j) {
             row[j] = exp(row[j] - m);
             l += row[j];
         }
         for (long j = 0; j < S_kv; ++j) row[j] = row[j] / l;
+        if (lse_out) lse_out[(size_t)(b * H + h) * (size_t)S_q + (size_t)i] = m + log(l);
     }
 
     /* Pass 3: O = P V. Each output element is the sum over j = 0, 1, ...
@@ -139,7 +151,7 @@ int oracle_attn_fwd_f64(const double* q, const double* k, const double* v, doubl
     if (!S) return ORACLE_ENOMEM;
     for (long b = 0; b < B; ++b)
         for (long h = 0; h < H; ++h)
-            oracle_head(q, k, v, o, p, b, h, H, D, S_q, S_q, S_kv, S_kv, causal, S);
+            oracle_head(q, k, v, o, p, NULL, b, h, H, D, S_q, S_q, S_kv, S_kv, causal, S);
     free(S);
     return ORACLE_OK;
 }
@@ -167,7 +179,46 @@ int oracle_attn_decode_f64(const double* q, const double* kcache, const double* 
                 for (long d = 0; d < D; ++d) o[at(b, 0, h, d, 1, H, D)] = 0.0;
                 continue;
             }
-            oracle_head(q, kcache, vcache, o, NULL, b, h, H, D, 1, 1, n, S_cap, 1, S);
+            oracle_head(q, kcache, vcache, o, NULL, NULL, b, h, H, D, 1, 1, n, S_cap, 1, S);
+        }
+    }
+    free(S);
+    return ORACLE_OK;
+}
+
+/*
+ * Chunk of queries against a KV cache (chunked prefill), with the
+ * log-sum-exp of every query row.
+ *   q, o            : [B, S_q, H, D]
+ *   kcache, vcache  : [B, S_cap, H, D]
+ *   seqlens         : int32[B] or NULL; entry b holds len_b valid rows,
+ *                     len_b clamped to [0, S_cap] (NULL: S_cap). Query i of
+ *                     entry b sits at position len_b - S_q + i.
+ *   lse             : optional [B, H, S_q] (NULL to skip)
+ * Each (b, h) is the forward above over the len_b valid rows (S_kv = len_b);
+ * the query positions may be negative, and such rows see no key: zero output,
+ * log-sum-exp -inf. len_b == 0 makes every row of the entry such a row.
+ */
+int oracle_attn_fwd_kvcache_f64(const double* q, const double* kcache, const double* vcache,
+                                const int32_t* seqlens, double* o, double* lse, int B, int H, int S_q,
+                                int S_cap, int D, int causal) {
+    if (B <= 0 || H <= 0 || S_q <= 0 || S_cap <= 0 || D <= 0) return ORACLE_EINVAL;
+    if (causal != 0 && causal != 1) return ORACLE_EINVAL;
+    double* S = (double*)malloc(sizeof(double) * (size_t)S_q * (size_t)S_cap);
+    if (!S) return ORACLE_ENOMEM;
+    for (long b = 0; b < B; ++b) {
+        long n = seqlens ? seqlens[b] : S_cap;
+        if (n > S_cap) n = S_cap;
+        if (n < 0) n = 0;
+        for (long h = 0; h < H; ++h) {
+            if (n == 0) {
+                for (long i = 0; i < S_q; ++i) {
+                    for (long d = 0; d < D; ++d) o[at(b, i, h, d, S_q, H, D)] = 0.0;
+                    if (lse) lse[(size_t)(b * H + h) * (size_t)S_q + (size_t)i] = -INFINITY;
+                }
+                continue;
+            }
+            oracle_head(q, kcache, vcache, o, NULL, lse, b, h, H, D, S_q, S_q, n, S_cap, causal, S);
         }
     }
     free(S);

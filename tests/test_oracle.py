@@ -12,6 +12,7 @@ What each kind of mistake would trip:
   wrong S_q != S_kv alignment                               -> golden bottom-right case
   missing normalisation / max subtraction overflow          -> row sums, large-logit test
   decode reading past the length                            -> NaN-filled cache test
+  log-sum-exp without the max, or ignoring the entry lengths -> golden, SDPA/logsumexp, merge pins
 """
 import json
 import math
@@ -89,10 +90,18 @@ def test_golden_geometric_weights():
         k = np.array(case["k"], dtype=np.float64)
         v = np.array(case["v"], dtype=np.float64)
         exact = np.vectorize(lambda s: float(Fraction(s)))(np.array(case["o_exact"], dtype=object))
-        got = oracle.attn_fwd(q, k, v, case["causal"])
-        assert got.shape == exact.shape
-        np.testing.assert_allclose(got, exact.astype(np.float64), rtol=1e-13, atol=1e-14,
-                                   err_msg=case["name"])
+        lse_exact = np.array([[[float(x) for x in row] for row in hb] for hb in case["lse_exact"]])
+        if "seqlens" not in case:
+            got = oracle.attn_fwd(q, k, v, case["causal"])
+            assert got.shape == exact.shape
+            np.testing.assert_allclose(got, exact.astype(np.float64), rtol=1e-13, atol=1e-14,
+                                       err_msg=case["name"])
+        # the KV-cache form, with the case's lengths or none (all rows valid)
+        o2, lse = oracle.attn_fwd_kvcache(q, k, v, case.get("seqlens"), case["causal"])
+        np.testing.assert_allclose(o2, exact.astype(np.float64), rtol=1e-13, atol=1e-14, err_msg=case["name"])
+        assert np.array_equal(np.isneginf(lse), np.isneginf(lse_exact)), case["name"]
+        fin = np.isfinite(lse_exact)
+        np.testing.assert_allclose(lse[fin], lse_exact[fin], rtol=1e-13, atol=1e-13, err_msg=case["name"])
 
 
 def test_two_keys_is_a_logistic_blend():
@@ -262,6 +271,91 @@ def test_decode_empty_and_overlong_lengths():
     o = oracle.attn_decode(q, kc, vc, np.array([0, -4, 99], dtype=np.int32))
     assert np.all(o[0] == 0.0) and np.all(o[1] == 0.0)
     full = oracle.attn_decode(q, kc, vc, np.array([10, 10, 10], dtype=np.int32))
+    assert np.array_equal(o[2], full[2])
+
+
+# --------------------------------------------------------------------------
+# KV-cache prefill with per-entry lengths and the log-sum-exp output
+# --------------------------------------------------------------------------
+def _kvcache_reference(q, kc, vc, seqlens, causal):
+    """torch float64: SDPA per entry over its valid rows with the explicit
+    bottom-right mask, and logsumexp of the explicitly scaled scores."""
+    B, S_q, H, D = q.shape
+    o = np.zeros_like(q)
+    lse = np.full((B, H, S_q), -np.inf)
+    for b in range(B):
+        n = int(min(max(seqlens[b], 0), kc.shape[1]))
+        if n == 0:
+            continue
+        qt = torch.from_numpy(q[b]).permute(1, 0, 2)            # H, S_q, D
+        kt = torch.from_numpy(kc[b, :n]).permute(1, 0, 2)
+        vt = torch.from_numpy(vc[b, :n]).permute(1, 0, 2)
+        i = torch.arange(S_q)[:, None]
+        j = torch.arange(n)[None, :]
+        mask = (j <= i + (n - S_q)) if causal else torch.ones(S_q, n, dtype=torch.bool)
+        rows = mask.any(dim=1)                                   # rows that see a key
+        s = (qt @ kt.transpose(1, 2)) / math.sqrt(D)
+        s = s.masked_fill(~mask, -math.inf)
+        lse[b][:, rows.numpy()] = torch.logsumexp(s[:, rows], dim=-1).numpy()
+        if rows.any():
+            ob = torch.nn.functional.scaled_dot_product_attention(qt[:, rows], kt, vt, attn_mask=mask[rows])
+            o[b][rows.numpy()] = ob.permute(1, 0, 2).numpy()
+    return o, lse
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_kvcache_matches_sdpa_and_logsumexp_float64(causal):
+    B, S_q, S_cap, H, D = 4, 21, 50, 2, 32
+    seqlens = np.array([50, 33, 9, 0], dtype=np.int32)   # 9 < S_q: early rows see no key
+    q, kc, vc = rnd(201, B, S_q, H, D), rnd(202, B, S_cap, H, D), rnd(203, B, S_cap, H, D)
+    for b in range(B):   # rows past the length are never read
+        kc[b, seqlens[b]:] = np.nan
+        vc[b, seqlens[b]:] = np.nan
+    o, lse = oracle.attn_fwd_kvcache(q, kc, vc, seqlens, causal)
+    ro, rlse = _kvcache_reference(q, kc, vc, seqlens, causal)
+    assert np.all(np.isfinite(o))
+    assert np.max(np.abs(o - ro)) <= 1e-12
+    assert np.array_equal(np.isneginf(lse), np.isneginf(rlse))
+    fin = np.isfinite(rlse)
+    assert np.max(np.abs(lse[fin] - rlse[fin])) <= 1e-12
+
+
+def test_kvcache_without_lengths_is_the_forward():
+    B, S_q, S_cap, H, D = 2, 13, 29, 3, 16
+    q, kc, vc = rnd(211, B, S_q, H, D), rnd(212, B, S_cap, H, D), rnd(213, B, S_cap, H, D)
+    for causal in (True, False):
+        o, lse = oracle.attn_fwd_kvcache(q, kc, vc, None, causal)
+        assert np.array_equal(o, oracle.attn_fwd(q, kc, vc, causal))
+        o2, lse2 = oracle.attn_fwd_kvcache(q, kc, vc, np.full(B, S_cap, dtype=np.int32), causal)
+        assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
+def test_lse_merges_results_over_disjoint_key_sets():
+    """softmax over keys A u B equals the two partial softmaxes weighted by
+    exp(lse_A - lse) and exp(lse_B - lse), lse = ln(exp(lse_A) + exp(lse_B))."""
+    B, S_q, H, D, n, m = 2, 7, 2, 16, 40, 15
+    q, kc, vc = rnd(221, B, S_q, H, D, std=2.0), rnd(222, B, n, H, D, std=2.0), rnd(223, B, n, H, D)
+    o, lse = oracle.attn_fwd_kvcache(q, kc, vc, None, causal=False)
+    oa, la = oracle.attn_fwd_kvcache(q, kc[:, :m].copy(), vc[:, :m].copy(), None, causal=False)
+    ob, lb = oracle.attn_fwd_kvcache(q, kc[:, m:].copy(), vc[:, m:].copy(), None, causal=False)
+    lt = np.logaddexp(la, lb)
+    assert np.max(np.abs(lse - lt)) <= 1e-12
+    wa = np.exp(la - lt).transpose(0, 2, 1)[..., None]   # B, S_q, H, 1
+    wb = np.exp(lb - lt).transpose(0, 2, 1)[..., None]
+    assert np.max(np.abs(o - (wa * oa + wb * ob))) <= 1e-12
+
+
+def test_kvcache_rows_that_see_no_key():
+    B, S_q, S_cap, H, D = 3, 6, 8, 2, 8
+    q, kc, vc = rnd(231, B, S_q, H, D), rnd(232, B, S_cap, H, D), rnd(233, B, S_cap, H, D)
+    o, lse = oracle.attn_fwd_kvcache(q, kc, vc, np.array([0, 2, 99], dtype=np.int32), causal=True)
+    assert np.all(o[0] == 0.0) and np.all(np.isneginf(lse[0]))
+    # entry 1: queries at positions -4..1; rows 0..3 see nothing, row 4 sees key 0 only
+    assert np.all(o[1, :4] == 0.0) and np.all(np.isneginf(lse[1, :, :4]))
+    assert np.array_equal(o[1, 4], vc[1, 0])
+    np.testing.assert_allclose(lse[1, :, 4], (q[1, 4] * kc[1, 0]).sum(-1) / math.sqrt(D), rtol=1e-14)
+    # entry 2: the length is clamped to S_cap
+    full, _ = oracle.attn_fwd_kvcache(q, kc, vc, np.array([8, 8, 8], dtype=np.int32), causal=True)
     assert np.array_equal(o[2], full[2])
 
 

@@ -34,6 +34,10 @@ MUTANTS = {
     "query_key_swapped": ("dot += q[at(b, i, h, d, S_qdim, H, D)] * k[at(b, j, h, d, S_kdim, H, D)];",
                           "dot += q[at(b, i, h, d, S_qdim, H, D)] * q[at(b, j % S_q, h, d, S_qdim, H, D)];"),
     "max_over_first_key_only": ("if (row[j] > m) m = row[j];", "if (j == 0) m = row[j];"),
+    "lse_without_max": ("= m + log(l);", "= log(l);"),
+    "lse_log2": ("= m + log(l);", "= m + log2(l);"),
+    "kvcache_ignores_lengths": ("long n = seqlens ? seqlens[b] : S_cap;", "long n = S_cap;"),
+    "empty_rows_not_zero": ("if (m == -INFINITY) {", "if (0) {"),
 }
 
 PINS = [
@@ -50,6 +54,9 @@ PINS = [
     pins.test_large_logits_stay_finite_and_match_lse_brute_force,
     pins.test_decode_equals_forward_with_one_query_and_ignores_slots_past_len,
     pins.test_decode_empty_and_overlong_lengths,
+    lambda: pins.test_kvcache_matches_sdpa_and_logsumexp_float64(True),
+    pins.test_lse_merges_results_over_disjoint_key_sets,
+    pins.test_kvcache_rows_that_see_no_key,
 ]
 
 
