@@ -8,6 +8,7 @@ PyTorch fallback: if ``libattn.so`` is missing the import fails.
 
     o = attn_fwd(q, k, v, causal=True)                      # [B, S, H, D]
     o = attn_decode(q, kcache, vcache, seqlens)             # q [B, 1, H, D]
+    o, lse = attn_fwd_kvcache(q, kcache, vcache, seqlens_kv, return_lse=True)
 """
 from __future__ import annotations
 
@@ -52,6 +53,8 @@ def _load() -> ctypes.CDLL:
     vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i]
     lib.attn_fwd.restype = i
+    lib.attn_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i]
+    lib.attn_fwd_kvcache.restype = i
     lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, sz]
@@ -142,6 +145,41 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor 
     return o
 
 
+def attn_fwd_kvcache(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
+                     seqlens_kv: torch.Tensor | None = None, o: torch.Tensor | None = None,
+                     causal: bool = True, return_lse: bool = False):
+    """Chunk of queries against a KV cache with per-sequence lengths.
+
+    q [B,S_q,H,D]; caches [B,S_cap,H,D]; seqlens_kv int32[B] on the GPU or None (all S_cap rows valid).
+    Returns o [B,S_q,H,D], or (o, lse) with lse float32 [B,H,S_q] when return_lse is set."""
+    for n, t in (("q", q), ("kcache", kcache), ("vcache", vcache)):
+        _dev_tensor(n, t, 4)
+    B, S_q, H, D = q.shape
+    S_cap = kcache.shape[1]
+    if tuple(kcache.shape) != (B, S_cap, H, D) or tuple(vcache.shape) != tuple(kcache.shape):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, kcache {tuple(kcache.shape)}, "
+                         f"vcache {tuple(vcache.shape)}")
+    if not (q.dtype == kcache.dtype == vcache.dtype):
+        raise TypeError("q and the caches must share one dtype")
+    if seqlens_kv is not None:
+        _dev_tensor("seqlens_kv", seqlens_kv, 1)
+        if seqlens_kv.dtype != torch.int32 or seqlens_kv.shape[0] != B:
+            raise ValueError("seqlens_kv must be int32[B]")
+    if o is None:
+        o = torch.empty_like(q)
+    else:
+        _dev_tensor("o", o, 4)
+        if tuple(o.shape) != tuple(q.shape) or o.dtype != q.dtype:
+            raise ValueError("o must match q in shape and dtype")
+    lse = torch.empty((B, H, S_q), dtype=torch.float32, device=q.device) if return_lse else None
+    _set_stream(q.device)
+    _check(load().attn_fwd_kvcache(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(),
+                                   seqlens_kv.data_ptr() if seqlens_kv is not None else None, o.data_ptr(),
+                                   lse.data_ptr() if lse is not None else None, B, H, S_q, S_cap, D,
+                                   int(bool(causal)), _dtype_code(q)))
+    return (o, lse) if return_lse else o
+
+
 def attn_decode_workspace_bytes(B: int, H: int, S_cap: int, D: int) -> int:
     return int(load().attn_decode_workspace_bytes(B, H, S_cap, D))
 
@@ -190,6 +228,6 @@ def attn_decode_plan(B: int, H: int, S_cap: int, D: int, dtype: int) -> DecodePl
     return plan
 
 
-__all__ = ["attn_fwd", "attn_decode", "attn_decode_workspace_bytes", "attn_fwd_plan", "attn_decode_plan",
+__all__ = ["attn_fwd", "attn_fwd_kvcache", "attn_decode", "attn_decode_workspace_bytes", "attn_fwd_plan", "attn_decode_plan",
            "attn_set_timing_events",
            "AttnError", "ATTN_F32", "ATTN_BF16", "lib", "LIB_PATH"]

@@ -42,7 +42,9 @@ __device__ __forceinline__ float wave_sum(float x) {
 template <typename T, int D>
 __global__ __launch_bounds__(kRowThreads) void fwd_row_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                               const T* __restrict__ V, T* __restrict__ O,
-                                                              int H, int S_q, int S_kv, int causal, float c) {
+                                                              int H, int S_q, int S_cap, int causal, float c,
+                                                              const int32_t* __restrict__ kv_lens,
+                                                              float* __restrict__ lse) {
     constexpr int DPL = (D + 63) / 64;   // head dims per lane in the P.V phase
     __shared__ float qs[D];
     const int lane = threadIdx.x;
@@ -54,7 +56,9 @@ __global__ __launch_bounds__(kRowThreads) void fwd_row_kernel(const T* __restric
     for (int d = lane; d < D; d += 64) qs[d] = to_f32(Q[qoff + d]);
     __syncthreads();
 
-    const int n_keys = causal ? min(S_kv, i + 1 + (S_kv - S_q)) : S_kv;
+    // valid keys of this batch entry; rows of K and V are S_cap apart per entry
+    const int S_kv = kv_lens ? min(max(kv_lens[b], 0), S_cap) : S_cap;
+    const int n_keys = causal ? max(0, min(S_kv, i + 1 + (S_kv - S_q))) : S_kv;
     float m_run = -INFINITY, l_run = 0.f;
     float acc[DPL];
 #pragma unroll
@@ -64,7 +68,7 @@ __global__ __launch_bounds__(kRowThreads) void fwd_row_kernel(const T* __restric
         const int j = j0 + lane;
         float s = -INFINITY;
         if (j < n_keys) {
-            const T* krow = K + ((size_t)((size_t)b * S_kv + j) * H + h) * D;
+            const T* krow = K + ((size_t)((size_t)b * S_cap + j) * H + h) * D;
             float dot = 0.f;
 #pragma unroll 8
             for (int d = 0; d < D; ++d) dot = __builtin_fmaf(qs[d], to_f32(krow[d]), dot);
@@ -80,7 +84,7 @@ __global__ __launch_bounds__(kRowThreads) void fwd_row_kernel(const T* __restric
         const int nj = min(64, n_keys - j0);
         for (int jj = 0; jj < nj; ++jj) {
             const float p = __shfl(pj, jj);
-            const T* vrow = V + ((size_t)((size_t)b * S_kv + j0 + jj) * H + h) * D;
+            const T* vrow = V + ((size_t)((size_t)b * S_cap + j0 + jj) * H + h) * D;
 #pragma unroll
             for (int e = 0; e < DPL; ++e) {
                 const int d = lane + 64 * e;
@@ -88,12 +92,17 @@ __global__ __launch_bounds__(kRowThreads) void fwd_row_kernel(const T* __restric
             }
         }
     }
-    const float inv = 1.0f / l_run;
+    // a row that sees no key (a KV-cache entry shorter than the chunk) is 0
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) {
         const int d = lane + 64 * e;
         if (d < D) O[qoff + d] = from_f32<T>(acc[e] * inv);
     }
+    // log of the softmax denominator, natural units: ln 2 * (m + log2 l)
+    if (lse && lane == 0)
+        lse[((size_t)b * H + h) * S_q + i] = l_run > 0.f ? (m_run + __builtin_log2f(l_run)) * 0.69314718055994531f
+                                                         : -INFINITY;
 }
 
 template <typename T, int D>
@@ -101,7 +110,7 @@ hipError_t launch_row(const FwdArgs& a, hipStream_t stream) {
     const unsigned grid = (unsigned)((long long)a.B * a.H * a.S_q);
     hipExtLaunchKernelGGL((fwd_row_kernel<T, D>), dim3(grid), dim3(kRowThreads), 0, stream, a.ev_start, a.ev_stop,
                           0, (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.H, a.S_q, a.S_kv, a.causal,
-                          a.scale_log2);
+                          a.scale_log2, a.kv_lens, a.lse);
     return hipGetLastError();
 }
 

@@ -121,10 +121,12 @@ __device__ __forceinline__ int tok_off(int tok, int ch, int H) {
 // tile's first token, its range shortened to match (zero once past the end).
 // All operands are wave-uniform, so this is scalar work; the per-lane offsets
 // then stay loop-invariant.
+// The K and V rows of batch entry b are S_cap rows apart (the cache
+// capacity); only the first S valid ones are in range.
 template <int D>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const __bf16* base, int b, int h, int S, int H,
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const __bf16* base, int b, int h, int S_cap, int S, int H,
                                                             int tile0) {
-    const __bf16* p = base + ((size_t)b * S * H + h) * D + (size_t)tile0 * H * D;
+    const __bf16* p = base + ((size_t)b * S_cap * H + h) * D + (size_t)tile0 * H * D;
     const int bytes = ((S - 1) * H + 1) * D * 2 - tile0 * H * D * 2;
     return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, bytes > 0 ? bytes : 0, 0x00020000);
 }
@@ -231,8 +233,8 @@ constexpr float kLazy = 8.0f;
 template <int D>
 __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    __bf16* __restrict__ O, int B, int H, int S_q, int S_kv, int causal, float c /* scale*log2e */,
-    int n_qblk, int items_per_bh, int paired) {
+    __bf16* __restrict__ O, int B, int H, int S_q, int S_cap, int causal, float c /* scale*log2e */,
+    int n_qblk, int items_per_bh, int paired, const int32_t* __restrict__ kv_lens, float* __restrict__ lse) {
     using C = TileCfg<D>;
     __shared__ __attribute__((aligned(16))) char lds[C::LDS];
     // stages: K0 K1 V0 V1
@@ -247,7 +249,6 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
     const int wq = wave & 3;     // query sub-block of this wave
     const int half = wave >> 2;  // key half of every tile
     const bool k_loader = tid < 256;
-    const int off = S_kv - S_q;  // absolute position of query i is i + off
     // per-lane operand offsets inside a stage (the k-steps / blocks are immediates)
     const int k_lane = (32 * half + l32) * C::KROW + 16 * g;
     const int v_lane = l32 * C::VROW + 16 * (4 * half + g);
@@ -256,6 +257,9 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
     const int bh = item / items_per_bh;
     const int p = item % items_per_bh;
     const int b = bh / H, h = bh % H;
+    // valid keys of this batch entry (all S_cap rows unless lengths are given)
+    const int S_kv = kv_lens ? min(max(kv_lens[b], 0), S_cap) : S_cap;
+    const int off = S_kv - S_q;  // absolute position of query i is i + off (may be < 0)
     const int qb_first = n_qblk - 1 - p;
     const int nphase = (paired && p != qb_first) ? 2 : 1;
 
@@ -274,9 +278,12 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
         for (int ks = 0; ks < C::KS; ++ks)
             qf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
                                                      rq, tok_off<D>(qi, 2 * ks + g, H), 0, 0));
-        const int first = (tiles_for_block(qb, S_q, S_kv, causal) - 1) * kTileN;   // tiles run backwards
-        if (k_loader) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_kv, H, first), H, tid);
-        else load_v<D>(pre, tile_rsrc<D>(V, b, h, S_kv, H, first), H, tid);
+        const int ntq = tiles_for_block(qb, S_q, S_kv, causal);
+        const int first = (ntq - 1) * kTileN;   // tiles run backwards
+        if (ntq > 0) {
+            if (k_loader) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_cap, S_kv, H, first), H, tid);
+            else load_v<D>(pre, tile_rsrc<D>(V, b, h, S_cap, S_kv, H, first), H, tid);
+        }
     };
     issue_block(qb_first);
 
@@ -304,7 +311,7 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
         __syncthreads();
         // step u works on KV tile nt-1-u: the diagonal tile first
         auto tile_of = [&](int u) { return nt - 1 - u; };
-        if (k_loader && nt > 1) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_kv, H, tile_of(1) * kTileN), H, tid);
+        if (k_loader && nt > 1) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_cap, S_kv, H, tile_of(1) * kTileN), H, tid);
         // unconditional: every path into the loop has then waited for the Q
         // loads, so the loop body never waits on them (or on the prefetch)
         f32x16_t sa = qk_tile<D>(kst(0) + k_lane, qf), sb;
@@ -316,8 +323,8 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
             // (a) HBM loads: K two tiles ahead, V one tile ahead
             const bool ld_k = k_loader && t + 2 < nt;
             const bool ld_v = !k_loader && t + 1 < nt;
-            if (ld_k) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_kv, H, tile_of(t + 2) * kTileN), H, tid);
-            if (ld_v) load_v<D>(pre, tile_rsrc<D>(V, b, h, S_kv, H, tile_of(t + 1) * kTileN), H, tid);
+            if (ld_k) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_cap, S_kv, H, tile_of(t + 2) * kTileN), H, tid);
+            if (ld_v) load_v<D>(pre, tile_rsrc<D>(V, b, h, S_cap, S_kv, H, tile_of(t + 1) * kTileN), H, tid);
 
             const int kbase = tile_of(t) * kTileN + 32 * half;   // first key of this wave's half tile
             const bool work = wave_has_rows && kbase <= key_last && kbase < S_kv;
@@ -434,7 +441,12 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
             const float a1 = __builtin_amdgcn_exp2f(m1 - mu);
             float l = a0 * l_run + a1 * l1;
             l += partner_lane(l);
-            const float inv = 1.0f / l;
+            // a row that sees no key (a KV-cache entry shorter than the chunk) is 0
+            const float inv = l > 0.f ? 1.0f / l : 0.f;
+            // log of the softmax denominator in natural units: ln 2 * (m + log2 l)
+            if (lse && g == 0 && qi < S_q)
+                lse[((size_t)b * H + h) * S_q + qi] = l > 0.f ? (mu + __builtin_log2f(l)) * 0.69314718055994531f
+                                                            : -INFINITY;
 #pragma unroll
             for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -462,7 +474,7 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
     hipExtLaunchKernelGGL(fwd_tile_bf16_kernel<D>, dim3((unsigned)tg.n_items), dim3(kTileThreads), 0, stream,
                           a.ev_start, a.ev_stop, 0, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
                           (__bf16*)a.o, a.B, a.H, a.S_q, a.S_kv, a.causal, a.scale_log2, tg.n_qblk,
-                          tg.items_per_bh, tg.paired);
+                          tg.items_per_bh, tg.paired, a.kv_lens, a.lse);
     return hipGetLastError();
 }
 

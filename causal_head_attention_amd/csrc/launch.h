@@ -19,6 +19,11 @@ struct FwdArgs {
     float scale_log2;   // (1/sqrt(D)) * log2(e), fp32
     hipEvent_t ev_start;   // optional: recorded when the first kernel starts
     hipEvent_t ev_stop;    // optional: recorded when the last kernel ends
+    // KV-cache form: k and v hold S_kv rows per batch entry (the cache
+    // capacity), of which kv_lens[b] (device, clamped to [0, S_kv]) are valid;
+    // nullptr means all S_kv rows are valid.
+    const int32_t* kv_lens;
+    float* lse;   // optional [B, H, S_q] natural-log sum of exp(scaled scores)
 };
 
 struct DecodeArgs {

@@ -61,6 +61,7 @@ ATTN_HD inline int tiles_for_block(int qb, int S_q, int S_kv, int causal) {
     int last_q = (qb + 1) * kTileM - 1;
     if (last_q > S_q - 1) last_q = S_q - 1;
     const int last_key = last_q + (S_kv - S_q);
+    if (last_key < 0) return 0;   // no query of the block sees any key (S_kv < S_q)
     const int n = last_key / kTileN + 1;
     return n < n_all ? n : n_all;
 }

@@ -79,6 +79,38 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H,
              int S_kv, int D, int causal, int dtype);
 
 /*
+ * attn_fwd_kvcache -- attn_fwd for a chunk of new queries against a KV cache
+ * with per-sequence lengths (chunked prefill), optionally returning the
+ * log-sum-exp of each query row. Definition: the masked attention of the
+ * MMHA page, section 2, applied per batch entry to the cache rows that are
+ * valid for it; positions follow the bottom-right rule above with S_kv taken
+ * per entry. The log-sum-exp is the log of the softmax denominator (the
+ * running-sum state of the "Week-4 CUDA notes" page, section 2.2), which lets
+ * partial results over disjoint key sets be merged later.
+ *
+ *   q, o        : [B, S_q, H, D]   the new queries (their keys and values are
+ *                 expected to be in the cache already, at the end of each
+ *                 entry's valid rows)
+ *   kcache, vcache : [B, S_cap, H, D]
+ *   seqlens_kv  : DEVICE int32[B] or NULL. Entry b's valid rows are
+ *                 0 .. len_b-1, len_b = seqlens_kv[b] clamped to [0, S_cap]
+ *                 (NULL: len_b = S_cap). Query i of entry b sits at position
+ *                 len_b - S_q + i; causal=1 lets it see keys j <= that
+ *                 position, causal=0 all len_b keys. A query that sees no key
+ *                 (len_b < S_q, or len_b == 0) gets an all-zero output row and
+ *                 a log-sum-exp of -inf. Rows at or past len_b are never read.
+ *   lse         : DEVICE float [B, H, S_q] or NULL: ln(sum_j exp(q.k_j/sqrt(D)))
+ *                 over the keys the query sees.
+ *   dtype, D    : as attn_fwd (ATTN_F32 or ATTN_BF16; D in {32, 64, 128}).
+ *   B, H or S_q equal to 0 is a valid empty call; S_cap must then be >= 0,
+ *   otherwise >= 1. o may not overlap any other argument, nor lse any input.
+ * With seqlens_kv = NULL and S_q <= S_cap this is attn_fwd (S_kv = S_cap)
+ * plus the log-sum-exp, and o is bit-identical to attn_fwd's.
+ */
+int attn_fwd_kvcache(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens_kv,
+                     void* o, float* lse, int B, int H, int S_q, int S_cap, int D, int causal, int dtype);
+
+/*
  * attn_decode_workspace_bytes -- device workspace attn_decode needs for
  * these sizes (per-split partial max, sum and D accumulators, fp32).
  * Returns 0 for invalid or empty sizes.

@@ -231,6 +231,78 @@ def test_decode_matches_forward_with_one_query(attn):
 
 
 # ---------------------------------------------------------------------------
+# KV-cache prefill (chunk of queries, per-entry lengths) and its log-sum-exp.
+# LSE bars: the kernels add up the probabilities as rounded for P.V, so in
+# bf16 the row sum carries a relative error up to 2^-9 and the log of it an
+# absolute error up to about 2e-3 (plus fp32 rounding of the scores): bar
+# 4e-3. fp32 inputs go through the row kernel (fp32 throughout): bar 1e-5.
+# ---------------------------------------------------------------------------
+LSE_ATOL = {torch.bfloat16: 4e-3, torch.float32: 1e-5}
+
+
+def check_lse(got: torch.Tensor, ref: np.ndarray, dtype: torch.dtype, what: str = ""):
+    g = got.detach().cpu().double().numpy()
+    assert g.shape == ref.shape, what
+    assert np.array_equal(np.isneginf(g), np.isneginf(ref)), f"{what}: -inf rows differ"
+    fin = np.isfinite(ref)
+    assert np.all(np.isfinite(g[fin])), f"{what}: non-finite lse"
+    err = float(np.abs(g[fin] - ref[fin]).max()) if fin.any() else 0.0
+    assert err <= LSE_ATOL[dtype], f"{what}: lse max abs err {err:.3e} > {LSE_ATOL[dtype]}"
+    return err
+
+
+def test_kvcache_workload(attn):
+    cfg = workloads.BF16_KVCACHE
+    sl, q, kc, vc = workloads.make_kvcache_prefill(cfg, nan_fill=True)
+    say(f"kvcache {cfg.name} B={cfg.B} S_q={cfg.S_q} S_cap={cfg.S_cap} lengths {sl.tolist()}")
+    o, lse = attn.attn_fwd_kvcache(q.cuda(), kc.cuda(), vc.cuda(), sl.cuda(), causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rlse = oracle.attn_fwd_kvcache(q, kc, vc, sl.numpy(), causal=True)
+    ma, rel = check(o, ro, torch.bfloat16, "kvcache workload")
+    le = check_lse(lse, rlse, torch.bfloat16, "kvcache workload")
+    say(f"kvcache: max abs {ma:.2e}, rel L2 {rel:.2e}, lse max abs {le:.2e}")
+
+
+KV_EDGE = [  # (B, H, S_q, S_cap, D, causal, lengths)
+    (4, 2, 65, 200, 128, True, [200, 130, 64, 1]),          # entries shorter than the chunk
+    (3, 1, 129, 129, 64, True, [0, 129, 300]),              # empty entry, clamped length
+    (2, 3, 7, 90, 32, True, [90, 7]),
+    (3, 2, 130, 400, 128, False, [400, 129, 5]),
+    (2, 2, 1, 77, 128, True, [77, 33]),                      # one query = decode
+    (1, 4, 300, 1000, 128, True, [999]),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("case", KV_EDGE, ids=lambda c: "x".join(map(str, c[:6])))
+def test_kvcache_edge_cases(attn, case, dtype):
+    B, H, S_q, S_cap, D, causal, lens = case
+    say(f"kvcache edge {case} {dtype}")
+    cfg = workloads.KVCachePrefill("edge", dtype, B, H, S_q, S_cap, D, 400 + D, 1, S_cap, causal)
+    sl, q, kc, vc = workloads.make_kvcache_prefill(cfg, nan_fill=True, seqlens=lens)
+    o, lse = attn.attn_fwd_kvcache(q.cuda(), kc.cuda(), vc.cuda(), sl.cuda(), causal=causal, return_lse=True)
+    ro, rlse = oracle.attn_fwd_kvcache(q, kc, vc, sl.numpy(), causal=causal)
+    check(o, ro, dtype, f"kvcache {case}")
+    check_lse(lse, rlse, dtype, f"kvcache {case}")
+    # rows that see no key come out exactly 0
+    empty = np.isneginf(rlse).all(axis=1)          # B, S_q
+    assert torch.all(o.cpu()[torch.from_numpy(empty)] == 0)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_kvcache_without_lengths_is_attn_fwd_bitwise(attn, dtype):
+    q, k, v = workloads.make_prefill_shape(500, dtype, 2, 4, 200, 333, 128)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    for causal in (True, False):
+        o1 = attn.attn_fwd(q, k, v, causal=causal)
+        o2, lse = attn.attn_fwd_kvcache(q, k, v, None, causal=causal, return_lse=True)
+        o3 = attn.attn_fwd_kvcache(q, k, v, torch.full((2,), 333, dtype=torch.int32, device="cuda"), causal=causal)
+        assert torch.equal(o1, o2) and torch.equal(o1, o3)
+        _, rlse = oracle.attn_fwd_kvcache(q.cpu(), k.cpu(), v.cpu(), None, causal=causal)
+        check_lse(lse, rlse, dtype, f"lse causal={causal}")
+
+
+# ---------------------------------------------------------------------------
 # Error paths through the binding on a live device
 # ---------------------------------------------------------------------------
 def test_error_paths_on_device(attn):

@@ -19,10 +19,15 @@ The five workloads:
                     V ~ N(0,1) (logits reach about +-100: stability stress)
 * ``bf16_decode``   bf16 decode, B=16 sequences, one query each, H=32, D=128,
                     KV-cache capacity 4096, lengths uniform in [1, 4096]
+* ``bf16_kvcache``  bf16 chunked prefill into a KV cache: B=8 sequences, a chunk
+                    of 512 new queries each, H=32, D=128, cache capacity 4096,
+                    lengths (cached tokens including the chunk) uniform in
+                    [512, 4096], causal
 
-Generator: a torch CPU ``Generator`` seeded with ``1000 + index`` (1001..1005).
-Prefill draws q, k, v in that order as ``randn(B,S,H,D) * std``; decode draws
-the lengths first, then q, the K cache and the V cache. bf16 tensors are the
+Generator: a torch CPU ``Generator`` seeded with ``1000 + index`` (1001..1006).
+Prefill draws q, k, v in that order as ``randn(B,S,H,D) * std``; decode and
+the KV-cache prefill draw the lengths first, then q, the K cache and the V
+cache. bf16 tensors are the
 round-to-nearest-even cast of the fp32 draw (``Tensor.to(torch.bfloat16)``).
 """
 from __future__ import annotations
@@ -68,6 +73,37 @@ class Decode:
     len_hi: int = 4096
 
 
+@dataclass(frozen=True)
+class KVCachePrefill:
+    name: str
+    dtype: torch.dtype
+    B: int
+    H: int
+    S_q: int
+    S_cap: int
+    D: int
+    seed: int
+    len_lo: int
+    len_hi: int
+    causal: bool = True
+
+    def flops(self, seqlens) -> int:
+        """Algorithmic FLOP: 4*H*D per visible (query, key) pair, summed over entries."""
+        pairs = 0
+        for n in seqlens:
+            n = max(0, min(int(n), self.S_cap))
+            pairs += visible_pairs_kv(self.S_q, n, self.causal)
+        return 4 * self.H * self.D * pairs
+
+
+def visible_pairs_kv(S_q: int, n: int, causal: bool) -> int:
+    """Visible pairs of S_q queries at positions n-S_q .. n-1 over n keys (none for a
+    query at a negative position)."""
+    if not causal:
+        return S_q * n
+    return sum(max(0, min(n, n - S_q + i + 1)) for i in range(S_q))
+
+
 def visible_pairs(S_q: int, S_kv: int, causal: bool) -> int:
     """Number of (i, j) pairs a query sees (bottom-right causal alignment)."""
     if not causal:
@@ -82,6 +118,7 @@ BF16_S2048 = Prefill("bf16_s2048", torch.bfloat16, 1, 32, 2048, 2048, 128, True,
 BF16_S4096 = Prefill("bf16_s4096", torch.bfloat16, 1, 32, 4096, 4096, 128, True, 1004,
                      qk_std=4.0, v_std=1.0)
 BF16_DECODE = Decode("bf16_decode", torch.bfloat16, 16, 32, 4096, 128, 1005)
+BF16_KVCACHE = KVCachePrefill("bf16_kvcache", torch.bfloat16, 8, 32, 512, 4096, 128, 1006, 512, 4096)
 
 PREFILL_CONFIGS = (FP32_TINY, FP32_SMALL, BF16_S2048, BF16_S4096)
 
@@ -142,3 +179,27 @@ def decode_kv_bytes(seqlens, H: int, D: int, elem_bytes: int, S_cap: int) -> int
         total += max(0, min(int(n), S_cap))
     B = len(seqlens)
     return total * H * D * 2 * elem_bytes + 2 * B * H * D * elem_bytes
+
+
+def make_kvcache_prefill(cfg: KVCachePrefill, nan_fill: bool = False, seqlens=None, S_cap: int | None = None,
+                         B: int | None = None, S_q: int | None = None):
+    """Draw (seqlens, q, kcache, vcache) for a KV-cache prefill on the CPU.
+
+    ``seqlens`` is int32[B] uniform in [len_lo, len_hi] unless given; with
+    ``nan_fill`` the cache rows at or past each length hold NaN.
+    """
+    B = cfg.B if B is None else B
+    S_cap = cfg.S_cap if S_cap is None else S_cap
+    S_q = cfg.S_q if S_q is None else S_q
+    g = torch.Generator().manual_seed(cfg.seed)
+    drawn = torch.randint(cfg.len_lo, cfg.len_hi + 1, (B,), generator=g, dtype=torch.int32)
+    seqlens = drawn if seqlens is None else torch.as_tensor(seqlens, dtype=torch.int32)
+    q = torch.randn(B, S_q, cfg.H, cfg.D, generator=g).to(cfg.dtype)
+    kc = torch.randn(B, S_cap, cfg.H, cfg.D, generator=g).to(cfg.dtype)
+    vc = torch.randn(B, S_cap, cfg.H, cfg.D, generator=g).to(cfg.dtype)
+    if nan_fill:
+        for b in range(B):
+            n = max(0, min(int(seqlens[b]), S_cap))
+            kc[b, n:] = float("nan")
+            vc[b, n:] = float("nan")
+    return seqlens, q.contiguous(), kc.contiguous(), vc.contiguous()
