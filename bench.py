@@ -100,12 +100,17 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, copy_mib: int = 256) -
     The result is keyed by the SHA-256 of the kernel sources it was taken on."""
     import csv
 
+    prefill_grid = str(256 * 512)   # workgroups x threads of the S=2048 prefill launch
+
     def per_kernel(path, counter):
         vals = {}
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
-            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+            name = r["Kernel_Name"]
+            if "fwd_tile_bf16_kernel" in name and r["Grid_Size"] != prefill_grid:
+                name += " [kvcache]"   # the KV-cache launch of the same kernel
+            vals.setdefault(name, []).append(float(r["Counter_Value"]))
         return vals
 
     fetch = per_kernel(fetch_csv, "FETCH_SIZE")
@@ -115,7 +120,7 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, copy_mib: int = 256) -
     w_scale = copy_kib / max(write["__amd_rocclr_copyBuffer"])
 
     def mean_of(vals, key):
-        xs = [v for name, v in vals.items() if key in name]
+        xs = [v for name, v in vals.items() if key in name and "[kvcache]" not in name]
         assert len(xs) == 1, f"{key}: {len(xs)} kernels match"
         return statistics.fmean(xs[0])
 
@@ -153,6 +158,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="also time 20 back-to-back calls without the flush")
+    ap.add_argument("--skip-kvcache", action="store_true",
+                    help="leave out the KV-cache prefill measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one device copy of MIB MiB (reference for HBM counters)")
     args = ap.parse_args()
@@ -236,6 +243,46 @@ def main() -> int:
             warm_d.append(hev.ms(e[2], e[3]))
             hev.destroy(e)
 
+    # KV-cache prefill (chunk of 512 queries per sequence against caches of
+    # per-sequence length): the same tile kernel behind attn_fwd_kvcache,
+    # timed cold like the step, outside the step's headline figure
+    kv = None
+    if not args.skip_kvcache:
+        kc_cfg = workloads.BF16_KVCACHE
+        log("KV-cache prefill: generating inputs")
+        sl_kv_h, q_kv_h, kc_kv_h, vc_kv_h = workloads.make_kvcache_prefill(kc_cfg)
+        sl_kv, q_kv, kc_kv, vc_kv = (t.to(dev) for t in (sl_kv_h, q_kv_h, kc_kv_h, vc_kv_h))
+        o_kv = torch.empty_like(q_kv)
+        lse_kv = torch.empty((kc_cfg.B, kc_cfg.H, kc_cfg.S_q), dtype=torch.float32, device=dev)
+        kv_flops = kc_cfg.flops(sl_kv_h.tolist())
+
+        def kv_call():
+            attn.attn_fwd_kvcache(q_kv, kc_kv, vc_kv, sl_kv, o_kv, causal=True)
+
+        for _ in range(3):
+            kv_call()
+        torch.cuda.synchronize()
+        kv_ms = []
+        for _ in range(20):
+            e = hev.create(2)
+            flush.zero_()
+            attn.attn_set_timing_events(e[0], e[1])
+            kv_call()
+            torch.cuda.synchronize()
+            kv_ms.append(hev.ms(e[0], e[1]))
+            hev.destroy(e)
+        kv_mean = statistics.fmean(kv_ms)
+        kv_tf = kv_flops / (kv_mean * 1e-3) / 1e12
+        kv = {"value": round(kv_tf, 2), "unit": "TFLOPS",
+              "workload": f"bf16 causal chunk of {kc_cfg.S_q} queries x {kc_cfg.B} sequences, H={kc_cfg.H} "
+                          f"D={kc_cfg.D}, cache capacity {kc_cfg.S_cap}, lengths {sl_kv_h.tolist()} (seed "
+                          f"{kc_cfg.seed}); cold, 20 calls",
+              "roofline": {"bound": "mfma", "achieved": round(kv_tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(kv_tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                           "flop_per_launch": kv_flops, "mean_launch_us": round(kv_mean * 1e3, 2),
+                           "median_launch_us": round(statistics.median(kv_ms) * 1e3, 2)}}
+        del kc_kv, vc_kv
+
     if args.copy_calibration:
         n = args.copy_calibration << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -297,7 +344,8 @@ def main() -> int:
                      "traffic": measured_traffic("fwd_tile_bf16", TILE_SRC),
                      "kernel": "fwd_tile_bf16_kernel<128>", "flop_per_launch": flops,
                      "mean_launch_us": round(fwd_mean * 1e3, 2),
-                     "median_launch_us": round(statistics.median(fwd_ms) * 1e3, 2)},
+                     "median_launch_us": round(statistics.median(fwd_ms) * 1e3, 2),
+                     "p95_launch_us": round(float(np.percentile(fwd_ms, 95)) * 1e3, 2)},
         "decode": {"value": round(dec_gbs, 1), "unit": "GB/s",
                    "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
@@ -305,6 +353,7 @@ def main() -> int:
                                 "bytes_per_call": dec_bytes,
                                 "mean_call_us": round(dec_mean * 1e3, 2),
                                 "median_call_us": round(statistics.median(dec_ms) * 1e3, 2),
+                                "p95_call_us": round(float(np.percentile(dec_ms, 95)) * 1e3, 2),
                                 "note": "one call = split kernel + combine kernel"}},
         "warm_cache": ({"prefill_tflops": round(flops / (statistics.median(warm_f) * 1e-3) / 1e12, 2),
                         "decode_gbs": round(dec_bytes / (statistics.median(warm_d) * 1e-3) / 1e9, 1)}
@@ -312,6 +361,7 @@ def main() -> int:
         "timing": "hipEvents attached to the first/last kernel dispatch of each call (start->end of the "
                   "kernels, no queueing gaps); 512 MiB fill before every call",
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "kvcache_prefill": kv,
         "cpu_baseline": cpu,
         "parity": parity,
     }

@@ -224,6 +224,28 @@ __device__ __forceinline__ float partner_lane(float x) {
     return __builtin_bit_cast(float, (__lane_id() < 32) ? hi : lo);
 }
 
+// Entries whose lengths are ranked in LDS (2 ints each); above this the
+// longest-first order is skipped.
+// (The ranking is O(B) per thread, a few hundred cycles at the limit.)
+constexpr int kMaxRankedEntries = 256;
+static_assert(2 * kMaxRankedEntries * sizeof(int) <= tile_lds_bytes(32), "rank table fits in LDS");
+
+// Work placement for the KV-cache form. Logical unit u = rank * H + h (rank
+// 0 = the longest entry) has items_per_bh items p. Hardware workgroup x runs
+// on XCD x % 8 and workgroups start roughly in x order, so: consecutive
+// groups of 8 units take consecutive blocks of 8*G workgroups (G =
+// items_per_bh), and the G items of one unit sit 8 apart -- the same XCD,
+// sharing its L2 for that head's K and V. A final group of m < 8 units is
+// packed the same way with stride m. A bijection on [0, n).
+__device__ __forceinline__ void kv_order(int x, int n, int G, int& u, int& p) {
+    const int group = x / (8 * G);
+    const int within = x % (8 * G);
+    const int full_units = (n / G) / 8 * 8;   // units in complete groups of 8
+    const int m = (group * 8 < full_units) ? 8 : (n / G - full_units);
+    p = within / m;
+    u = group * 8 + within % m;
+}
+
 // Row maxima are only re-based when they grow by more than 2^kLazy: until
 // then probabilities are taken against a stale maximum (at most 2^kLazy,
 // far from fp32/bf16 overflow) and the accumulators are left alone. The
@@ -253,9 +275,31 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
     const int k_lane = (32 * half + l32) * C::KROW + 16 * g;
     const int v_lane = l32 * C::VROW + 16 * (4 * half + g);
 
-    const int item = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = item / items_per_bh;
-    const int p = item % items_per_bh;
+    int bh, p;
+    if (!kv_lens) {
+        const int item = xcd_remap(blockIdx.x, gridDim.x);
+        bh = item / items_per_bh;
+        p = item % items_per_bh;
+    } else {
+        // KV-cache entries differ in length: run the longest first. Every
+        // workgroup ranks the entries by length (in LDS) and takes the
+        // (b, h) of its rank; see kv_order for the XCD placement.
+        kv_order(blockIdx.x, gridDim.x, items_per_bh, bh, p);
+        if (B <= kMaxRankedEntries) {
+            int* lens = (int*)lds;
+            int* perm = lens + kMaxRankedEntries;
+            for (int e = tid; e < B; e += kTileThreads) lens[e] = min(max(kv_lens[e], 0), S_cap);
+            __syncthreads();
+            for (int e = tid; e < B; e += kTileThreads) {
+                int rank = 0;
+                for (int f = 0; f < B; ++f) rank += (lens[f] > lens[e]) || (lens[f] == lens[e] && f < e);
+                perm[rank] = e;
+            }
+            __syncthreads();
+            bh = perm[bh / H] * H + bh % H;
+            __syncthreads();   // the table's LDS is reused by the first stage stores
+        }
+    }
     const int b = bh / H, h = bh % H;
     // valid keys of this batch entry (all S_cap rows unless lengths are given)
     const int S_kv = kv_lens ? min(max(kv_lens[b], 0), S_cap) : S_cap;
