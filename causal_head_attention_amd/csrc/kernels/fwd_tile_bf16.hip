@@ -514,7 +514,7 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
-    const TileGrid tg = tile_grid(a.B, a.H, a.S_q, a.causal);
+    const TileGrid tg = tile_grid(a.B, a.H, a.S_q, a.causal, a.kv_lens != nullptr);
     hipExtLaunchKernelGGL(fwd_tile_bf16_kernel<D>, dim3((unsigned)tg.n_items), dim3(kTileThreads), 0, stream,
                           a.ev_start, a.ev_stop, 0, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
                           (__bf16*)a.o, a.B, a.H, a.S_q, a.S_kv, a.causal, a.scale_log2, tg.n_qblk,

@@ -73,10 +73,15 @@ struct TileGrid {
     long long n_items;  // total workgroups
 };
 
-ATTN_HD inline TileGrid tile_grid(int B, int H, int S_q, int causal) {
+// Pairing evens out the causal triangle of a square (or nearly square)
+// problem, where query block j sees about j+1 key tiles. With per-entry cache
+// lengths the chunk is usually short against the cache, every block of an
+// entry sees nearly the same number of tiles, and pairing would only double
+// the longest workgroup; such launches run one block per workgroup.
+ATTN_HD inline TileGrid tile_grid(int B, int H, int S_q, int causal, bool kv_lengths = false) {
     TileGrid g;
     g.n_qblk = (S_q + kTileM - 1) / kTileM;
-    g.paired = causal ? 1 : 0;
+    g.paired = (causal && !kv_lengths) ? 1 : 0;
     g.items_per_bh = g.paired ? (g.n_qblk + 1) / 2 : g.n_qblk;
     g.n_items = (long long)B * H * g.items_per_bh;
     return g;
