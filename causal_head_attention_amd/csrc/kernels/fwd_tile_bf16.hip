@@ -16,11 +16,13 @@
 // reach a given tile at different times, the one with the shortest block
 // first, so only one of them waits for its first fetch from HBM.
 //
-// Software pipeline, one barrier per tile: in iteration t a wave computes
-// the scores of tile t+1 on the matrix cores while it runs the softmax of
-// tile t on the vector ALUs, then accumulates P(t) V(t). K tiles are staged
-// two tiles ahead and V tiles one ahead (double-buffered LDS for each), so
-// HBM/L2 latency overlaps a whole iteration. Loads go through per-head
+// Software pipeline, one barrier per tile: in iteration t a wave issues
+// P(t-1) V(t-1) and the scores of tile t+1 on the matrix cores while it runs
+// the softmax of tile t on the vector ALUs; no MFMA of an iteration waits
+// for that iteration's vector work. K tiles are staged two tiles ahead, V
+// tiles are loaded in the iteration before the one that reads them
+// (double-buffered LDS for each), so HBM/L2 latency overlaps a whole
+// iteration. Loads go through per-head
 // buffer descriptors: rows past the end read as zeros, with no branches.
 // The score matrix never leaves registers.
 //
@@ -351,7 +353,12 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
 
         // Prologue: tile 0 (K and V) staged; S(0) computed while K(1) lands.
         if (k_loader) store_k<D>(pre, kst(0), tid);
-        else store_v<D>(pre, vst(0), tid);
+        else {
+            store_v<D>(pre, vst(0), tid);
+            // the stage a first-step P.V (with P = 0) reads: finite zeros
+            const u32x4_t z = {0u, 0u, 0u, 0u};
+            for (int i = tid - 256; i < C::V_BYTES / 16; i += 256) *(u32x4_t*)(vst(1) + 16 * i) = z;
+        }
         __syncthreads();
         // step u works on KV tile nt-1-u: the diagonal tile first
         auto tile_of = [&](int u) { return nt - 1 - u; };
@@ -362,22 +369,45 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
         if (k_loader && nt > 1) store_k<D>(pre, kst(1), tid);
         __syncthreads();
 
-        // One tile: s_c holds S(t); S(t+1) goes to s_n.
+        // One tile: s_c holds S(t); S(t+1) goes to s_n. P(t-1) waits in
+        // pb_prev and its P.V product runs in step t, so no MFMA of a step
+        // depends on that step's vector work. V(t) is loaded in step t and
+        // staged at its end; P.V(t-1) reads the stage written one step ago.
+        bf16x8_t pb_prev[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pb_prev[s2][i] = (__bf16)0.f;
+        // a re-base decided in step t scales the accumulator at the start of
+        // step t+1, once P.V(t-1) is in and before P.V(t) is added
+        bool rescale_due = false;
+        float alpha_due = 1.f;
+        auto apply_rescale = [&]() {
+            if (rescale_due) {
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[db][r] *= alpha_due;
+                rescale_due = false;
+            }
+        };
         auto step = [&](int t, f32x16_t& s_c, f32x16_t& s_n) {
-            // (a) HBM loads: K two tiles ahead, V one tile ahead
+            // (a) HBM loads: K two tiles ahead; V of this tile (V(0) came with
+            // the block's opening loads)
             const bool ld_k = k_loader && t + 2 < nt;
-            const bool ld_v = !k_loader && t + 1 < nt;
+            const bool ld_v = !k_loader && t >= 1;
             if (ld_k) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_cap, S_kv, H, tile_of(t + 2) * kTileN), H, tid);
-            if (ld_v) load_v<D>(pre, tile_rsrc<D>(V, b, h, S_cap, S_kv, H, tile_of(t + 1) * kTileN), H, tid);
+            if (ld_v) load_v<D>(pre, tile_rsrc<D>(V, b, h, S_cap, S_kv, H, tile_of(t) * kTileN), H, tid);
 
             const int kbase = tile_of(t) * kTileN + 32 * half;   // first key of this wave's half tile
             const bool work = wave_has_rows && kbase <= key_last && kbase < S_kv;
             // a wave skips the tiles whose keys all lie past its last query (the
-            // first ones in this order); the first tile it does see still needs
-            // its scores from here
+            // first ones in this order, so no P.V is pending there); the first
+            // tile it does see still needs its scores from here
             if (!work && t + 1 < nt && wave_has_rows && kbase - kTileN <= key_last && kbase - kTileN < S_kv)
                 s_n = qk_tile<D>(kst((t + 1) & 1) + k_lane, qf);
             if (work) {
+                apply_rescale();
                 // (b) mask: only where the tile crosses the diagonal or the key end
                 if ((causal && kbase + 31 > q0 + off) || (kbase + 32 > S_kv)) {
 #pragma unroll
@@ -386,44 +416,21 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
                         if (key > lane_key_limit || key >= S_kv) s_c[r] = -INFINITY;
                     }
                 }
-                // (c) row max (one exchange with the partner lane l^32), lazy re-base
                 float mx = s_c[0];
 #pragma unroll
                 for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_c[r]);
+                // (c) row max (one exchange with the partner lane l^32), lazy re-base
                 mx = fmaxf(mx, partner_lane(mx)) * c;   // row max over both half-waves
-                if (__builtin_amdgcn_ballot_w64(mx > m_ref + kLazy)) {
-                    const float m_new = fmaxf(m_ref, mx);
-                    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-                    l_run *= alpha;
-#pragma unroll
-                    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-                    m_ref = m_new;
-                }
+                const bool rebase = __builtin_amdgcn_ballot_w64(mx > m_ref + kLazy) != 0;
+                // re-base: the sum now; the accumulator after P.V(t-1) is in
+                const float m_new = rebase ? fmaxf(m_ref, mx) : m_ref;
+                const float alpha = (m_new == -INFINITY || !rebase) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+                l_run *= alpha;
+                m_ref = m_new;
                 const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-                // (d) next tile's scores on the matrix cores, interleaved with
-                // this tile's exponentials on the vector ALUs
-                s_n = qk_tile<D>(kst((t + 1) & 1) + k_lane, qf);
-                // P is rounded to bf16 for the P.V product; the row sum adds up
-                // the same rounded values, so the weights that multiply V are
-                // exactly normalised (a near one-hot row returns its V row)
-                bf16x8_t pb[2];
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        pb[s2][i] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_c[8 * s2 + i], c, -m_use));
-                    // row sum of the rounded values: one v_dot2 (x 1.0) per pair
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const bf16x2_t pair = {pb[s2][2 * i], pb[s2][2 * i + 1]};
-                        l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, l_run, false);
-                    }
-                }
-                // (e) O^T += V^T . P^T; the V^T operands are read once the
-                // S(t+1) operands are consumed, so both sets share registers
-                const char* vt = vst(t & 1) + v_lane;
+                // (d) O^T += V^T . P(t-1)^T, then S(t+1), both on the matrix
+                // cores while the vector ALUs form P(t)
+                const char* vt = vst((t + 1) & 1) + v_lane;
                 bf16x8_t va[C::DB][2];
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db)
@@ -433,33 +440,63 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
                 for (int db = 0; db < C::DB; ++db)
 #pragma unroll
                     for (int s2 = 0; s2 < 2; ++s2)
-                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][s2], pb[s2], acc[db], 0, 0, 0);
-                // schedule: all K operand reads first, then the S(t+1) MFMAs
-                // each followed by a slice of the softmax VALU work, then the
-                // V^T operand reads and the P.V MFMAs
-                __builtin_amdgcn_sched_group_barrier(0x100, C::KS, 0);
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][s2], pb_prev[s2], acc[db], 0, 0, 0);
+                s_n = qk_tile<D>(kst((t + 1) & 1) + k_lane, qf);
+                // P is rounded to bf16 for the P.V product; the row sum adds up
+                // the same rounded values, so the weights that multiply V are
+                // exactly normalised (a near one-hot row returns its V row)
 #pragma unroll
-                for (int i = 0; i < C::KS / 2; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+                for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        pb_prev[s2][i] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_c[8 * s2 + i], c, -m_use));
+#pragma unroll
+                    // row sum of the rounded values: one v_dot2 (x 1.0) per pair
+                    for (int i = 0; i < 4; ++i) {
+                        const bf16x2_t pair = {pb_prev[s2][2 * i], pb_prev[s2][2 * i + 1]};
+                        l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, l_run, false);
+                    }
                 }
+                // schedule: the V^T operand reads, the P.V MFMAs each followed by
+                // a slice of the softmax VALU work, then the K operand reads and
+                // the S(t+1) MFMAs, likewise interleaved
                 __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::DB, 0);
 #pragma unroll
-                for (int i = 0; i < C::KS / 2; ++i) {
+                for (int i = 0; i < 2 * C::DB; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
                 }
-                __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::DB, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, C::KS, 0);
+#pragma unroll
+                for (int i = 0; i < C::KS; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                }
+                rescale_due = rebase;
+                alpha_due = alpha;
             }
-            // (f) land the prefetched tiles in the stages read one iteration ago
+            // (f) land the loaded tiles in stages whose last reader ran one
+            // iteration ago
             if (ld_k) store_k<D>(pre, kst(t & 1), tid);
-            if (ld_v) store_v<D>(pre, vst((t + 1) & 1), tid);
+            if (ld_v) store_v<D>(pre, vst(t & 1), tid);
             __syncthreads();
         };
         for (int t = 0; t < nt; t += 2) {
             step(t, sa, sb);
             if (t + 1 < nt) step(t + 1, sb, sa);
         }
+        // the last P.V: V(nt-1) was staged at the end of the last step
+        apply_rescale();
+        {
+            const char* vt = vst((nt - 1) & 1) + v_lane;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        *(const bf16x8_t*)(vt + 32 * db * C::VROW + 32 * s2), pb_prev[s2], acc[db], 0, 0, 0);
+        }
+        lds_barrier();   // every wave's reads of the stages are done before the merge reuses them
 
         // the next block's opening loads run under this block's merge
         if (phase + 1 < nphase) issue_block(p);
