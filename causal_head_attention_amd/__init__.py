@@ -38,7 +38,7 @@ class FwdPlan(ctypes.Structure):
 
 
 class DecodePlan(ctypes.Structure):
-    _fields_ = [("chunk", ctypes.c_int), ("n_split_max", ctypes.c_int), ("threads", ctypes.c_int),
+    _fields_ = [("split_workgroups", ctypes.c_int), ("records", ctypes.c_int), ("threads", ctypes.c_int),
                 ("workspace_bytes", ctypes.c_size_t)]
 
 

@@ -249,17 +249,14 @@ int attn_decode_plan(int B, int H, int S_cap, int D, int dtype, attn_decode_plan
         return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: dtype " + std::to_string(dtype) + " not built");
     if (D != 32 && D != 64 && D != 128)
         return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: head dim D=" + std::to_string(D) + " not built");
-    if (attn::decode_n_split_max(S_cap) > attn::kDecodeMaxSplits)
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: S_cap above " +
-                                              std::to_string(attn::kDecodeMaxSplits * attn::kDecodeChunk) +
-                                              " tokens is not built");
-    if (((long long)S_cap + attn::kDecodeChunk) * H * D * elem_size(dtype) > 0x7fffffffLL)
+    // key offsets inside one sequence are 32-bit (a load batch may reach
+    // kDecodeBatch keys past the last valid one)
+    if (((long long)S_cap + attn::kDecodeBatch) * H * D * elem_size(dtype) > 0x7fffffffLL)
         return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: one sequence's cache spans more than 2 GiB");
-    if (tensor_bytes(B, S_cap, H, D, elem_size(dtype)) < 0 ||
-        (long long)attn::decode_n_split_max(S_cap) * H * B > 0x7fffffffLL)
+    if (tensor_bytes(B, S_cap, H, D, elem_size(dtype)) < 0 || attn::decode_records(B) * H > 0x7fffffffLL)
         return fail(ATTN_ERR_INVALID_ARG, "attn_decode: sizes overflow");
-    plan->chunk = attn::kDecodeChunk;
-    plan->n_split_max = attn::decode_n_split_max(S_cap);
+    plan->split_workgroups = attn::kDecodeSplitWGs;
+    plan->records = (int)attn::decode_records(B);
     plan->threads = attn::kDecodeThreads;
     plan->workspace_bytes = attn_decode_workspace_bytes(B, H, S_cap, D);
     return ok();

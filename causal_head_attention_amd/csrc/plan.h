@@ -94,25 +94,34 @@ constexpr int kRowThreads = 64;
 
 // ---------------------------------------------------------------------------
 // Split-KV decode.
-//   Split kernel: one workgroup per (split, b) covering ALL heads of keys
-//   [64*split, 64*split+64): each wave owns a group of heads, each load
-//   instruction reads one token's rows of those heads (contiguous bytes).
-//   Combine kernel: one workgroup per (h, b).
+//   The valid keys of all sequences, laid end to end, form one token space
+//   of T = sum of the lengths. Split workgroup w (of kDecodeSplitWGs) takes
+//   tokens [w*C, (w+1)*C) with C = ceil(T / kDecodeSplitWGs): every
+//   workgroup streams the same number of keys, and a range that crosses a
+//   sequence boundary is processed as one segment per sequence. Each
+//   workgroup covers ALL heads of its keys: each wave owns a group of heads,
+//   each load instruction reads one token's rows of those heads (contiguous
+//   bytes). A segment (w, b) leaves one partial record per head at record
+//   index w + b (unique: see decode.hip).
+//   Combine kernel: one workgroup per (b, h).
 // ---------------------------------------------------------------------------
 constexpr int kDecodeWaves = 8;
-constexpr int kDecodeChunk = 64;          // keys per split
+constexpr int kDecodeSplitWGs = 256;      // one per CU of the chip
 constexpr int kDecodeBatch = 16;          // keys whose loads are in flight together
 constexpr int kDecodeThreads = kDecodeWaves * 64;
 constexpr int kCombineThreads = 512;
-constexpr int kDecodeMaxSplits = 16384;  // S_cap up to 16384 * 64 = 1,048,576 tokens
+constexpr int kDecodeScanLds = 1024;      // length prefix sums kept in LDS up to this many sequences
 
-ATTN_HD inline int decode_n_split_max(int S_cap) {
-    return (S_cap + kDecodeChunk - 1) / kDecodeChunk;
+// Partial records: segment (w, b) uses index w + b, so at most
+// kDecodeSplitWGs + B - 1 of them.
+ATTN_HD inline long long decode_records(int B) {
+    return (long long)kDecodeSplitWGs + B - 1;
 }
 
-// Workspace: per (b, h, split) one float max, one float sum, D float accumulators.
-ATTN_HD inline size_t decode_workspace_floats(int B, int H, int S_cap, int D) {
-    return (size_t)B * (size_t)H * (size_t)decode_n_split_max(S_cap) * (size_t)(D + 2);
+// Workspace: per (record, h) one float max, one float sum, D float
+// accumulators. It does not depend on the cache capacity.
+ATTN_HD inline size_t decode_workspace_floats(int B, int H, int /*S_cap*/, int D) {
+    return (size_t)decode_records(B) * (size_t)H * (size_t)(D + 2);
 }
 
 }  // namespace attn

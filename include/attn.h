@@ -112,17 +112,20 @@ int attn_fwd_kvcache(const void* q, const void* kcache, const void* vcache, cons
 
 /*
  * attn_decode_workspace_bytes -- device workspace attn_decode needs for
- * these sizes (per-split partial max, sum and D accumulators, fp32).
- * Returns 0 for invalid or empty sizes.
+ * these sizes: (256 + B - 1) * H partial records of D + 2 floats (max, sum
+ * and D accumulators). It does not depend on S_cap. Returns 0 for invalid
+ * or empty sizes.
  */
 size_t attn_decode_workspace_bytes(int B, int H, int S_cap, int D);
 
 /*
  * attn_decode -- single-query (GEMV-shaped) masked attention against a KV
  * cache: the per-query mapping of the MMHA page, section 2.1, with the
- * keys split across workgroups and the per-split partial softmax states
- * merged afterwards (rows spanning several blocks need one common
- * normaliser: "Week-4 CUDA notes" page, section 2.2).
+ * keys split across workgroups and the partial softmax states merged
+ * afterwards (rows spanning several blocks need one common normaliser:
+ * "Week-4 CUDA notes" page, section 2.2). The valid keys of all sequences,
+ * laid end to end, are cut into 256 equal ranges, one workgroup each, so
+ * the work is balanced whatever the length mix.
  *
  *   q, o            : [B, 1, H, D]
  *   kcache, vcache  : [B, S_cap, H, D]
@@ -203,12 +206,14 @@ int attn_fwd_plan(int B, int H, int S_q, int S_kv, int D, int causal, int dtype,
                   attn_fwd_plan_t* plan);
 
 /*
- * Decode plan: keys per split, number of split workgroups along the cache
- * (grid.x), and the workspace it needs. Host only.
+ * Decode plan: split workgroups (each streams an equal share of the
+ * sequences' valid keys), the partial records the workspace holds per head
+ * (one per workgroup-sequence segment), threads per workgroup, and the
+ * workspace size. Host only.
  */
 typedef struct {
-    int chunk;
-    int n_split_max;
+    int split_workgroups;
+    int records;
     int threads;
     size_t workspace_bytes;
 } attn_decode_plan_t;

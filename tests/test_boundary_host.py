@@ -143,13 +143,15 @@ def test_xcd_remap_is_a_bijection_with_contiguous_ranges(n):
 # Decode boundary
 # ---------------------------------------------------------------------------
 def test_decode_workspace_and_plan():
-    assert attn.attn_decode_workspace_bytes(16, 32, 4096, 128) == 16 * 32 * 64 * 130 * 4
+    # one record per (workgroup, sequence) segment: at most 256 + B - 1, per head
+    assert attn.attn_decode_workspace_bytes(16, 32, 4096, 128) == (256 + 15) * 32 * 130 * 4
+    assert attn.attn_decode_workspace_bytes(16, 32, 1, 128) == attn.attn_decode_workspace_bytes(16, 32, 4096, 128)
     assert attn.attn_decode_workspace_bytes(0, 32, 4096, 128) == 0
     p = attn.attn_decode_plan(16, 32, 4096, 128, attn.ATTN_BF16)
-    assert (p.chunk, p.n_split_max) == (64, 64)
-    assert attn.attn_decode_plan(1, 1, 257, 64, attn.ATTN_F32).n_split_max == 5
-    with pytest.raises(attn.AttnError):   # beyond the built split count
-        attn.attn_decode_plan(1, 1, 64 * 16384 + 1, 64, attn.ATTN_BF16)
+    assert (p.split_workgroups, p.records, p.threads) == (256, 271, 512)
+    assert p.workspace_bytes == attn.attn_decode_workspace_bytes(16, 32, 4096, 128)
+    with pytest.raises(attn.AttnError):   # one sequence's cache beyond 32-bit offsets
+        attn.attn_decode_plan(1, 32, 1 << 18, 128, attn.ATTN_BF16)
 
 
 def dec(q=A, kc=A + 0x100000, vc=A + 0x200000, sl=A + 0x300000, o=A + 0x310000, B=2, H=2, S_cap=100,

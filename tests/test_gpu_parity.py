@@ -215,6 +215,44 @@ def test_decode_lengths(attn, dtype, D):
     check(o.cuda(), ref, dtype, f"decode D={D}")
 
 
+# The split cuts the sequences' valid keys, laid end to end, into 256 equal
+# ranges: short and empty sequences put several sequences into one range and
+# leave ranges empty; more than 1024 sequences take the path that rescans the
+# lengths in memory instead of LDS.
+DECODE_SEGMENTS = [
+    # seed, B, H, S_cap, D, length range
+    (401, 5, 2, 16, 32, (0, 8)),          # 13-ish keys in all: one key per workgroup, most idle
+    (402, 300, 2, 8, 64, (-1, 4)),        # about 2 keys per sequence: ranges span many sequences
+    (403, 1100, 2, 40, 32, (-2, 45)),     # beyond the LDS length scan
+    (404, 3, 4, 3000, 128, (2500, 3000)), # long sequences: several ranges each
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("case", DECODE_SEGMENTS, ids=lambda c: f"B{c[1]}_S{c[3]}")
+def test_decode_balanced_segments(attn, case, dtype):
+    seed, B, H, S_cap, D, (lo, hi) = case
+    say(f"decode segments seed={seed} B={B} H={H} S_cap={S_cap} D={D} {dtype}")
+    g = torch.Generator().manual_seed(seed)
+    sl = torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int32)
+    q = torch.randn(B, 1, H, D, generator=g).to(dtype)
+    kc = torch.randn(B, S_cap, H, D, generator=g).to(dtype)
+    vc = torch.randn(B, S_cap, H, D, generator=g).to(dtype)
+    for b in range(B):
+        n = max(0, min(int(sl[b]), S_cap))
+        kc[b, n:] = float("nan")
+        vc[b, n:] = float("nan")
+    o = attn.attn_decode(q.cuda(), kc.cuda(), vc.cuda(), sl.cuda())
+    torch.cuda.synchronize()
+    oc = o.cpu()
+    empty = sl <= 0
+    assert torch.all(oc[empty] == 0)
+    ref = oracle.attn_decode(q, kc, vc, sl.numpy())
+    check(o, ref, dtype, f"decode segments B={B}")
+    o2 = attn.attn_decode(q.cuda(), kc.cuda(), vc.cuda(), sl.cuda())
+    assert torch.equal(o2.cpu(), oc)   # fixed merge order: the same bits every run
+
+
 def test_decode_matches_forward_with_one_query(attn):
     """attn_decode row b equals attn_fwd(S_q = 1, S_kv = len_b) on the same data."""
     B, H, S_cap, D = 4, 4, 700, 128
