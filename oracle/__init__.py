@@ -10,7 +10,8 @@ it with ctypes and widens inputs to fp64 exactly. Passages followed: the
 "Hand-written Masked Multi-Head Attention CUDA kernel" page, sections 2,
 2.1 and 2.2 (definition, [B,S,H,D] layout, j <= i), and the "Week-4 CUDA
 notes" page, section 2.2 (unfused softmax(QK^T/sqrt(d))V, -inf mask, max
-subtraction; the running sum whose log is the log-sum-exp output).
+subtraction; the running sum whose log is the log-sum-exp output; a padded
+key's score set to -inf so that its weight is exactly 0).
 """
 from __future__ import annotations
 
@@ -55,6 +56,9 @@ def _load():
             lib.oracle_attn_decode_f64.restype = ctypes.c_int
             lib.oracle_attn_fwd_kvcache_f64.argtypes = [dp, dp, dp, ip, dp, dp] + [ctypes.c_int] * 6
             lib.oracle_attn_fwd_kvcache_f64.restype = ctypes.c_int
+            u8p = ctypes.POINTER(ctypes.c_uint8)
+            lib.oracle_attn_fwd_mask_f64.argtypes = [dp, dp, dp, u8p, dp, dp] + [ctypes.c_int] * 6
+            lib.oracle_attn_fwd_mask_f64.restype = ctypes.c_int
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
             _lib = lib
@@ -138,6 +142,35 @@ def attn_fwd_kvcache(q, kcache, vcache, seqlens=None, causal: bool = True):
         _ptr(o), _ptr(lse), B, H, S_q, S_cap, D, int(bool(causal)))
     if rc != 0:
         raise ValueError(f"oracle_attn_fwd_kvcache_f64 rejected the arguments (code {rc})")
+    return o, lse
+
+
+def attn_fwd_mask(q, k, v, key_mask=None, causal: bool = True):
+    """Forward with a key-padding mask, plus log-sum-exp.
+
+    q [B,S_q,H,D]; k, v [B,S_kv,H,D]; key_mask [B,S_kv] (nonzero = visible) or
+    None. Returns (O [B,S_q,H,D], LSE [B,H,S_q]) as fp64 numpy arrays; rows with
+    no visible key are 0 with LSE -inf.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, S_q, H, D = q.shape
+    S_kv = k.shape[1]
+    if k.shape != (B, S_kv, H, D) or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    km = None
+    if key_mask is not None:
+        if hasattr(key_mask, "numpy"):
+            key_mask = key_mask.cpu().numpy()
+        km = np.ascontiguousarray(np.asarray(key_mask) != 0, dtype=np.uint8)
+        if km.shape != (B, S_kv):
+            raise ValueError("key_mask must be [B, S_kv]")
+    o = np.zeros((B, S_q, H, D), dtype=np.float64)
+    lse = np.zeros((B, H, S_q), dtype=np.float64)
+    rc = _load().oracle_attn_fwd_mask_f64(
+        _ptr(q), _ptr(k), _ptr(v), km.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)) if km is not None else None,
+        _ptr(o), _ptr(lse), B, H, S_q, S_kv, D, int(bool(causal)))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_fwd_mask_f64 rejected the arguments (code {rc})")
     return o, lse
 
 

@@ -34,7 +34,12 @@
  *     queries are the last S_q positions (query i at len_b - S_q + i); a
  *     query that sees no key at all gets a zero output row;
  *   - the log-sum-exp of a row is ln(sum_j exp(S[i][j])) over its visible
- *     keys (the log of the softmax denominator), -inf for a row with none.
+ *     keys (the log of the softmax denominator), -inf for a row with none;
+ *   - key-padding mask: a byte per (b, key), 0 hides the key from every
+ *     query of entry b (its score is -inf, so exp gives exactly 0: "Week-4
+ *     CUDA notes" page, section 2.2); it combines with the causal rule, and
+ *     a row left with no visible key is a zero row. Hidden keys still enter
+ *     O = P V with weight 0, so their values must be finite.
  *
  * The score matrix of one (b, h) is materialised in full (S_q*S_kv doubles),
  * the three stages run as three separate passes over it, and OpenMP only
@@ -68,17 +73,19 @@ static size_t at(long b, long s, long h, long d, long S, long H, long D) {
 static int oracle_head(const double* q, const double* k, const double* v, double* o,
                        double* p_out, double* lse_out, long b, long h, long H, long D,
                        long S_q, long S_qdim, long S_kv, long S_kdim, int causal,
+                       const uint8_t* kmask /* this entry's S_kv key bytes, or NULL */,
                        double* S /* scratch, S_q*S_kv */) {
     const double scale = 1.0 / sqrt((double)D);
     const long off = S_kv - S_q; /* absolute position of query i is i + off */
     long i;
 
-    /* Pass 1: scores S = Q K^T * scale, masked entries set to -inf. */
+    /* Pass 1: scores S = Q K^T * scale, masked entries (causal rule or key
+     * mask) set to -inf. */
 #pragma omp parallel for schedule(static)
     for (i = 0; i < S_q; ++i) {
         double* row = S + (size_t)i * (size_t)S_kv;
         for (long j = 0; j < S_kv; ++j) {
-            if (causal && j > i + off) {
+            if ((causal && j > i + off) || (kmask && kmask[j] == 0)) {
                 row[j] = -INFINITY;
                 continue;
             }
@@ -151,7 +158,7 @@ int oracle_attn_fwd_f64(const double* q, const double* k, const double* v, doubl
     if (!S) return ORACLE_ENOMEM;
     for (long b = 0; b < B; ++b)
         for (long h = 0; h < H; ++h)
-            oracle_head(q, k, v, o, p, NULL, b, h, H, D, S_q, S_q, S_kv, S_kv, causal, S);
+            oracle_head(q, k, v, o, p, NULL, b, h, H, D, S_q, S_q, S_kv, S_kv, causal, NULL, S);
     free(S);
     return ORACLE_OK;
 }
@@ -179,7 +186,7 @@ int oracle_attn_decode_f64(const double* q, const double* kcache, const double* 
                 for (long d = 0; d < D; ++d) o[at(b, 0, h, d, 1, H, D)] = 0.0;
                 continue;
             }
-            oracle_head(q, kcache, vcache, o, NULL, NULL, b, h, H, D, 1, 1, n, S_cap, 1, S);
+            oracle_head(q, kcache, vcache, o, NULL, NULL, b, h, H, D, 1, 1, n, S_cap, 1, NULL, S);
         }
     }
     free(S);
@@ -218,9 +225,33 @@ int oracle_attn_fwd_kvcache_f64(const double* q, const double* kcache, const dou
                 }
                 continue;
             }
-            oracle_head(q, kcache, vcache, o, NULL, lse, b, h, H, D, S_q, S_q, n, S_cap, causal, S);
+            oracle_head(q, kcache, vcache, o, NULL, lse, b, h, H, D, S_q, S_q, n, S_cap, causal, NULL, S);
         }
     }
+    free(S);
+    return ORACLE_OK;
+}
+
+/*
+ * Forward with a key-padding mask, plus the log-sum-exp of every row.
+ *   q, o     : [B, S_q, H, D];  k, v : [B, S_kv, H, D]
+ *   key_mask : uint8 [B, S_kv]; 0 hides key j of entry b from all its
+ *              queries (NULL: every key visible, the forward above)
+ *   lse      : optional [B, H, S_q] (NULL to skip)
+ * The causal rule (bottom-right aligned) applies as well when causal is 1.
+ * A row with no visible key gets a zero output row and log-sum-exp -inf.
+ */
+int oracle_attn_fwd_mask_f64(const double* q, const double* k, const double* v, const uint8_t* key_mask,
+                             double* o, double* lse, int B, int H, int S_q, int S_kv, int D, int causal) {
+    if (B <= 0 || H <= 0 || S_q <= 0 || S_kv <= 0 || D <= 0) return ORACLE_EINVAL;
+    if (causal != 0 && causal != 1) return ORACLE_EINVAL;
+    if (causal && S_q > S_kv) return ORACLE_EINVAL;
+    double* S = (double*)malloc(sizeof(double) * (size_t)S_q * (size_t)S_kv);
+    if (!S) return ORACLE_ENOMEM;
+    for (long b = 0; b < B; ++b)
+        for (long h = 0; h < H; ++h)
+            oracle_head(q, k, v, o, NULL, lse, b, h, H, D, S_q, S_q, S_kv, S_kv, causal,
+                        key_mask ? key_mask + (size_t)b * (size_t)S_kv : NULL, S);
     free(S);
     return ORACLE_OK;
 }

@@ -359,6 +359,99 @@ def test_kvcache_rows_that_see_no_key():
     assert np.array_equal(o[2], full[2])
 
 
+# ---------------------------------------------------------------------------
+# Key-padding mask ("Week-4 CUDA notes" page, section 2.2: a padded position's
+# score is set to -inf so that its exponential is exactly 0)
+# ---------------------------------------------------------------------------
+def _mask_reference(q, k, v, key_mask, causal):
+    """torch float64 SDPA with the explicit boolean mask (key mask AND the
+    bottom-right causal rule) and logsumexp of the explicitly scaled scores;
+    rows that see no key stay 0 / -inf."""
+    B, S_q, H, D = q.shape
+    S_kv = k.shape[1]
+    o = np.zeros_like(q)
+    lse = np.full((B, H, S_q), -np.inf)
+    i = torch.arange(S_q)[:, None]
+    j = torch.arange(S_kv)[None, :]
+    for b in range(B):
+        vis = torch.from_numpy(np.asarray(key_mask[b]) != 0)[None, :].expand(S_q, S_kv)
+        if causal:
+            vis = vis & (j <= i + (S_kv - S_q))
+        rows = vis.any(dim=1)
+        qt = torch.from_numpy(q[b]).permute(1, 0, 2)
+        kt = torch.from_numpy(k[b]).permute(1, 0, 2)
+        vt = torch.from_numpy(v[b]).permute(1, 0, 2)
+        s = ((qt @ kt.transpose(1, 2)) / math.sqrt(D)).masked_fill(~vis, -math.inf)
+        if rows.any():
+            lse[b][:, rows.numpy()] = torch.logsumexp(s[:, rows], dim=-1).numpy()
+            ob = torch.nn.functional.scaled_dot_product_attention(qt[:, rows], kt, vt, attn_mask=vis[rows])
+            o[b][rows.numpy()] = ob.permute(1, 0, 2).numpy()
+    return o, lse
+
+
+@pytest.mark.parametrize("S_q,S_kv,causal", [(23, 23, True), (9, 31, True), (17, 40, False), (40, 17, False)])
+def test_key_mask_matches_sdpa_and_logsumexp_float64(S_q, S_kv, causal):
+    B, H, D = 3, 2, 16
+    q, k, v = rnd(241, B, S_q, H, D), rnd(242, B, S_kv, H, D), rnd(243, B, S_kv, H, D)
+    g = np.random.default_rng(244)
+    km = (g.random((B, S_kv)) < 0.6).astype(np.uint8)
+    km[1, :] = 0
+    km[1, S_kv - 1] = 1            # entry 1: only its last key (causal: only the last query sees it)
+    km[2, :] = 0                   # entry 2: nothing visible at all
+    o, lse = oracle.attn_fwd_mask(q, k, v, km, causal)
+    ro, rlse = _mask_reference(q, k, v, km, causal)
+    assert np.all(np.isfinite(o))
+    assert np.max(np.abs(o - ro)) <= 1e-12
+    assert np.array_equal(np.isneginf(lse), np.isneginf(rlse))
+    fin = np.isfinite(rlse)
+    assert np.max(np.abs(lse[fin] - rlse[fin])) <= 1e-12
+    assert np.all(o[2] == 0.0) and np.all(np.isneginf(lse[2]))
+
+
+def test_key_mask_equals_deleting_the_keys():
+    """Without the causal rule, hiding keys is the same as removing their rows
+    from K and V (the plain forward on the remaining keys)."""
+    B, S_q, S_kv, H, D = 3, 11, 26, 2, 8
+    q, k, v = rnd(251, B, S_q, H, D, std=1.5), rnd(252, B, S_kv, H, D, std=1.5), rnd(253, B, S_kv, H, D)
+    g = np.random.default_rng(254)
+    km = (g.random((B, S_kv)) < 0.5).astype(np.uint8)
+    km[:, 3] = 1
+    o, _ = oracle.attn_fwd_mask(q, k, v, km, causal=False)
+    for b in range(B):
+        keep = np.nonzero(km[b])[0]
+        ref = oracle.attn_fwd(q[b:b + 1], k[b:b + 1, keep].copy(), v[b:b + 1, keep].copy(), causal=False)
+        assert np.max(np.abs(o[b:b + 1] - ref)) <= 1e-12
+
+
+def test_key_mask_with_equal_keys_gives_means_of_the_visible_values():
+    """All keys equal: every visible key has the same weight, so row i is the
+    plain mean of the values of the keys it may see (closed form)."""
+    B, S, H, D = 2, 19, 2, 8
+    q, v = rnd(261, B, S, H, D), rnd(262, B, S, H, D)
+    k = np.broadcast_to(rnd(263, B, 1, H, D), (B, S, H, D)).copy()
+    km = np.ones((B, S), dtype=np.uint8)
+    km[0, [0, 4, 5, 11]] = 0
+    km[1, 1::2] = 0
+    o, _ = oracle.attn_fwd_mask(q, k, v, km, causal=True)
+    for b in range(B):
+        for i in range(S):
+            vis = [j for j in range(i + 1) if km[b, j]]
+            if vis:
+                np.testing.assert_allclose(o[b, i], v[b, vis].mean(axis=0), rtol=0, atol=1e-13)
+            else:
+                assert np.all(o[b, i] == 0.0)
+
+
+def test_key_mask_absent_or_all_visible_is_the_forward():
+    B, S, H, D = 2, 15, 3, 16
+    q, k, v = rnd(271, B, S, H, D), rnd(272, B, S, H, D), rnd(273, B, S, H, D)
+    for causal in (True, False):
+        ref = oracle.attn_fwd(q, k, v, causal)
+        o1, l1 = oracle.attn_fwd_mask(q, k, v, None, causal)
+        o2, l2 = oracle.attn_fwd_mask(q, k, v, np.ones((B, S), dtype=np.uint8), causal)
+        assert np.array_equal(o1, ref) and np.array_equal(o2, ref) and np.array_equal(l1, l2)
+
+
 def test_rejects_invalid_arguments():
     q = rnd(1, 1, 4, 1, 8)
     with pytest.raises(ValueError):

@@ -19,10 +19,10 @@ from tests import test_oracle as pins
 SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
 
 MUTANTS = {
-    "diagonal_hidden": ("if (causal && j > i + off)", "if (causal && j >= i + off)"),
+    "diagonal_hidden": ("(causal && j > i + off)", "(causal && j >= i + off)"),
     "alignment_top_left": ("const long off = S_kv - S_q;", "const long off = 0;"),
     "alignment_sign": ("const long off = S_kv - S_q;", "const long off = S_q - S_kv;"),
-    "mask_ignored": ("if (causal && j > i + off)", "if (0 && j > i + off)"),
+    "mask_ignored": ("(causal && j > i + off)", "(0 && j > i + off)"),
     "scale_dropped": ("row[j] = dot * scale;", "row[j] = dot;"),
     "scale_is_1_over_d": ("1.0 / sqrt((double)D)", "1.0 / (double)D"),
     "values_replaced_by_keys": ("const double* vrow = v + at(", "const double* vrow = k + at("),
@@ -38,6 +38,10 @@ MUTANTS = {
     "lse_log2": ("= m + log(l);", "= m + log2(l);"),
     "kvcache_ignores_lengths": ("long n = seqlens ? seqlens[b] : S_cap;", "long n = S_cap;"),
     "empty_rows_not_zero": ("if (m == -INFINITY) {", "if (0) {"),
+    "key_mask_ignored": ("(kmask && kmask[j] == 0)", "(0)"),
+    "key_mask_inverted": ("kmask[j] == 0", "kmask[j] != 0"),
+    "key_mask_on_queries": ("(kmask && kmask[j] == 0)", "(kmask && kmask[i % S_kv] == 0)"),
+    "key_mask_of_entry_0_for_all": ("key_mask ? key_mask + (size_t)b * (size_t)S_kv : NULL", "key_mask"),
 }
 
 PINS = [
@@ -57,6 +61,9 @@ PINS = [
     lambda: pins.test_kvcache_matches_sdpa_and_logsumexp_float64(True),
     pins.test_lse_merges_results_over_disjoint_key_sets,
     pins.test_kvcache_rows_that_see_no_key,
+    lambda: pins.test_key_mask_matches_sdpa_and_logsumexp_float64(9, 31, True),
+    pins.test_key_mask_equals_deleting_the_keys,
+    pins.test_key_mask_with_equal_keys_gives_means_of_the_visible_values,
 ]
 
 
