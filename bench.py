@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 BF16_MFMA_PEAK_TFLOPS = 2516.6   # MI355X dense bf16: 256 CU x 4096 FLOP/clk x 2.4 GHz
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 FLUSH_BYTES = 512 << 20
-TILE_SRC = os.path.join(ROOT, "causal_head_attention_amd", "csrc", "kernels", "fwd_tile_bf16.hip")
+TILE_SRC = os.path.join(ROOT, "causal_head_attention_amd", "csrc", "kernels", "fwd_tile.hip")
 DECODE_SRC = os.path.join(ROOT, "causal_head_attention_amd", "csrc", "kernels", "decode.hip")
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -108,7 +108,7 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, copy_mib: int = 256) -
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            if "fwd_tile_bf16_kernel" in name and r["Grid_Size"] != prefill_grid:
+            if "fwd_tile_kernel" in name and r["Grid_Size"] != prefill_grid:
                 name += " [kvcache]"   # the KV-cache launch of the same kernel
             vals.setdefault(name, []).append(float(r["Counter_Value"]))
         return vals
@@ -128,8 +128,8 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, copy_mib: int = 256) -
                     f"scaled by what the counter reads for a {copy_mib} MiB device copy: FETCH_SIZE x {f_scale:.5f}, "
                     f"WRITE_SIZE x {w_scale:.5f}.")}
     rows = []
-    prefill = {"fetch_kib": mean_of(fetch, "fwd_tile_bf16_kernelILi128"),
-               "write_kib": mean_of(write, "fwd_tile_bf16_kernelILi128")}
+    prefill = {"fetch_kib": mean_of(fetch, "fwd_tile_kernelIDF16bLi128ELb0"),
+               "write_kib": mean_of(write, "fwd_tile_kernelIDF16bLi128ELb0")}
     split = {"fetch_kib": mean_of(fetch, "decode_split_kernelIDF16bLi128"),
              "write_kib": mean_of(write, "decode_split_kernelIDF16bLi128")}
     comb = {"fetch_kib": mean_of(fetch, "decode_combine_kernelIDF16bLi128"),
@@ -137,7 +137,7 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, copy_mib: int = 256) -
     pb = round((prefill["fetch_kib"] * f_scale + prefill["write_kib"] * w_scale) * 1024)
     db = round(((split["fetch_kib"] + comb["fetch_kib"]) * f_scale + (split["write_kib"] + comb["write_kib"]) * w_scale)
                * 1024)
-    out["fwd_tile_bf16"] = {"bytes_per_launch": pb, "algorithmic_bytes": 4 * 2048 * 32 * 128 * 2,
+    out["fwd_tile"] = {"bytes_per_launch": pb, "algorithmic_bytes": 4 * 2048 * 32 * 128 * 2,
                             "counters_kib": prefill, "source_sha256": sha256(TILE_SRC)}
     out["decode"] = {"bytes_per_launch": db, "counters_kib": {"split": split, "combine": comb},
                      "source_sha256": sha256(DECODE_SRC), "note": "one call = split + combine kernels"}
@@ -341,8 +341,8 @@ def main() -> int:
                    "decode_tokens": int(sum(int(x) for x in seqlens_h))},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("fwd_tile_bf16", TILE_SRC),
-                     "kernel": "fwd_tile_bf16_kernel<128>", "flop_per_launch": flops,
+                     "traffic": measured_traffic("fwd_tile", TILE_SRC),
+                     "kernel": "fwd_tile_kernel<bf16,128>", "flop_per_launch": flops,
                      "mean_launch_us": round(fwd_mean * 1e3, 2),
                      "median_launch_us": round(statistics.median(fwd_ms) * 1e3, 2),
                      "p95_launch_us": round(float(np.percentile(fwd_ms, 95)) * 1e3, 2)},

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 ATTN_F32, ATTN_BF16, ATTN_F16 = 0, 1, 2
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = 0, 1, 2, 3, 4
 
-_DTYPES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
+_DTYPES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}
 
 
 class AttnError(RuntimeError):
@@ -59,6 +59,8 @@ def _load() -> ctypes.CDLL:
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, sz]
     lib.attn_decode.restype = i
+    lib.attn_fwd_mask.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i]
+    lib.attn_fwd_mask.restype = i
     lib.attn_set_stream.argtypes = [vp]
     lib.attn_set_stream.restype = i
     lib.attn_set_timing_events.argtypes = [vp, vp]
@@ -103,7 +105,7 @@ def _check(status: int) -> None:
 
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype not in _DTYPES:
-        raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+        raise TypeError(f"unsupported dtype {t.dtype}: float32, bfloat16 or float16")
     return _DTYPES[t.dtype]
 
 
@@ -180,6 +182,42 @@ def attn_fwd_kvcache(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor
     return (o, lse) if return_lse else o
 
 
+def attn_fwd_mask(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_mask: torch.Tensor | None = None,
+                  o: torch.Tensor | None = None, causal: bool = True, return_lse: bool = False):
+    """Forward with a key-padding mask. q [B,S_q,H,D]; k, v [B,S_kv,H,D]; key_mask [B,S_kv] on the GPU
+    (bool or uint8; False / 0 hides the key from every query of its entry) or None.
+    Returns o, or (o, lse) with lse float32 [B,H,S_q] when return_lse is set."""
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(n, t, 4)
+    B, S_q, H, D = q.shape
+    S_kv = k.shape[1]
+    if tuple(k.shape) != (B, S_kv, H, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if key_mask is not None:
+        _dev_tensor("key_mask", key_mask, 2)
+        if tuple(key_mask.shape) != (B, S_kv):
+            raise ValueError(f"key_mask must be [B, S_kv] = {(B, S_kv)}, got {tuple(key_mask.shape)}")
+        if key_mask.dtype == torch.bool:
+            key_mask = key_mask.view(torch.uint8)
+        elif key_mask.dtype != torch.uint8:
+            raise TypeError("key_mask must be bool or uint8")
+    if o is None:
+        o = torch.empty_like(q)
+    else:
+        _dev_tensor("o", o, 4)
+        if tuple(o.shape) != tuple(q.shape) or o.dtype != q.dtype:
+            raise ValueError("o must match q in shape and dtype")
+    lse = torch.empty((B, H, S_q), dtype=torch.float32, device=q.device) if return_lse else None
+    _set_stream(q.device)
+    _check(load().attn_fwd_mask(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                key_mask.data_ptr() if key_mask is not None else None, o.data_ptr(),
+                                lse.data_ptr() if lse is not None else None, B, H, S_q, S_kv, D,
+                                int(bool(causal)), _dtype_code(q)))
+    return (o, lse) if return_lse else o
+
+
 def attn_decode_workspace_bytes(B: int, H: int, S_cap: int, D: int) -> int:
     return int(load().attn_decode_workspace_bytes(B, H, S_cap, D))
 
@@ -228,6 +266,6 @@ def attn_decode_plan(B: int, H: int, S_cap: int, D: int, dtype: int) -> DecodePl
     return plan
 
 
-__all__ = ["attn_fwd", "attn_fwd_kvcache", "attn_decode", "attn_decode_workspace_bytes", "attn_fwd_plan", "attn_decode_plan",
+__all__ = ["attn_fwd", "attn_fwd_kvcache", "attn_fwd_mask", "attn_decode", "attn_decode_workspace_bytes", "attn_fwd_plan", "attn_decode_plan",
            "attn_set_timing_events",
-           "AttnError", "ATTN_F32", "ATTN_BF16", "lib", "LIB_PATH"]
+           "AttnError", "ATTN_F32", "ATTN_BF16", "ATTN_F16", "lib", "LIB_PATH"]

@@ -66,6 +66,12 @@ bool overlap(const void* a, long long na, const void* b, long long nb) {
 
 int elem_size(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
 
+bool dtype_built(int dtype) { return dtype == ATTN_F32 || dtype == ATTN_BF16 || dtype == ATTN_F16; }
+
+attn::Elt elt_of(int dtype) {
+    return dtype == ATTN_BF16 ? attn::Elt::BF16 : (dtype == ATTN_F16 ? attn::Elt::F16 : attn::Elt::F32);
+}
+
 enum Algo { kAuto, kTile, kRow };
 
 Algo algo_from_env() {
@@ -76,20 +82,20 @@ Algo algo_from_env() {
     return kAuto;
 }
 
-// Checks shared by attn_fwd, attn_fwd_kvcache and attn_fwd_plan (sizes and
-// flags only). With kvcache, S_kv is the cache capacity and the per-entry
+// Checks shared by attn_fwd, attn_fwd_kvcache, attn_fwd_mask and
+// attn_fwd_plan (sizes and flags only). With kvcache, S_kv is the cache capacity and the per-entry
 // lengths may be shorter than S_q (rows that see no key come out as 0).
-int check_fwd_sizes(int B, int H, int S_q, int S_kv, int D, int causal, int dtype, bool kvcache = false) {
-    const char* fn = kvcache ? "attn_fwd_kvcache" : "attn_fwd";
+int check_fwd_sizes(int B, int H, int S_q, int S_kv, int D, int causal, int dtype, bool kvcache = false,
+                    const char* fn = "attn_fwd") {
     if (B < 0 || H < 0 || S_q < 0 || S_kv < 0)
         return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + ": negative size (B=" + std::to_string(B) + " H=" +
                                               std::to_string(H) + " S_q=" + std::to_string(S_q) +
                                               " S_kv=" + std::to_string(S_kv) + ")");
     if (D <= 0) return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + ": head dim D must be positive");
     if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + ": causal must be 0 or 1");
-    if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+    if (!dtype_built(dtype))
         return fail(ATTN_ERR_UNSUPPORTED, std::string(fn) + ": dtype " + std::to_string(dtype) +
-                                              " not built (ATTN_F32=0, ATTN_BF16=1)");
+                                              " not built (ATTN_F32=0, ATTN_BF16=1, ATTN_F16=2)");
     if (D != 32 && D != 64 && D != 128)
         return fail(ATTN_ERR_UNSUPPORTED, std::string(fn) + ": head dim D=" + std::to_string(D) +
                                               " not built (32, 64 or 128)");
@@ -99,51 +105,55 @@ int check_fwd_sizes(int B, int H, int S_q, int S_kv, int D, int causal, int dtyp
         return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + (kvcache ? ": S_cap == 0 leaves no cache rows"
                                                                      : ": S_kv == 0 leaves the softmax without keys"));
     if (!kvcache && causal && S_q > S_kv)
-        return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: causal needs S_q <= S_kv (queries are the last S_q positions)");
+        return fail(ATTN_ERR_INVALID_ARG, std::string(fn) +
+                                              ": causal needs S_q <= S_kv (queries are the last S_q positions)");
     const int es = elem_size(dtype);
     if (tensor_bytes(B, S_q, H, D, es) < 0 || tensor_bytes(B, S_kv, H, D, es) < 0)
-        return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: tensor size overflows");
+        return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + ": tensor size overflows");
     if ((long long)B * H * S_q > 0x7fffffffLL || (long long)B * H * ((S_q + 127) / 128) > 0x7fffffffLL)
-        return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: B*H*S_q exceeds the launch grid");
+        return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + ": B*H*S_q exceeds the launch grid");
     // the kernels address one head's rows with 32-bit byte offsets
     const long long S_max = (S_q > S_kv ? S_q : S_kv) + 128;
     if (S_max * H * D * es > 0x7fffffffLL)
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: one batch entry spans more than 2 GiB "
-                                          "((S + 128) * H * D * elem_size); split the batch");
+        return fail(ATTN_ERR_UNSUPPORTED, std::string(fn) + ": one batch entry spans more than 2 GiB "
+                                                            "((S + 128) * H * D * elem_size); split the batch");
     return ATTN_OK;
 }
 
-// attn_fwd and attn_fwd_kvcache: pointer checks and dispatch.
-int run_fwd(const char* fn, const void* q, const void* k, const void* v, const int32_t* kv_lens, void* o,
-            float* lse, int B, int H, int S_q, int S_kv, int D, int causal, int dtype, bool kvcache) {
+// attn_fwd, attn_fwd_kvcache and attn_fwd_mask: pointer checks and dispatch.
+int run_fwd(const char* fn, const void* q, const void* k, const void* v, const int32_t* kv_lens,
+            const uint8_t* key_mask, void* o, float* lse, int B, int H, int S_q, int S_kv, int D, int causal,
+            int dtype, bool kvcache) {
     hipEvent_t ev_start, ev_stop;
     take_events(ev_start, ev_stop);
-    const int st = check_fwd_sizes(B, H, S_q, S_kv, D, causal, dtype, kvcache);
+    const int st = check_fwd_sizes(B, H, S_q, S_kv, D, causal, dtype, kvcache, fn);
     if (st != ATTN_OK) return st;
     if ((long long)B * H * S_q == 0) return ok();
     const int es = elem_size(dtype);
     const long long nq = tensor_bytes(B, S_q, H, D, es), nkv = tensor_bytes(B, S_kv, H, D, es);
     const long long nlse = lse ? (long long)B * H * S_q * 4 : 0, nlen = kv_lens ? (long long)B * 4 : 0;
+    const long long nmask = key_mask ? (long long)B * S_kv : 0;
     if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + ": NULL tensor pointer");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + ": tensor pointers must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(kv_lens) & 3u))
         return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + ": lse and seqlens_kv must be 4-byte aligned");
     if (overlap(o, nq, q, nq) || overlap(o, nq, k, nkv) || overlap(o, nq, v, nkv) || overlap(o, nq, kv_lens, nlen) ||
-        overlap(o, nq, lse, nlse))
+        overlap(o, nq, lse, nlse) || overlap(o, nq, key_mask, nmask))
         return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + ": output overlaps another argument");
     if (overlap(lse, nlse, q, nq) || overlap(lse, nlse, k, nkv) || overlap(lse, nlse, v, nkv) ||
-        overlap(lse, nlse, kv_lens, nlen))
+        overlap(lse, nlse, kv_lens, nlen) || overlap(lse, nlse, key_mask, nmask))
         return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + ": lse overlaps an input");
 
     attn::FwdArgs a{q, k, v, o, B, H, S_q, S_kv, D, causal,
-                    (float)(1.0f / std::sqrt((float)D)) * 1.4426950408889634f, ev_start, ev_stop, kv_lens, lse};
+                    (float)(1.0f / std::sqrt((float)D)) * 1.4426950408889634f, ev_start, ev_stop, kv_lens, lse,
+                    key_mask};
     const Algo algo = algo_from_env();
     hipError_t e;
-    if (dtype == ATTN_BF16 && algo != kRow)
-        e = attn::launch_fwd_tile_bf16(a, t_stream);
+    if (dtype != ATTN_F32 && algo != kRow)
+        e = attn::launch_fwd_tile(a, elt_of(dtype), t_stream);
     else
-        e = attn::launch_fwd_row(a, dtype == ATTN_BF16, t_stream);
+        e = attn::launch_fwd_row(a, elt_of(dtype), t_stream);
     if (e != hipSuccess)
         return fail(ATTN_ERR_HIP, std::string(fn) + ": launch failed: " + hipGetErrorString(e));
     return ok();
@@ -191,7 +201,7 @@ int attn_fwd_plan(int B, int H, int S_q, int S_kv, int D, int causal, int dtype,
     if (st != ATTN_OK) return st;
     if ((long long)B * H * S_q == 0) return ok();
     const Algo algo = algo_from_env();
-    const bool tile = dtype == ATTN_BF16 && algo != kRow;
+    const bool tile = dtype != ATTN_F32 && algo != kRow;
     if (tile) {
         const attn::TileGrid g = attn::tile_grid(B, H, S_q, causal);
         plan->kernel = 1;
@@ -226,13 +236,18 @@ int attn_fwd_plan(int B, int H, int S_q, int S_kv, int D, int causal, int dtype,
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q, int S_kv, int D,
              int causal, int dtype) {
-    return run_fwd("attn_fwd", q, k, v, nullptr, o, nullptr, B, H, S_q, S_kv, D, causal, dtype, false);
+    return run_fwd("attn_fwd", q, k, v, nullptr, nullptr, o, nullptr, B, H, S_q, S_kv, D, causal, dtype, false);
+}
+
+int attn_fwd_mask(const void* q, const void* k, const void* v, const uint8_t* key_mask, void* o, float* lse, int B,
+                  int H, int S_q, int S_kv, int D, int causal, int dtype) {
+    return run_fwd("attn_fwd_mask", q, k, v, nullptr, key_mask, o, lse, B, H, S_q, S_kv, D, causal, dtype, false);
 }
 
 int attn_fwd_kvcache(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens_kv, void* o,
                      float* lse, int B, int H, int S_q, int S_cap, int D, int causal, int dtype) {
-    return run_fwd("attn_fwd_kvcache", q, kcache, vcache, seqlens_kv, o, lse, B, H, S_q, S_cap, D, causal, dtype,
-                   true);
+    return run_fwd("attn_fwd_kvcache", q, kcache, vcache, seqlens_kv, nullptr, o, lse, B, H, S_q, S_cap, D, causal,
+                   dtype, true);
 }
 
 size_t attn_decode_workspace_bytes(int B, int H, int S_cap, int D) {
@@ -245,7 +260,7 @@ int attn_decode_plan(int B, int H, int S_cap, int D, int dtype, attn_decode_plan
     std::memset(plan, 0, sizeof(*plan));
     if (B < 0 || H < 0 || S_cap <= 0 || D <= 0)
         return fail(ATTN_ERR_INVALID_ARG, "attn_decode: sizes must be B, H >= 0 and S_cap, D >= 1");
-    if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+    if (!dtype_built(dtype))
         return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: dtype " + std::to_string(dtype) + " not built");
     if (D != 32 && D != 64 && D != 128)
         return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: head dim D=" + std::to_string(D) + " not built");
@@ -294,7 +309,7 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
     attn::DecodeArgs a{q, kcache, vcache, seqlens, o, B, H, S_cap, D,
                        (float)(1.0f / std::sqrt((float)D)) * 1.4426950408889634f, (float*)workspace, ev_start,
                        ev_stop};
-    const hipError_t e = attn::launch_decode(a, dtype == ATTN_BF16, t_stream);
+    const hipError_t e = attn::launch_decode(a, elt_of(dtype), t_stream);
     if (e != hipSuccess)
         return fail(ATTN_ERR_HIP, std::string("attn_decode: launch failed: ") + hipGetErrorString(e));
     return ok();

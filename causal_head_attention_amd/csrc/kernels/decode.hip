@@ -36,7 +36,6 @@ namespace attn {
 namespace {
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 template <typename T>
 struct Elem;
@@ -50,13 +49,27 @@ struct Elem<float> {
         return __builtin_bit_cast(float, u);
     }
 };
+// 16-bit types: elements stay packed in pairs for v_dot2 (exact products,
+// fp32 accumulation).
 template <>
 struct Elem<__bf16> {
     static constexpr int PER16 = 8;
+    typedef __bf16 v2 __attribute__((ext_vector_type(2)));
     __device__ static float get(const u32x4_t& x, int e) {
         const unsigned u = (x[e >> 1] >> (16 * (e & 1))) << 16;
         return __builtin_bit_cast(float, u);
     }
+    __device__ static float dot2(v2 a, v2 b, float c) { return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false); }
+};
+template <>
+struct Elem<_Float16> {
+    static constexpr int PER16 = 8;
+    typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+    __device__ static float get(const u32x4_t& x, int e) {
+        const unsigned short u = (unsigned short)(x[e >> 1] >> (16 * (e & 1)));
+        return (float)__builtin_bit_cast(_Float16, u);
+    }
+    __device__ static float dot2(v2 a, v2 b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
 };
 
 constexpr int kNonTemporal = 2;   // buffer-load cache policy: nt
@@ -123,7 +136,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(const T* _
                                                                       float c) {
     using C = DecCfg<T, D>;
     constexpr int E = C::E, LPH = C::LPH, HPI = C::HPI;
-    constexpr bool kBf16 = sizeof(T) == 2;
+    constexpr bool k16 = sizeof(T) == 2;   // bf16 or fp16: packed v_dot2 paths
     __shared__ long long red[kDecodeThreads / 64];
     __shared__ long long incl_s[kDecodeScanLds];   // inclusive prefix sums of the lengths
 
@@ -231,11 +244,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(const T* _
                 const bool h_ok = h < H;
                 const int lane_off = ((h_ok ? h : 0) * D + E * sub) * (int)sizeof(T);
 
-                // this row's query chunk; bf16 stays packed (exact) for v_dot2
+                // this row's query chunk; 16-bit types stay packed (exact) for v_dot2
                 // and the scale is applied to the reduced score
                 const u32x4_t qx = *(const u32x4_t*)(q + ((size_t)b * H + (h_ok ? h : 0)) * D + E * sub);
                 float qf[E];
-                if constexpr (!kBf16) {
+                if constexpr (!k16) {
 #pragma unroll
                     for (int e = 0; e < E; ++e) qf[e] = Elem<T>::get(qx, e);
                 }
@@ -257,14 +270,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(const T* _
 #pragma unroll
                     for (int it = 0; it < kDecodeBatch; ++it) {
                         float d = 0.f;
-                        if constexpr (kBf16) {
+                        if constexpr (k16) {
 #pragma unroll
                             for (int w = 0; w < 4; ++w) {
                                 // scalar copies first (bit-casting a vector-element lvalue
                                 // reads element 0 with this compiler)
                                 const unsigned kw = kr[it][w], qw = qx[w];
-                                d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kw),
-                                                                    __builtin_bit_cast(bf16x2_t, qw), d, false);
+                                d = Elem<T>::dot2(__builtin_bit_cast(typename Elem<T>::v2, kw),
+                                                  __builtin_bit_cast(typename Elem<T>::v2, qw), d);
                             }
                         } else {
 #pragma unroll
@@ -290,21 +303,21 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(const T* _
 #pragma unroll
                     for (int e = 0; e < E; ++e) acc[e] *= alpha;
                     m_run = m_new;
-                    if constexpr (kBf16) {
-                        // pairs of keys: P rounded to bf16, V pairs packed per head dim,
+                    if constexpr (k16) {
+                        // pairs of keys: P rounded to the storage type, V pairs packed per head dim,
                         // one v_dot2 per (pair, dim); the sum adds the same rounded P
 #pragma unroll
                         for (int it = 0; it < kDecodeBatch; it += 2) {
-                            const bf16x2_t pp = {(__bf16)__builtin_amdgcn_exp2f(s[it] - m_new),
-                                                 (__bf16)__builtin_amdgcn_exp2f(s[it + 1] - m_new)};
-                            const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-                            l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
+                            typedef typename Elem<T>::v2 v2;
+                            const v2 pp = {(T)__builtin_amdgcn_exp2f(s[it] - m_new),
+                                           (T)__builtin_amdgcn_exp2f(s[it + 1] - m_new)};
+                            const v2 ones = {(T)1.0f, (T)1.0f};
+                            l_run = Elem<T>::dot2(pp, ones, l_run);
 #pragma unroll
                             for (int e = 0; e < E; ++e) {
                                 const unsigned va = (vr[it][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
                                 const unsigned vb = (vr[it + 1][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                                acc[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, va | (vb << 16)), pp,
-                                                                         acc[e], false);
+                                acc[e] = Elem<T>::dot2(__builtin_bit_cast(v2, va | (vb << 16)), pp, acc[e]);
                             }
                         }
                     } else {
@@ -445,8 +458,13 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, bool dtype_is_bf16, hipStream_t stream) {
-    return dtype_is_bf16 ? launch_t<__bf16>(a, stream) : launch_t<float>(a, stream);
+hipError_t launch_decode(const DecodeArgs& a, Elt t, hipStream_t stream) {
+    switch (t) {
+        case Elt::F32: return launch_t<float>(a, stream);
+        case Elt::BF16: return launch_t<__bf16>(a, stream);
+        case Elt::F16: return launch_t<_Float16>(a, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace attn

@@ -2,7 +2,7 @@
 //
 // Serves the fp32 forward (gfx950 has no reduced-precision fp32 matrix
 // path, and fp32 inputs are held to a 1e-4 absolute bound) and, under
-// ATTN_ALGO=row, a bf16 cross-check of the tile kernel. Each iteration takes
+// ATTN_ALGO=row, a bf16 / fp16 cross-check of the tile kernel. Each iteration takes
 // 64 keys: lane j computes the score of key j0+j (one K row, 16-byte
 // loads), the wave reduces max and sum with cross-lane shuffles, and the
 // lanes switch to owning head dims to accumulate p_j * V[j0+j, :] with
@@ -14,7 +14,8 @@
 // (same page, section 2.2; shuffle reduction instead of shared memory and
 // barriers: section 4.1); online softmax with running max and sum and the
 // -inf mask ("Week-4 CUDA notes" page, section 2.2); fp32 accumulation
-// (MMHA page, section 3.3).
+// (MMHA page, section 3.3); a padded key's score set to -inf (Week-4 notes
+// page, section 2.2).
 #include <hip/hip_runtime.h>
 
 #include "../launch.h"
@@ -25,6 +26,7 @@ namespace {
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(_Float16 x) { return (float)x; }
 template <typename T>
 __device__ __forceinline__ T from_f32(float x) { return (T)x; }
 
@@ -44,7 +46,8 @@ __global__ __launch_bounds__(kRowThreads) void fwd_row_kernel(const T* __restric
                                                               const T* __restrict__ V, T* __restrict__ O,
                                                               int H, int S_q, int S_cap, int causal, float c,
                                                               const int32_t* __restrict__ kv_lens,
-                                                              float* __restrict__ lse) {
+                                                              float* __restrict__ lse,
+                                                              const uint8_t* __restrict__ key_mask) {
     constexpr int DPL = (D + 63) / 64;   // head dims per lane in the P.V phase
     __shared__ float qs[D];
     const int lane = threadIdx.x;
@@ -67,7 +70,8 @@ __global__ __launch_bounds__(kRowThreads) void fwd_row_kernel(const T* __restric
     for (int j0 = 0; j0 < n_keys; j0 += 64) {
         const int j = j0 + lane;
         float s = -INFINITY;
-        if (j < n_keys) {
+        // key j is hidden when the key-padding mask says so ([B, S_cap] bytes)
+        if (j < n_keys && (!key_mask || key_mask[(size_t)b * S_cap + j] != 0)) {
             const T* krow = K + ((size_t)((size_t)b * S_cap + j) * H + h) * D;
             float dot = 0.f;
 #pragma unroll 8
@@ -75,8 +79,10 @@ __global__ __launch_bounds__(kRowThreads) void fwd_row_kernel(const T* __restric
             s = dot * c;
         }
         const float m_new = fmaxf(m_run, wave_max(s));
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // m_new is finite: key j0 is valid
-        const float pj = __builtin_amdgcn_exp2f(s - m_new);
+        // m_new is -inf only while every key so far is hidden by the mask
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        const float pj = __builtin_amdgcn_exp2f(s - m_use);
         l_run = l_run * alpha + wave_sum(pj);
         m_run = m_new;
 #pragma unroll
@@ -110,7 +116,7 @@ hipError_t launch_row(const FwdArgs& a, hipStream_t stream) {
     const unsigned grid = (unsigned)((long long)a.B * a.H * a.S_q);
     hipExtLaunchKernelGGL((fwd_row_kernel<T, D>), dim3(grid), dim3(kRowThreads), 0, stream, a.ev_start, a.ev_stop,
                           0, (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.H, a.S_q, a.S_kv, a.causal,
-                          a.scale_log2, a.kv_lens, a.lse);
+                          a.scale_log2, a.kv_lens, a.lse, a.key_mask);
     return hipGetLastError();
 }
 
@@ -126,8 +132,13 @@ hipError_t launch_row_t(const FwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_fwd_row(const FwdArgs& a, bool dtype_is_bf16, hipStream_t stream) {
-    return dtype_is_bf16 ? launch_row_t<__bf16>(a, stream) : launch_row_t<float>(a, stream);
+hipError_t launch_fwd_row(const FwdArgs& a, Elt t, hipStream_t stream) {
+    switch (t) {
+        case Elt::F32: return launch_row_t<float>(a, stream);
+        case Elt::BF16: return launch_row_t<__bf16>(a, stream);
+        case Elt::F16: return launch_row_t<_Float16>(a, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace attn

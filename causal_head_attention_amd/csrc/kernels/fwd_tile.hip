@@ -1,4 +1,5 @@
-// fwd_tile_bf16.hip -- fused causal attention forward on gfx950 matrix cores.
+// fwd_tile.hip -- fused causal attention forward on gfx950 matrix cores
+// (bf16 or fp16 storage, fp32 arithmetic).
 //
 // One workgroup (8 waves) owns one (b, h, block of 128 queries); with the
 // causal mask it owns two blocks, r and n-1-r, run one after the other so
@@ -7,9 +8,11 @@
 //   K tile  : HBM -> registers -> LDS  (row-major, rows padded by 16 bytes)
 //   V tile  : HBM -> registers -> transposed in registers -> LDS as V^T
 //   S^T     = K . Q^T            v_mfma_f32_32x32x16_bf16, fp32 accumulate
-//   mask    : only on tiles that cross the diagonal or the ragged key end
+//   mask    : on tiles that cross the diagonal or the ragged key end, and
+//             on every tile when a key-padding mask is given
 //   softmax : online (running max, running sum) in fp32, base-2 exponent
-//   O^T    += V^T . P^T          v_mfma_f32_32x32x16_bf16, P rounded to bf16
+//   O^T    += V^T . P^T          v_mfma_f32_32x32x16_bf16 (or _f16), P rounded
+//                                to the storage type
 //
 // A block walks its KV tiles from the diagonal down to tile 0 (the online
 // softmax does not depend on the order). The workgroups of one head then
@@ -60,20 +63,38 @@
 namespace attn {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+// The 16-bit storage types and their matrix-core / dot-product forms.
+template <typename T>
+struct Mma;
+template <>
+struct Mma<__bf16> {
+    typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+    typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+    __device__ static f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static float dot2(v2 a, v2 b, float c) { return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false); }
+};
+template <>
+struct Mma<_Float16> {
+    typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+    typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+    __device__ static f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static float dot2(v2 a, v2 b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
+};
 
 __device__ __forceinline__ int swap_bits23(int x) {
     return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
 __device__ __forceinline__ unsigned half_of(u32x4_t x, int e) {
-    // bf16 element e (0..7) of a 16-byte vector
+    // 16-bit element e (0..7) of a 16-byte vector
     return (x[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
 }
 
@@ -107,8 +128,8 @@ struct TileCfg {
 // whose offset lies past the last row returns zeros and a store there is
 // dropped, so ragged tails need neither branches nor clamped addresses.
 template <int D>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const __bf16* base, int b, int h, int S, int H) {
-    const __bf16* p = base + ((size_t)b * S * H + h) * D;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, int b, int h, int S, int H) {
+    const uint16_t* p = base + ((size_t)b * S * H + h) * D;
     const int bytes = ((S - 1) * H + 1) * D * 2;
     return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, bytes, 0x00020000);
 }
@@ -126,9 +147,9 @@ __device__ __forceinline__ int tok_off(int tok, int ch, int H) {
 // The K and V rows of batch entry b are S_cap rows apart (the cache
 // capacity); only the first S valid ones are in range.
 template <int D>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const __bf16* base, int b, int h, int S_cap, int S, int H,
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int b, int h, int S_cap, int S, int H,
                                                             int tile0) {
-    const __bf16* p = base + ((size_t)b * S_cap * H + h) * D + (size_t)tile0 * H * D;
+    const uint16_t* p = base + ((size_t)b * S_cap * H + h) * D + (size_t)tile0 * H * D;
     const int bytes = ((S - 1) * H + 1) * D * 2 - tile0 * H * D * 2;
     return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, bytes > 0 ? bytes : 0, 0x00020000);
 }
@@ -195,16 +216,16 @@ __device__ __forceinline__ void store_v(const u32x4_t (&pre)[TileCfg<D>::NPRE], 
 
 // S^T (32 keys of this wave's half tile x 32 queries) = K . Q^T; `krow` is
 // this lane's K row (chunk g) in the stage.
-template <int D>
-__device__ __forceinline__ f32x16_t qk_tile(const char* krow, const bf16x8_t (&qf)[TileCfg<D>::KS]) {
+template <typename T, int D>
+__device__ __forceinline__ f32x16_t qk_tile(const char* krow, const typename Mma<T>::v8 (&qf)[TileCfg<D>::KS]) {
     using C = TileCfg<D>;
     f32x16_t s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8_t a = *(const bf16x8_t*)(krow + 32 * ks);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
+        const typename Mma<T>::v8 a = *(const typename Mma<T>::v8*)(krow + 32 * ks);
+        s = Mma<T>::mfma(a, qf[ks], s);
     }
     return s;
 }
@@ -254,16 +275,23 @@ __device__ __forceinline__ void kv_order(int x, int n, int G, int& u, int& p) {
 // final O = acc / l is the same quantity either way.
 constexpr float kLazy = 8.0f;
 
-template <int D>
-__global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    __bf16* __restrict__ O, int B, int H, int S_q, int S_cap, int causal, float c /* scale*log2e */,
-    int n_qblk, int items_per_bh, int paired, const int32_t* __restrict__ kv_lens, float* __restrict__ lse) {
+// KMASK: a key-padding mask is given (a separate instantiation, so the
+// unmasked kernel carries none of its registers or branches).
+template <typename T, int D, bool KMASK>
+__global__ __launch_bounds__(kTileThreads) void fwd_tile_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    T* __restrict__ O, int B, int H, int S_q, int S_cap, int causal, float c /* scale*log2e */,
+    int n_qblk, int items_per_bh, int paired, const int32_t* __restrict__ kv_lens, float* __restrict__ lse,
+    const uint8_t* __restrict__ key_mask) {
+    typedef typename Mma<T>::v8 v8;
+    typedef typename Mma<T>::v2 v2;
+    const v2 kOnes2 = {(T)1.0f, (T)1.0f};
     using C = TileCfg<D>;
     __shared__ __attribute__((aligned(16))) char lds[C::LDS];
-    // stages: K0 K1 V0 V1
+    // stages: K0 K1 V0 V1, then four key-mask stages (tile of step u in u % 4)
     auto kst = [&](int i) { return lds + i * C::K_BYTES; };
     auto vst = [&](int i) { return lds + 2 * C::K_BYTES + i * C::V_BYTES; };
+    auto mst = [&](int u) { return lds + tile_stage_bytes(D) + (u & 3) * kTileN; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -310,25 +338,38 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
     const int nphase = (paired && p != qb_first) ? 2 : 1;
 
     const __amdgpu_buffer_rsrc_t rq = head_rsrc<D>(Q, b, h, S_q, H);
-    const __amdgpu_buffer_rsrc_t ro = head_rsrc<D>((const __bf16*)O, b, h, S_q, H);
+    const __amdgpu_buffer_rsrc_t ro = head_rsrc<D>((const uint16_t*)O, b, h, S_q, H);
 
     // The loads that open a query block: its Q^T fragments (B operand: lane
     // holds query qi, head dims 16*ks + 8*g .. +7) and tile 0 of K and V.
     // They are issued before the previous block's merge, so their latency
     // overlaps it.
-    bf16x8_t qf[C::KS];
+    v8 qf[C::KS];
     u32x4_t pre[C::NPRE];
+    // Key-padding mask: the first kTileN K-loader threads carry one byte of
+    // it per key of the tile they stage (bytes past S_kv read as 0: hidden).
+    const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(key_mask ? key_mask + (size_t)b * S_cap : key_mask), (short)0, key_mask ? S_kv : 0, 0x00020000);
+    const bool m_loader = KMASK && tid < kTileN;
+    unsigned mpre = 0;
+    auto load_mask = [&](int tile0) {
+        if (m_loader) mpre = __builtin_amdgcn_raw_buffer_load_b8(rm, tile0 + tid, 0, 0);
+    };
+    auto store_mask = [&](int u) {
+        if (m_loader) mst(u)[tid] = (char)mpre;
+    };
     auto issue_block = [&](int qb) {
         const int qi = qb * kTileM + 32 * wq + l32;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
-            qf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
+            qf[ks] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(
                                                      rq, tok_off<D>(qi, 2 * ks + g, H), 0, 0));
         const int ntq = tiles_for_block(qb, S_q, S_kv, causal);
         const int first = (ntq - 1) * kTileN;   // tiles run backwards
         if (ntq > 0) {
             if (k_loader) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_cap, S_kv, H, first), H, tid);
             else load_v<D>(pre, tile_rsrc<D>(V, b, h, S_cap, S_kv, H, first), H, tid);
+            load_mask(first);
         }
     };
     issue_block(qb_first);
@@ -352,8 +393,10 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
         float l_run = 0.f;         // this lane's share of the running sum
 
         // Prologue: tile 0 (K and V) staged; S(0) computed while K(1) lands.
-        if (k_loader) store_k<D>(pre, kst(0), tid);
-        else {
+        if (k_loader) {
+            store_k<D>(pre, kst(0), tid);
+            store_mask(0);
+        } else {
             store_v<D>(pre, vst(0), tid);
             // the stage a first-step P.V (with P = 0) reads: finite zeros
             const u32x4_t z = {0u, 0u, 0u, 0u};
@@ -362,22 +405,28 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
         __syncthreads();
         // step u works on KV tile nt-1-u: the diagonal tile first
         auto tile_of = [&](int u) { return nt - 1 - u; };
-        if (k_loader && nt > 1) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_cap, S_kv, H, tile_of(1) * kTileN), H, tid);
+        if (k_loader && nt > 1) {
+            load_k<D>(pre, tile_rsrc<D>(K, b, h, S_cap, S_kv, H, tile_of(1) * kTileN), H, tid);
+            load_mask(tile_of(1) * kTileN);
+        }
         // unconditional: every path into the loop has then waited for the Q
         // loads, so the loop body never waits on them (or on the prefetch)
-        f32x16_t sa = qk_tile<D>(kst(0) + k_lane, qf), sb;
-        if (k_loader && nt > 1) store_k<D>(pre, kst(1), tid);
+        f32x16_t sa = qk_tile<T, D>(kst(0) + k_lane, qf), sb;
+        if (k_loader && nt > 1) {
+            store_k<D>(pre, kst(1), tid);
+            store_mask(1);
+        }
         __syncthreads();
 
         // One tile: s_c holds S(t); S(t+1) goes to s_n. P(t-1) waits in
         // pb_prev and its P.V product runs in step t, so no MFMA of a step
         // depends on that step's vector work. V(t) is loaded in step t and
         // staged at its end; P.V(t-1) reads the stage written one step ago.
-        bf16x8_t pb_prev[2];
+        v8 pb_prev[2];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) pb_prev[s2][i] = (__bf16)0.f;
+            for (int i = 0; i < 8; ++i) pb_prev[s2][i] = (T)0.f;
         // a re-base decided in step t scales the accumulator at the start of
         // step t+1, once P.V(t-1) is in and before P.V(t) is added
         bool rescale_due = false;
@@ -396,7 +445,10 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
             // the block's opening loads)
             const bool ld_k = k_loader && t + 2 < nt;
             const bool ld_v = !k_loader && t >= 1;
-            if (ld_k) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_cap, S_kv, H, tile_of(t + 2) * kTileN), H, tid);
+            if (ld_k) {
+                load_k<D>(pre, tile_rsrc<D>(K, b, h, S_cap, S_kv, H, tile_of(t + 2) * kTileN), H, tid);
+                load_mask(tile_of(t + 2) * kTileN);
+            }
             if (ld_v) load_v<D>(pre, tile_rsrc<D>(V, b, h, S_cap, S_kv, H, tile_of(t) * kTileN), H, tid);
 
             const int kbase = tile_of(t) * kTileN + 32 * half;   // first key of this wave's half tile
@@ -405,15 +457,33 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
             // first ones in this order, so no P.V is pending there); the first
             // tile it does see still needs its scores from here
             if (!work && t + 1 < nt && wave_has_rows && kbase - kTileN <= key_last && kbase - kTileN < S_kv)
-                s_n = qk_tile<D>(kst((t + 1) & 1) + k_lane, qf);
+                s_n = qk_tile<T, D>(kst((t + 1) & 1) + k_lane, qf);
             if (work) {
                 apply_rescale();
-                // (b) mask: only where the tile crosses the diagonal or the key end
-                if ((causal && kbase + 31 > q0 + off) || (kbase + 32 > S_kv)) {
+                // (b) mask: where the tile crosses the diagonal or the key end,
+                // and everywhere when keys are hidden by the key-padding mask
+                // (this lane's keys are bytes 32*half + 16*(r/8) + 8*g + r%8 of
+                // the tile's mask stage)
+                if constexpr (KMASK) {
+                    const char* mrow = mst(t) + 32 * half + 8 * g;
+                    const u32x2_t m0 = *(const u32x2_t*)mrow;
+                    const u32x2_t m1 = *(const u32x2_t*)(mrow + 16);
+                    const unsigned w4[4] = {m0[0], m0[1], m1[0], m1[1]};
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = kbase + 16 * (r >> 3) + 8 * g + (r & 7);
-                        if (key > lane_key_limit || key >= S_kv) s_c[r] = -INFINITY;
+                        const unsigned byte = (w4[r >> 2] >> (8 * (r & 3))) & 0xFFu;
+                        // branch-free: one compare chain and a select per register
+                        const bool hide = (key > lane_key_limit) | (key >= S_kv) | (byte == 0u);
+                        s_c[r] = hide ? -INFINITY : s_c[r];
+                    }
+                } else {
+                    if ((causal && kbase + 31 > q0 + off) || (kbase + 32 > S_kv)) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = kbase + 16 * (r >> 3) + 8 * g + (r & 7);
+                            if (key > lane_key_limit || key >= S_kv) s_c[r] = -INFINITY;
+                        }
                     }
                 }
                 float mx = s_c[0];
@@ -431,30 +501,30 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
                 // (d) O^T += V^T . P(t-1)^T, then S(t+1), both on the matrix
                 // cores while the vector ALUs form P(t)
                 const char* vt = vst((t + 1) & 1) + v_lane;
-                bf16x8_t va[C::DB][2];
+                v8 va[C::DB][2];
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) va[db][s2] = *(const bf16x8_t*)(vt + 32 * db * C::VROW + 32 * s2);
+                    for (int s2 = 0; s2 < 2; ++s2) va[db][s2] = *(const v8*)(vt + 32 * db * C::VROW + 32 * s2);
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db)
 #pragma unroll
                     for (int s2 = 0; s2 < 2; ++s2)
-                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][s2], pb_prev[s2], acc[db], 0, 0, 0);
-                s_n = qk_tile<D>(kst((t + 1) & 1) + k_lane, qf);
-                // P is rounded to bf16 for the P.V product; the row sum adds up
+                        acc[db] = Mma<T>::mfma(va[db][s2], pb_prev[s2], acc[db]);
+                s_n = qk_tile<T, D>(kst((t + 1) & 1) + k_lane, qf);
+                // P is rounded to the storage type for the P.V product; the row sum adds up
                 // the same rounded values, so the weights that multiply V are
                 // exactly normalised (a near one-hot row returns its V row)
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
-                        pb_prev[s2][i] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_c[8 * s2 + i], c, -m_use));
+                        pb_prev[s2][i] = (T)__builtin_amdgcn_exp2f(__builtin_fmaf(s_c[8 * s2 + i], c, -m_use));
 #pragma unroll
                     // row sum of the rounded values: one v_dot2 (x 1.0) per pair
                     for (int i = 0; i < 4; ++i) {
-                        const bf16x2_t pair = {pb_prev[s2][2 * i], pb_prev[s2][2 * i + 1]};
-                        l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, l_run, false);
+                        const v2 pair = {pb_prev[s2][2 * i], pb_prev[s2][2 * i + 1]};
+                        l_run = Mma<T>::dot2(pair, kOnes2, l_run);
                     }
                 }
                 // schedule: the V^T operand reads, the P.V MFMAs each followed by
@@ -477,7 +547,10 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
             }
             // (f) land the loaded tiles in stages whose last reader ran one
             // iteration ago
-            if (ld_k) store_k<D>(pre, kst(t & 1), tid);
+            if (ld_k) {
+                store_k<D>(pre, kst(t & 1), tid);
+                store_mask(t + 2);   // stage (t+2)%4 was last read in step t-2
+            }
             if (ld_v) store_v<D>(pre, vst(t & 1), tid);
             __syncthreads();
         };
@@ -493,8 +566,7 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
             for (int db = 0; db < C::DB; ++db)
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2)
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        *(const bf16x8_t*)(vt + 32 * db * C::VROW + 32 * s2), pb_prev[s2], acc[db], 0, 0, 0);
+                    acc[db] = Mma<T>::mfma(*(const v8*)(vt + 32 * db * C::VROW + 32 * s2), pb_prev[s2], acc[db]);
         }
         lds_barrier();   // every wave's reads of the stages are done before the merge reuses them
 
@@ -532,12 +604,12 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
             for (int db = 0; db < C::DB; ++db)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    __bf16 ob[4];
+                    T ob[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * j + e;
                         const float x1 = slot[128 + (db * 16 + r) * 64 + lane];
-                        ob[e] = (__bf16)((a0 * acc[db][r] + a1 * x1) * inv);
+                        ob[e] = (T)((a0 * acc[db][r] + a1 * x1) * inv);
                     }
                     // lane holds head dims 32*db + 8*j + 4*g .. +3 of its query;
                     // rows past S_q fall outside the descriptor and are dropped
@@ -549,23 +621,38 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_bf16_kernel(
     }
 }
 
-template <int D>
+template <typename T, int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
     const TileGrid tg = tile_grid(a.B, a.H, a.S_q, a.causal, a.kv_lens != nullptr);
-    hipExtLaunchKernelGGL(fwd_tile_bf16_kernel<D>, dim3((unsigned)tg.n_items), dim3(kTileThreads), 0, stream,
-                          a.ev_start, a.ev_stop, 0, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                          (__bf16*)a.o, a.B, a.H, a.S_q, a.S_kv, a.causal, a.scale_log2, tg.n_qblk,
-                          tg.items_per_bh, tg.paired, a.kv_lens, a.lse);
+    if (a.key_mask)
+        hipExtLaunchKernelGGL((fwd_tile_kernel<T, D, true>), dim3((unsigned)tg.n_items), dim3(kTileThreads), 0,
+                              stream, a.ev_start, a.ev_stop, 0, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                              (const uint16_t*)a.v, (T*)a.o, a.B, a.H, a.S_q, a.S_kv, a.causal, a.scale_log2,
+                              tg.n_qblk, tg.items_per_bh, tg.paired, a.kv_lens, a.lse, a.key_mask);
+    else
+        hipExtLaunchKernelGGL((fwd_tile_kernel<T, D, false>), dim3((unsigned)tg.n_items), dim3(kTileThreads), 0,
+                              stream, a.ev_start, a.ev_stop, 0, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                              (const uint16_t*)a.v, (T*)a.o, a.B, a.H, a.S_q, a.S_kv, a.causal, a.scale_log2,
+                              tg.n_qblk, tg.items_per_bh, tg.paired, a.kv_lens, a.lse, nullptr);
     return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
+    switch (a.D) {
+        case 32: return launch_d<T, 32>(a, stream);
+        case 64: return launch_d<T, 64>(a, stream);
+        case 128: return launch_d<T, 128>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
-hipError_t launch_fwd_tile_bf16(const FwdArgs& a, hipStream_t stream) {
-    switch (a.D) {
-        case 32: return launch_d<32>(a, stream);
-        case 64: return launch_d<64>(a, stream);
-        case 128: return launch_d<128>(a, stream);
+hipError_t launch_fwd_tile(const FwdArgs& a, Elt t, hipStream_t stream) {
+    switch (t) {
+        case Elt::BF16: return launch_t<__bf16>(a, stream);
+        case Elt::F16: return launch_t<_Float16>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -24,7 +24,13 @@ struct FwdArgs {
     // nullptr means all S_kv rows are valid.
     const int32_t* kv_lens;
     float* lse;   // optional [B, H, S_q] natural-log sum of exp(scaled scores)
+    // optional device uint8 [B, S_kv]: 0 hides key j of entry b from all
+    // its queries (key padding); nullptr means no key is hidden
+    const uint8_t* key_mask;
 };
+
+// Storage type of q, k, v and o (arithmetic is fp32 throughout).
+enum class Elt { F32, BF16, F16 };
 
 struct DecodeArgs {
     const void* q;
@@ -39,11 +45,11 @@ struct DecodeArgs {
     hipEvent_t ev_stop;    // optional: recorded when the combine kernel ends
 };
 
-// MFMA bf16 tile kernel; D in {32, 64, 128}.
-hipError_t launch_fwd_tile_bf16(const FwdArgs& a, hipStream_t stream);
-// Row kernel: one wave per query row; dtype_is_bf16 selects the storage type.
-hipError_t launch_fwd_row(const FwdArgs& a, bool dtype_is_bf16, hipStream_t stream);
-// Split-KV decode (split + combine kernels).
-hipError_t launch_decode(const DecodeArgs& a, bool dtype_is_bf16, hipStream_t stream);
+// MFMA tile kernel for 16-bit storage (BF16 or F16); D in {32, 64, 128}.
+hipError_t launch_fwd_tile(const FwdArgs& a, Elt t, hipStream_t stream);
+// Row kernel: one wave per query row, any storage type.
+hipError_t launch_fwd_row(const FwdArgs& a, Elt t, hipStream_t stream);
+// Split-KV decode (split + combine kernels), any storage type.
+hipError_t launch_decode(const DecodeArgs& a, Elt t, hipStream_t stream);
 
 }  // namespace attn

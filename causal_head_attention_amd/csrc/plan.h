@@ -44,15 +44,20 @@ ATTN_HD inline int xcd_remap(int x, int n) {
     return tall * per + (xcd - tall) * (per - 1) + local;
 }
 
+// Key-mask stages of the tile kernel: four tiles of kTileN bytes.
+constexpr int kMaskStageBytes = 4 * kTileN;
+
 // LDS bytes of the tile kernel for head dim D: two stages of (K tile with
 // rows padded to 2*D+16 bytes, V^T tile with rows of 2*kTileN+16 bytes), or
 // the end-of-block exchange of the partial softmax states of four waves
-// (64 lanes x (2 + D/2) floats each), whichever is larger.
-ATTN_HD constexpr int tile_lds_bytes(int D) {
+// (64 lanes x (2 + D/2) floats each), whichever is larger; then the
+// key-mask stages.
+ATTN_HD constexpr int tile_stage_bytes(int D) {
     return (2 * (kTileN * (2 * D + 16) + D * (2 * kTileN + 16))) > (4 * 64 * (2 + D / 2) * 4)
                ? (2 * (kTileN * (2 * D + 16) + D * (2 * kTileN + 16)))
                : (4 * 64 * (2 + D / 2) * 4);
 }
+ATTN_HD constexpr int tile_lds_bytes(int D) { return tile_stage_bytes(D) + kMaskStageBytes; }
 
 // Number of KV tiles query block qb must visit.
 ATTN_HD inline int tiles_for_block(int qb, int S_q, int S_kv, int causal) {

@@ -48,7 +48,10 @@
 extern "C" {
 #endif
 
-/* Element types. ATTN_F16 is reserved and currently returns ATTN_ERR_UNSUPPORTED. */
+/* Element types of q, k, v and o (and the caches). Arithmetic is fp32 in
+ * every case; with ATTN_BF16 and ATTN_F16 the probabilities enter the P.V
+ * product rounded to the same 16-bit type. ATTN_F16 is the half-precision
+ * storage of the MMHA page, section 3.3. */
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_F16 = 2 } attn_dtype_t;
 
 typedef enum {
@@ -66,7 +69,7 @@ typedef enum {
  * page, section 2.2 (online softmax).
  *
  *   q : [B, S_q,  H, D]   k, v : [B, S_kv, H, D]   o : [B, S_q, H, D]
- *   All four have element type `dtype` (ATTN_F32 or ATTN_BF16).
+ *   All four have element type `dtype` (ATTN_F32, ATTN_BF16 or ATTN_F16).
  *   D must be 32, 64 or 128 (else ATTN_ERR_UNSUPPORTED).
  *   causal: 1 applies the mask above (requires S_q <= S_kv), 0 lets every
  *   query see all S_kv keys. Any other value is ATTN_ERR_INVALID_ARG.
@@ -101,7 +104,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H,
  *                 a log-sum-exp of -inf. Rows at or past len_b are never read.
  *   lse         : DEVICE float [B, H, S_q] or NULL: ln(sum_j exp(q.k_j/sqrt(D)))
  *                 over the keys the query sees.
- *   dtype, D    : as attn_fwd (ATTN_F32 or ATTN_BF16; D in {32, 64, 128}).
+ *   dtype, D    : as attn_fwd (ATTN_F32, ATTN_BF16 or ATTN_F16; D in {32, 64, 128}).
  *   B, H or S_q equal to 0 is a valid empty call; S_cap must then be >= 0,
  *   otherwise >= 1. o may not overlap any other argument, nor lse any input.
  * With seqlens_kv = NULL and S_q <= S_cap this is attn_fwd (S_kv = S_cap)
@@ -109,6 +112,26 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H,
  */
 int attn_fwd_kvcache(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens_kv,
                      void* o, float* lse, int B, int H, int S_q, int S_cap, int D, int causal, int dtype);
+
+/*
+ * attn_fwd_mask -- attn_fwd with a key-padding mask, optionally returning
+ * the log-sum-exp of each query row. A hidden key's score is -inf, so its
+ * weight is exactly 0 ("Week-4 CUDA notes" page, section 2.2, for padded
+ * positions); the mask combines with the causal rule of attn_fwd.
+ *
+ *   q, k, v, o, B, H, S_q, S_kv, D, causal, dtype : as attn_fwd
+ *   key_mask : DEVICE uint8 [B, S_kv] or NULL; key_mask[b*S_kv + j] == 0
+ *              hides key j of entry b from every query of that entry (any
+ *              other value: visible). NULL hides nothing. No alignment is
+ *              required.
+ *   lse      : DEVICE float [B, H, S_q] or NULL, as attn_fwd_kvcache.
+ * A query row left with no visible key gets an all-zero output row and a
+ * log-sum-exp of -inf. Hidden keys' K and V rows are read and their values
+ * enter P.V with weight 0, so they must hold finite numbers. o may not
+ * overlap any other argument, nor lse any input.
+ */
+int attn_fwd_mask(const void* q, const void* k, const void* v, const uint8_t* key_mask, void* o,
+                  float* lse, int B, int H, int S_q, int S_kv, int D, int causal, int dtype);
 
 /*
  * attn_decode_workspace_bytes -- device workspace attn_decode needs for
@@ -140,7 +163,7 @@ size_t attn_decode_workspace_bytes(int B, int H, int S_cap, int D);
  *                     16-byte aligned; contents on entry are ignored and on
  *                     return are unspecified. Calls that share a workspace
  *                     must be ordered on one stream.
- *   dtype           : ATTN_F32 or ATTN_BF16 for q, caches and o.
+ *   dtype           : ATTN_F32, ATTN_BF16 or ATTN_F16 for q, caches and o.
  *   D must be 32, 64 or 128. B == 0 or H == 0 is a valid empty call;
  *   S_cap must be >= 1. o may not overlap any other argument.
  * A too-small or NULL workspace returns ATTN_ERR_WORKSPACE.

@@ -3,8 +3,13 @@
 Bars (written here, applied per output tensor):
   fp32 storage : max |gpu - oracle| <= 1e-4
   bf16 storage : max |gpu - oracle| <= 2e-2  AND  ||gpu - oracle||_2 / ||oracle||_2 <= 1e-2
-The oracle receives exactly the values the GPU receives (bf16 widened to
-fp64), so input rounding is not counted as error.
+  fp16 storage : max |gpu - oracle| <= 5e-3  AND  ||gpu - oracle||_2 / ||oracle||_2 <= 3e-3
+The fp16 bar follows from the arithmetic: the output is rounded to fp16
+(half an ulp is at most 2^-9 ~ 2e-3 for |O| < 8) and the probabilities
+enter P.V rounded to fp16 (relative 2^-11, at most ~2e-3 on a convex
+combination of |V| <= 4), everything else is fp32.
+The oracle receives exactly the values the GPU receives (16-bit values
+widened to fp64), so input rounding is not counted as error.
 """
 import math
 import os
@@ -22,6 +27,10 @@ pytestmark = pytest.mark.gpu
 FP32_ATOL = 1e-4
 BF16_ATOL = 2e-2
 BF16_RELL2 = 1e-2
+FP16_ATOL = 5e-3
+FP16_RELL2 = 3e-3
+ALL_DTYPES = [torch.bfloat16, torch.float16, torch.float32]
+DTYPE_IDS = ["bf16", "fp16", "fp32"]
 
 
 def say(msg):
@@ -46,8 +55,9 @@ def check(got: torch.Tensor, ref: np.ndarray, dtype: torch.dtype, what: str = ""
         return max_abs, None
     den = float(np.linalg.norm(ref))
     rel = float(np.linalg.norm(g - ref) / den) if den > 0 else float(np.linalg.norm(g - ref))
-    assert max_abs <= BF16_ATOL, f"{what}: max abs err {max_abs:.3e} > {BF16_ATOL}"
-    assert rel <= BF16_RELL2, f"{what}: rel L2 err {rel:.3e} > {BF16_RELL2}"
+    atol, rell2 = (FP16_ATOL, FP16_RELL2) if dtype == torch.float16 else (BF16_ATOL, BF16_RELL2)
+    assert max_abs <= atol, f"{what}: max abs err {max_abs:.3e} > {atol}"
+    assert rel <= rell2, f"{what}: rel L2 err {rel:.3e} > {rell2}"
     return max_abs, rel
 
 
@@ -100,7 +110,7 @@ EDGE = [
 ]
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("dtype", ALL_DTYPES, ids=DTYPE_IDS)
 @pytest.mark.parametrize("shape", EDGE, ids=lambda s: "x".join(map(str, s)))
 def test_edge_shapes(attn, shape, dtype):
     B, H, S_q, S_kv, D, causal = shape
@@ -113,26 +123,29 @@ def test_edge_shapes(attn, shape, dtype):
 
 @pytest.mark.parametrize("shape", [(1, 2, 300, 300, 128, True), (2, 1, 130, 200, 64, True),
                                    (1, 1, 77, 77, 32, False)], ids=lambda s: "x".join(map(str, s)))
-def test_bf16_row_kernel_cross_check(attn, shape, monkeypatch):
-    """ATTN_ALGO=row runs the per-query kernel on bf16: both kernels meet the bar."""
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
+def test_16bit_row_kernel_cross_check(attn, shape, dtype, monkeypatch):
+    """ATTN_ALGO=row runs the per-query kernel on 16-bit storage: both kernels meet the bar."""
     B, H, S_q, S_kv, D, causal = shape
-    q, k, v = workloads.make_prefill_shape(9, torch.bfloat16, B, H, S_q, S_kv, D)
+    q, k, v = workloads.make_prefill_shape(9, dtype, B, H, S_q, S_kv, D)
     ref = oracle.attn_fwd(q, k, v, causal)
     qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    code = attn.ATTN_BF16 if dtype == torch.bfloat16 else attn.ATTN_F16
     monkeypatch.setenv("ATTN_ALGO", "row")
-    assert attn.attn_fwd_plan(B, H, S_q, S_kv, D, causal, attn.ATTN_BF16).kernel == 2
+    assert attn.attn_fwd_plan(B, H, S_q, S_kv, D, causal, code).kernel == 2
     o_row = attn.attn_fwd(qc, kc, vc, causal=causal)
     monkeypatch.setenv("ATTN_ALGO", "tile")
+    assert attn.attn_fwd_plan(B, H, S_q, S_kv, D, causal, code).kernel == 1
     o_tile = attn.attn_fwd(qc, kc, vc, causal=causal)
     torch.cuda.synchronize()
-    check(o_row, ref, torch.bfloat16, "row")
-    check(o_tile, ref, torch.bfloat16, "tile")
+    check(o_row, ref, dtype, "row")
+    check(o_tile, ref, dtype, "tile")
 
 
 # ---------------------------------------------------------------------------
 # Invariants the definition fixes exactly
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("dtype", ALL_DTYPES, ids=DTYPE_IDS)
 @pytest.mark.parametrize("D", [32, 64, 128])
 def test_identity_values_expose_probabilities(attn, dtype, D):
     """V = I (S_kv = D) makes O = P: masked entries exactly 0, rows sum to 1."""
@@ -146,12 +159,12 @@ def test_identity_values_expose_probabilities(attn, dtype, D):
     j = torch.arange(D)[None, :]
     masked = (j > i).expand(2, S, D).permute(1, 0, 2)[None]
     assert torch.all(o[masked] == 0.0)
-    tol = 1e-4 if dtype == torch.float32 else 2e-2
+    tol = {torch.float32: 1e-4, torch.float16: 2e-3, torch.bfloat16: 2e-2}[dtype]
     assert torch.max(torch.abs(o.sum(-1) - 1.0)) <= tol
     check(o.to(dtype).cuda(), oracle.attn_fwd(q, k, v, True), dtype, "V=I")
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("dtype", ALL_DTYPES, ids=DTYPE_IDS)
 def test_row_zero_is_value_row_zero_bitwise(attn, dtype):
     q, k, v = workloads.make_prefill_shape(11, dtype, 2, 4, 300, 300, 128, qk_std=4.0)
     o = attn.attn_fwd(q.cuda(), k.cuda(), v.cuda(), causal=True).cpu()
@@ -193,7 +206,7 @@ def test_guard_bands_untouched(attn):
 # ---------------------------------------------------------------------------
 # Decode edge cases
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("dtype", ALL_DTYPES, ids=DTYPE_IDS)
 @pytest.mark.parametrize("D", [64, 128, 32])
 def test_decode_lengths(attn, dtype, D):
     S_cap = 600
@@ -228,7 +241,7 @@ DECODE_SEGMENTS = [
 ]
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("dtype", ALL_DTYPES, ids=DTYPE_IDS)
 @pytest.mark.parametrize("case", DECODE_SEGMENTS, ids=lambda c: f"B{c[1]}_S{c[3]}")
 def test_decode_balanced_segments(attn, case, dtype):
     seed, B, H, S_cap, D, (lo, hi) = case
@@ -273,9 +286,10 @@ def test_decode_matches_forward_with_one_query(attn):
 # LSE bars: the kernels add up the probabilities as rounded for P.V, so in
 # bf16 the row sum carries a relative error up to 2^-9 and the log of it an
 # absolute error up to about 2e-3 (plus fp32 rounding of the scores): bar
-# 4e-3. fp32 inputs go through the row kernel (fp32 throughout): bar 1e-5.
+# 4e-3; in fp16 the relative error is up to 2^-11, the log error about 5e-4:
+# bar 1e-3. fp32 inputs go through the row kernel (fp32 throughout): bar 1e-5.
 # ---------------------------------------------------------------------------
-LSE_ATOL = {torch.bfloat16: 4e-3, torch.float32: 1e-5}
+LSE_ATOL = {torch.bfloat16: 4e-3, torch.float16: 1e-3, torch.float32: 1e-5}
 
 
 def check_lse(got: torch.Tensor, ref: np.ndarray, dtype: torch.dtype, what: str = ""):
@@ -311,7 +325,7 @@ KV_EDGE = [  # (B, H, S_q, S_cap, D, causal, lengths)
 ]
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("dtype", ALL_DTYPES, ids=DTYPE_IDS)
 @pytest.mark.parametrize("case", KV_EDGE, ids=lambda c: "x".join(map(str, c[:6])))
 def test_kvcache_edge_cases(attn, case, dtype):
     B, H, S_q, S_cap, D, causal, lens = case
@@ -327,7 +341,7 @@ def test_kvcache_edge_cases(attn, case, dtype):
     assert torch.all(o.cpu()[torch.from_numpy(empty)] == 0)
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("dtype", ALL_DTYPES, ids=DTYPE_IDS)
 def test_kvcache_without_lengths_is_attn_fwd_bitwise(attn, dtype):
     q, k, v = workloads.make_prefill_shape(500, dtype, 2, 4, 200, 333, 128)
     q, k, v = q.cuda(), k.cuda(), v.cuda()
@@ -338,6 +352,87 @@ def test_kvcache_without_lengths_is_attn_fwd_bitwise(attn, dtype):
         assert torch.equal(o1, o2) and torch.equal(o1, o3)
         _, rlse = oracle.attn_fwd_kvcache(q.cpu(), k.cpu(), v.cpu(), None, causal=causal)
         check_lse(lse, rlse, dtype, f"lse causal={causal}")
+
+
+# ---------------------------------------------------------------------------
+# Key-padding mask (attn_fwd_mask) and its log-sum-exp
+# ---------------------------------------------------------------------------
+MASK_CASES = [  # (B, H, S_q, S_kv, D, causal, pattern)
+    (3, 2, 200, 200, 128, True, "random"),
+    (2, 3, 129, 300, 64, True, "right_pad"),      # padded tail of each entry
+    (2, 2, 65, 130, 32, False, "left_pad"),       # padded head of each entry
+    (4, 2, 77, 77, 128, True, "edge_entries"),    # an entry fully hidden, one with only its last key
+    (1, 4, 1000, 1000, 128, True, "random"),
+    (2, 1, 33, 513, 128, False, "random"),
+]
+
+
+def _make_mask(pattern, B, S_kv, seed):
+    g = torch.Generator().manual_seed(seed)
+    if pattern == "random":
+        m = torch.rand(B, S_kv, generator=g) < 0.6
+    elif pattern == "right_pad":
+        n = torch.randint(1, S_kv + 1, (B,), generator=g)
+        m = torch.arange(S_kv)[None, :] < n[:, None]
+    elif pattern == "left_pad":
+        n = torch.randint(0, S_kv, (B,), generator=g)
+        m = torch.arange(S_kv)[None, :] >= n[:, None]
+    else:
+        m = torch.rand(B, S_kv, generator=g) < 0.5
+        m[0] = False
+        m[1] = False
+        m[1, -1] = True
+    return m
+
+
+@pytest.mark.parametrize("dtype", ALL_DTYPES, ids=DTYPE_IDS)
+@pytest.mark.parametrize("case", MASK_CASES, ids=lambda c: "x".join(map(str, c[:6])) + "_" + c[6])
+def test_key_mask_against_oracle(attn, case, dtype):
+    B, H, S_q, S_kv, D, causal, pattern = case
+    say(f"key mask {case} {dtype}")
+    q, k, v = workloads.make_prefill_shape(600 + D, dtype, B, H, S_q, S_kv, D)
+    m = _make_mask(pattern, B, S_kv, 700 + S_kv)
+    o, lse = attn.attn_fwd_mask(q.cuda(), k.cuda(), v.cuda(), m.cuda(), causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rlse = oracle.attn_fwd_mask(q, k, v, m.numpy(), causal)
+    check(o, ro, dtype, f"mask {case}")
+    check_lse(lse, rlse, dtype, f"mask {case}")
+    empty = np.isneginf(rlse).all(axis=1)          # B, S_q: rows with no visible key
+    assert torch.all(o.cpu()[torch.from_numpy(empty)] == 0)
+
+
+@pytest.mark.parametrize("dtype", ALL_DTYPES, ids=DTYPE_IDS)
+def test_key_mask_absent_or_all_visible_is_attn_fwd_bitwise(attn, dtype):
+    q, k, v = (t.cuda() for t in workloads.make_prefill_shape(610, dtype, 2, 3, 300, 300, 128))
+    for causal in (True, False):
+        ref = attn.attn_fwd(q, k, v, causal=causal)
+        o1 = attn.attn_fwd_mask(q, k, v, None, causal=causal)
+        o2 = attn.attn_fwd_mask(q, k, v, torch.ones(2, 300, dtype=torch.bool, device="cuda"), causal=causal)
+        assert torch.equal(o1, ref) and torch.equal(o2, ref)
+
+
+def test_key_mask_row_kernel_cross_check(attn, monkeypatch):
+    B, H, S, D = 2, 2, 150, 64
+    q, k, v = workloads.make_prefill_shape(620, torch.bfloat16, B, H, S, S, D)
+    m = _make_mask("random", B, S, 621)
+    ro, _ = oracle.attn_fwd_mask(q, k, v, m.numpy(), True)
+    monkeypatch.setenv("ATTN_ALGO", "row")
+    o_row = attn.attn_fwd_mask(q.cuda(), k.cuda(), v.cuda(), m.cuda(), causal=True)
+    monkeypatch.setenv("ATTN_ALGO", "tile")
+    o_tile = attn.attn_fwd_mask(q.cuda(), k.cuda(), v.cuda(), m.cuda(), causal=True)
+    torch.cuda.synchronize()
+    check(o_row, ro, torch.bfloat16, "mask row kernel")
+    check(o_tile, ro, torch.bfloat16, "mask tile kernel")
+
+
+def test_fp16_prefill_full_size(attn):
+    """The bf16_s2048 shape (B=1, H=32, S=2048, D=128, causal) in fp16."""
+    q, k, v = workloads.make_prefill_shape(1003, torch.float16, 1, 32, 2048, 2048, 128)
+    say("fp16 prefill B=1 H=32 S=2048 D=128")
+    o = attn.attn_fwd(q.cuda(), k.cuda(), v.cuda(), causal=True)
+    torch.cuda.synchronize()
+    max_abs, rel = check(o, oracle.attn_fwd(q, k, v, True), torch.float16, "fp16 s2048")
+    say(f"  fp16 s2048: max abs {max_abs:.3e} rel L2 {rel:.3e}")
 
 
 # ---------------------------------------------------------------------------
