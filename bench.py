@@ -158,8 +158,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="also time 20 back-to-back calls without the flush")
-    ap.add_argument("--skip-kvcache", action="store_true",
-                    help="leave out the KV-cache prefill measurement")
+    ap.add_argument("--skip-extras", action="store_true",
+                    help="leave out the KV-cache, fp16 and key-padding prefill measurements")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one device copy of MIB MiB (reference for HBM counters)")
     args = ap.parse_args()
@@ -246,8 +246,33 @@ def main() -> int:
     # KV-cache prefill (chunk of 512 queries per sequence against caches of
     # per-sequence length): the same tile kernel behind attn_fwd_kvcache,
     # timed cold like the step, outside the step's headline figure
-    kv = None
-    if not args.skip_kvcache:
+    def cold_ms(call, n=20):
+        """Device time of `call` (events on its kernels), 512 MiB fill before each."""
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(n):
+            e = hev.create(2)
+            flush.zero_()
+            attn.attn_set_timing_events(e[0], e[1])
+            call()
+            torch.cuda.synchronize()
+            out.append(hev.ms(e[0], e[1]))
+            hev.destroy(e)
+        return out
+
+    def mfma_leg(ms, flop, workload):
+        mean = statistics.fmean(ms)
+        tf = flop / (mean * 1e-3) / 1e12
+        return {"value": round(tf, 2), "unit": "TFLOPS", "workload": workload,
+                "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                             "flop_per_launch": flop, "mean_launch_us": round(mean * 1e3, 2),
+                             "median_launch_us": round(statistics.median(ms) * 1e3, 2)}}
+
+    kv = f16 = kp = None
+    if not args.skip_extras:
         kc_cfg = workloads.BF16_KVCACHE
         log("KV-cache prefill: generating inputs")
         sl_kv_h, q_kv_h, kc_kv_h, vc_kv_h = workloads.make_kvcache_prefill(kc_cfg)
@@ -259,29 +284,35 @@ def main() -> int:
         def kv_call():
             attn.attn_fwd_kvcache(q_kv, kc_kv, vc_kv, sl_kv, o_kv, causal=True)
 
-        for _ in range(3):
-            kv_call()
-        torch.cuda.synchronize()
-        kv_ms = []
-        for _ in range(20):
-            e = hev.create(2)
-            flush.zero_()
-            attn.attn_set_timing_events(e[0], e[1])
-            kv_call()
-            torch.cuda.synchronize()
-            kv_ms.append(hev.ms(e[0], e[1]))
-            hev.destroy(e)
-        kv_mean = statistics.fmean(kv_ms)
-        kv_tf = kv_flops / (kv_mean * 1e-3) / 1e12
-        kv = {"value": round(kv_tf, 2), "unit": "TFLOPS",
-              "workload": f"bf16 causal chunk of {kc_cfg.S_q} queries x {kc_cfg.B} sequences, H={kc_cfg.H} "
-                          f"D={kc_cfg.D}, cache capacity {kc_cfg.S_cap}, lengths {sl_kv_h.tolist()} (seed "
-                          f"{kc_cfg.seed}); cold, 20 calls",
-              "roofline": {"bound": "mfma", "achieved": round(kv_tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
-                           "unit": "TFLOP/s", "frac": round(kv_tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                           "flop_per_launch": kv_flops, "mean_launch_us": round(kv_mean * 1e3, 2),
-                           "median_launch_us": round(statistics.median(kv_ms) * 1e3, 2)}}
+        kv = mfma_leg(cold_ms(kv_call), kv_flops,
+                      f"bf16 causal chunk of {kc_cfg.S_q} queries x {kc_cfg.B} sequences, H={kc_cfg.H} "
+                      f"D={kc_cfg.D}, cache capacity {kc_cfg.S_cap}, lengths {sl_kv_h.tolist()} (seed "
+                      f"{kc_cfg.seed}); cold, 20 calls")
         del kc_kv, vc_kv
+
+        # the bf16_s2048 shape with fp16 storage (v_mfma_f32_32x32x16_f16;
+        # the dense fp16 peak equals the bf16 one)
+        fc = workloads.FP16_S2048
+        log("fp16 prefill")
+        q16, k16, v16 = (t.to(dev) for t in workloads.make_prefill(fc))
+        o16 = torch.empty_like(q16)
+        f16 = mfma_leg(cold_ms(lambda: attn.attn_fwd(q16, k16, v16, o16, causal=True)), fc.flops(),
+                       f"fp16 causal prefill B={fc.B} H={fc.H} S={fc.S_q} D={fc.D} (seed {fc.seed}); "
+                       f"cold, 20 calls")
+        del q16, k16, v16, o16
+
+        # key-padding forward: right-padded entries, no causal rule; FLOP over
+        # the visible (query, key) pairs only
+        pc_k = workloads.BF16_KEYPAD
+        log("key-padding prefill")
+        lens_k, mask_k, qk_h, kk_h, vk_h = workloads.make_keypad_prefill(pc_k)
+        qk, kk, vk, mk = (t.to(dev) for t in (qk_h, kk_h, vk_h, mask_k))
+        ok = torch.empty_like(qk)
+        kp = mfma_leg(cold_ms(lambda: attn.attn_fwd_mask(qk, kk, vk, mk, ok, causal=False)),
+                      pc_k.flops(lens_k.tolist()),
+                      f"bf16 key-padding forward B={pc_k.B} H={pc_k.H} S={pc_k.S} D={pc_k.D}, no causal rule, "
+                      f"key lengths {lens_k.tolist()} (seed {pc_k.seed}); cold, 20 calls")
+        del qk, kk, vk, mk, ok
 
     if args.copy_calibration:
         n = args.copy_calibration << 20
@@ -362,6 +393,8 @@ def main() -> int:
                   "kernels, no queueing gaps); 512 MiB fill before every call",
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         "kvcache_prefill": kv,
+        "fp16_prefill": f16,
+        "keypad_prefill": kp,
         "cpu_baseline": cpu,
         "parity": parity,
     }

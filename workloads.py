@@ -23,11 +23,16 @@ The five workloads:
                     of 512 new queries each, H=32, D=128, cache capacity 4096,
                     lengths (cached tokens including the chunk) uniform in
                     [512, 4096], causal
+* ``fp16_s2048``    the bf16_s2048 shape in fp16 (the pages' half-precision
+                    storage), N(0,1)
+* ``bf16_keypad``   bf16 key-padding forward: B=8 sequences padded to S=1024,
+                    H=32, D=128, no causal rule, key j of entry b visible iff
+                    j < len_b with len_b uniform in [256, 1024] (right padding)
 
-Generator: a torch CPU ``Generator`` seeded with ``1000 + index`` (1001..1006).
-Prefill draws q, k, v in that order as ``randn(B,S,H,D) * std``; decode and
-the KV-cache prefill draw the lengths first, then q, the K cache and the V
-cache. bf16 tensors are the
+Generator: a torch CPU ``Generator`` seeded with ``1000 + index`` (1001..1008).
+Prefill draws q, k, v in that order as ``randn(B,S,H,D) * std``; decode,
+the KV-cache prefill and the key-padding forward draw the lengths first,
+then q, K and V. bf16 tensors are the
 round-to-nearest-even cast of the fp32 draw (``Tensor.to(torch.bfloat16)``).
 """
 from __future__ import annotations
@@ -119,6 +124,28 @@ BF16_S4096 = Prefill("bf16_s4096", torch.bfloat16, 1, 32, 4096, 4096, 128, True,
                      qk_std=4.0, v_std=1.0)
 BF16_DECODE = Decode("bf16_decode", torch.bfloat16, 16, 32, 4096, 128, 1005)
 BF16_KVCACHE = KVCachePrefill("bf16_kvcache", torch.bfloat16, 8, 32, 512, 4096, 128, 1006, 512, 4096)
+FP16_S2048 = Prefill("fp16_s2048", torch.float16, 1, 32, 2048, 2048, 128, True, 1007)
+
+
+@dataclass(frozen=True)
+class KeyPadPrefill:
+    name: str
+    dtype: torch.dtype
+    B: int
+    H: int
+    S: int
+    D: int
+    seed: int
+    len_lo: int
+    len_hi: int
+
+    def flops(self, lens) -> int:
+        """Algorithmic FLOP: 4*H*D per visible pair; every one of the S queries of
+        entry b sees its len_b unpadded keys."""
+        return 4 * self.H * self.D * self.S * sum(max(0, min(int(n), self.S)) for n in lens)
+
+
+BF16_KEYPAD = KeyPadPrefill("bf16_keypad", torch.bfloat16, 8, 32, 1024, 128, 1008, 256, 1024)
 
 PREFILL_CONFIGS = (FP32_TINY, FP32_SMALL, BF16_S2048, BF16_S4096)
 
@@ -179,6 +206,18 @@ def decode_kv_bytes(seqlens, H: int, D: int, elem_bytes: int, S_cap: int) -> int
         total += max(0, min(int(n), S_cap))
     B = len(seqlens)
     return total * H * D * 2 * elem_bytes + 2 * B * H * D * elem_bytes
+
+
+def make_keypad_prefill(cfg: KeyPadPrefill):
+    """Draw (lens, key_mask, q, k, v) on the CPU: right-padded entries, key j of
+    entry b visible iff j < lens[b] (key_mask is bool [B, S])."""
+    g = torch.Generator().manual_seed(cfg.seed)
+    lens = torch.randint(cfg.len_lo, cfg.len_hi + 1, (cfg.B,), generator=g, dtype=torch.int32)
+    q = torch.randn(cfg.B, cfg.S, cfg.H, cfg.D, generator=g).to(cfg.dtype)
+    k = torch.randn(cfg.B, cfg.S, cfg.H, cfg.D, generator=g).to(cfg.dtype)
+    v = torch.randn(cfg.B, cfg.S, cfg.H, cfg.D, generator=g).to(cfg.dtype)
+    mask = torch.arange(cfg.S)[None, :] < lens[:, None]
+    return lens, mask, q.contiguous(), k.contiguous(), v.contiguous()
 
 
 def make_kvcache_prefill(cfg: KVCachePrefill, nan_fill: bool = False, seqlens=None, S_cap: int | None = None,
