@@ -106,7 +106,7 @@ struct DecCfg {
 };
 
 // Sum over the workgroup; every thread gets it. `red` holds one slot per wave.
-template <int NT>
+template <int NT = kDecodeThreads>
 __device__ __forceinline__ long long block_sum(long long x, long long* red) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -358,24 +358,29 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const f
                                                                          int G) {
     constexpr int NP = kCombineThreads / D;       // parts
     constexpr int PER = 16;                       // segments in flight per thread per round
-    __shared__ long long red[kCombineThreads / 64];
     __shared__ float part_m[NP], part_l[NP];
     __shared__ float part_acc[NP][D];
     const int bh = blockIdx.x;
     const int b = bh / H, h = bh % H;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     T* out = o + (size_t)bh * D;   // [B, 1, H, D]: the (b, h) row is bh
-    // token-space geometry: total, start of sequence b, its length
+    // token-space geometry (total, start of sequence b, its length): every
+    // wave sums the lengths itself, so no barrier precedes the record loads
     long long all = 0, before = 0, mine = 0;
-    for (int bb = tid; bb < B; bb += kCombineThreads) {
+    for (int bb = lane; bb < B; bb += 64) {
         const long long l = clamp_len(seqlens[bb], S_cap);
         all += l;
         if (bb < b) before += l;
         if (bb == b) mine = l;
     }
-    const long long Ttot = block_sum<kCombineThreads>(all, red);
-    const long long Pb = block_sum<kCombineThreads>(before, red);
-    const int len = (int)block_sum<kCombineThreads>(mine, red);
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) {
+        all += __shfl_xor(all, x);
+        before += __shfl_xor(before, x);
+        mine += __shfl_xor(mine, x);
+    }
+    const long long Ttot = all, Pb = before;
+    const int len = (int)mine;
     if (len == 0) {   // uniform; a sequence with no keys gives a zero row
         for (int d = tid; d < D; d += kCombineThreads) out[d] = (T)0.f;
         return;

@@ -306,7 +306,12 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_kernel(
     const int v_lane = l32 * C::VROW + 16 * (4 * half + g);
 
     int bh, p;
-    if (!kv_lens) {
+    if (KMASK && !kv_lens) {
+        // key padding: entries differ in the tiles they visit; kv_order spreads
+        // the heads of every entry over all XCDs, so no XCD is left with the
+        // longest entry alone
+        kv_order(blockIdx.x, gridDim.x, items_per_bh, bh, p);
+    } else if (!kv_lens) {
         const int item = xcd_remap(blockIdx.x, gridDim.x);
         bh = item / items_per_bh;
         p = item % items_per_bh;
@@ -358,15 +363,57 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_kernel(
     auto store_mask = [&](int u) {
         if (m_loader) mst(u)[tid] = (char)mpre;
     };
+    // With a key-padding mask, keys before the entry's first visible key and
+    // after its last one are skipped tile by tile: [vis_lo, vis_hi) bounds
+    // the visible keys (empty when none is visible).
+    int vis_lo = 0, vis_hi = S_kv;
+    if constexpr (KMASK) {
+        int* sv = (int*)mst(0);   // the mask stages are free until the prologue
+        if (tid == 0) {
+            sv[0] = S_kv;
+            sv[1] = 0;
+        }
+        __syncthreads();
+        int lo_t = S_kv, hi_t = 0;
+        const uint8_t* row = key_mask + (size_t)b * S_cap;
+        for (int j = tid; j < S_kv; j += kTileThreads)
+            if (row[j] != 0) {
+                lo_t = min(lo_t, j);
+                hi_t = j + 1;
+            }
+#pragma unroll
+        for (int x = 32; x >= 1; x >>= 1) {
+            lo_t = min(lo_t, __shfl_xor(lo_t, x));
+            hi_t = max(hi_t, __shfl_xor(hi_t, x));
+        }
+        if (lane == 0) {
+            atomicMin(&sv[0], lo_t);
+            atomicMax(&sv[1], hi_t);
+        }
+        __syncthreads();
+        vis_lo = sv[0];
+        vis_hi = sv[1];
+        __syncthreads();   // before the stages are written
+    }
+    // KV tiles [lo, hi) block qb visits (walked from hi-1 down to lo)
+    auto block_tiles = [&](int qb, int& lo, int& hi) {
+        hi = tiles_for_block(qb, S_q, S_kv, causal);
+        lo = 0;
+        if constexpr (KMASK) {
+            hi = min(hi, (vis_hi + kTileN - 1) / kTileN);
+            lo = min(vis_lo / kTileN, hi);
+        }
+    };
     auto issue_block = [&](int qb) {
         const int qi = qb * kTileM + 32 * wq + l32;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
             qf[ks] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(
                                                      rq, tok_off<D>(qi, 2 * ks + g, H), 0, 0));
-        const int ntq = tiles_for_block(qb, S_q, S_kv, causal);
-        const int first = (ntq - 1) * kTileN;   // tiles run backwards
-        if (ntq > 0) {
+        int lo, hi;
+        block_tiles(qb, lo, hi);
+        const int first = (hi - 1) * kTileN;   // tiles run backwards
+        if (hi > lo) {
             if (k_loader) load_k<D>(pre, tile_rsrc<D>(K, b, h, S_cap, S_kv, H, first), H, tid);
             else load_v<D>(pre, tile_rsrc<D>(V, b, h, S_cap, S_kv, H, first), H, tid);
             load_mask(first);
@@ -376,7 +423,9 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_kernel(
 
     for (int phase = 0; phase < nphase; ++phase) {
         const int qb = phase == 0 ? qb_first : p;
-        const int nt = tiles_for_block(qb, S_q, S_kv, causal);
+        int tile_lo, tile_hi;
+        block_tiles(qb, tile_lo, tile_hi);
+        const int nt = tile_hi - tile_lo;          // steps (tiles visited)
         const int q0 = qb * kTileM + 32 * wq;      // first query of this wave
         const int qi = q0 + l32;                   // this lane's query
         const bool wave_has_rows = q0 < S_q;
@@ -404,7 +453,7 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_kernel(
         }
         __syncthreads();
         // step u works on KV tile nt-1-u: the diagonal tile first
-        auto tile_of = [&](int u) { return nt - 1 - u; };
+        auto tile_of = [&](int u) { return tile_hi - 1 - u; };
         if (k_loader && nt > 1) {
             load_k<D>(pre, tile_rsrc<D>(K, b, h, S_cap, S_kv, H, tile_of(1) * kTileN), H, tid);
             load_mask(tile_of(1) * kTileN);

@@ -364,6 +364,8 @@ MASK_CASES = [  # (B, H, S_q, S_kv, D, causal, pattern)
     (4, 2, 77, 77, 128, True, "edge_entries"),    # an entry fully hidden, one with only its last key
     (1, 4, 1000, 1000, 128, True, "random"),
     (2, 1, 33, 513, 128, False, "random"),
+    (2, 2, 300, 300, 64, True, "right_pad"),      # causal, paired blocks, trailing tiles skipped
+    (3, 2, 300, 300, 128, True, "left_pad"),      # causal, leading tiles skipped
 ]
 
 
