@@ -59,6 +59,8 @@ def _load():
             u8p = ctypes.POINTER(ctypes.c_uint8)
             lib.oracle_attn_fwd_mask_f64.argtypes = [dp, dp, dp, u8p, dp, dp] + [ctypes.c_int] * 6
             lib.oracle_attn_fwd_mask_f64.restype = ctypes.c_int
+            lib.oracle_qkv_proj_f64.argtypes = [dp, dp, dp, dp, dp] + [ctypes.c_int] * 3
+            lib.oracle_qkv_proj_f64.restype = ctypes.c_int
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
             _lib = lib
@@ -172,6 +174,28 @@ def attn_fwd_mask(q, k, v, key_mask=None, causal: bool = True):
     if rc != 0:
         raise ValueError(f"oracle_attn_fwd_mask_f64 rejected the arguments (code {rc})")
     return o, lse
+
+
+def qkv_proj(x, w, H: int, D: int):
+    """Q, K, V projections as one stacked GEMM.
+
+    x [B,S,E] (or [M,E]); w [3*H*D, E] output-major (rows 0..HD-1 give Q's
+    columns, then K's, then V's). Returns (q, k, v), each [B,S,H,D] (or
+    [M,H,D]) fp64 numpy arrays.
+    """
+    x, w = _f64(x), _f64(w)
+    lead = x.shape[:-1]
+    E = x.shape[-1]
+    M = int(np.prod(lead))
+    N = H * D
+    if w.shape != (3 * N, E):
+        raise ValueError(f"w must be [3*H*D, E] = {(3 * N, E)}, got {w.shape}")
+    x2 = np.ascontiguousarray(x.reshape(M, E))
+    outs = [np.zeros((M, N), dtype=np.float64) for _ in range(3)]
+    rc = _load().oracle_qkv_proj_f64(_ptr(x2), _ptr(w), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), M, E, N)
+    if rc != 0:
+        raise ValueError(f"oracle_qkv_proj_f64 rejected the arguments (code {rc})")
+    return tuple(o.reshape(*lead, H, D) for o in outs)
 
 
 def num_threads() -> int:

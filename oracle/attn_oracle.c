@@ -256,6 +256,38 @@ int oracle_attn_fwd_mask_f64(const double* q, const double* k, const double* v, 
     return ORACLE_OK;
 }
 
+/*
+ * Q, K and V projections of the input rows, as one GEMM with the three
+ * weight matrices stacked ("Hand-written Masked Multi-Head Attention CUDA
+ * kernel" page, section 2: Q = X W_Q, K = X W_K, V = X W_V; "Week-4 CUDA
+ * notes" page, section 2.1: the three projections are one concatenated
+ * GEMM in practice).
+ *   x        : [M, E]      input rows (M = B*S tokens, E = model width)
+ *   w        : [3*N, E]    stacked weights, output-major: row n of block
+ *                          0 / 1 / 2 holds the E weights of output column n
+ *                          of Q / K / V (N = H*D)
+ *   q, k, v  : [M, N]      = [B, S, H, D] row-major
+ * Each output is the plain dot product sum_e x[m][e] * w[c*N + n][e] in
+ * fp64, e ascending.
+ */
+int oracle_qkv_proj_f64(const double* x, const double* w, double* q, double* k, double* v, int M, int E, int N) {
+    if (M <= 0 || E <= 0 || N <= 0) return ORACLE_EINVAL;
+    double* out[3] = {q, k, v};
+    long m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m) {
+        const double* xrow = x + (size_t)m * (size_t)E;
+        for (int c = 0; c < 3; ++c)
+            for (long n = 0; n < N; ++n) {
+                const double* wrow = w + ((size_t)c * (size_t)N + (size_t)n) * (size_t)E;
+                double acc = 0.0;
+                for (long e = 0; e < E; ++e) acc += xrow[e] * wrow[e];
+                out[c][(size_t)m * (size_t)N + (size_t)n] = acc;
+            }
+    }
+    return ORACLE_OK;
+}
+
 /* Threads the OpenMP runtime will use for the passes above (1 without OpenMP). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

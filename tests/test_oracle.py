@@ -452,6 +452,59 @@ def test_key_mask_absent_or_all_visible_is_the_forward():
         assert np.array_equal(o1, ref) and np.array_equal(o2, ref) and np.array_equal(l1, l2)
 
 
+# ---------------------------------------------------------------------------
+# Q, K, V projections as one stacked GEMM (MMHA page, section 2; Week-4
+# notes, section 2.1)
+# ---------------------------------------------------------------------------
+def test_qkv_proj_matches_numpy_matmul_float64():
+    B, S, E, H, D = 2, 5, 48, 3, 16
+    x = rnd(281, B, S, E)
+    w = rnd(282, 3 * H * D, E)
+    q, k, v = oracle.qkv_proj(x, w, H, D)
+    ref = x.reshape(B * S, E) @ w.T            # [M, 3*H*D], library GEMM in float64
+    got = np.concatenate([t.reshape(B * S, H * D) for t in (q, k, v)], axis=1)
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_qkv_proj_identity_and_permutation_weights_are_exact():
+    """W_Q = I gives Q = X, W_K = 2I gives K = 2X, W_V a permutation gives V =
+    the permuted columns of X: exact in any arithmetic."""
+    B, S, H, D = 2, 3, 2, 4
+    E = H * D
+    x = rnd(283, B, S, E)
+    perm = np.random.default_rng(284).permutation(E)
+    w = np.concatenate([np.eye(E), 2.0 * np.eye(E), np.eye(E)[perm]], axis=0)
+    q, k, v = oracle.qkv_proj(x, w, H, D)
+    assert np.array_equal(q.reshape(B, S, E), x)
+    assert np.array_equal(k.reshape(B, S, E), 2.0 * x)
+    assert np.array_equal(v.reshape(B, S, E), x[..., perm])
+
+
+def test_qkv_proj_brute_force_exact_rationals():
+    """Small integers: every dot product is exact, checked with Fractions."""
+    M, E, H, D = 3, 5, 1, 2
+    g = np.random.default_rng(285)
+    x = g.integers(-4, 5, (M, E)).astype(np.float64)
+    w = g.integers(-4, 5, (3 * H * D, E)).astype(np.float64)
+    q, k, v = oracle.qkv_proj(x, w, H, D)
+    for c, out in enumerate((q, k, v)):
+        for m in range(M):
+            for n in range(H * D):
+                exact = sum(Fraction(int(x[m, e])) * Fraction(int(w[c * H * D + n, e])) for e in range(E))
+                assert out[m].reshape(-1)[n] == float(exact)
+
+
+def test_qkv_proj_is_linear_in_the_input():
+    M, E, H, D = 7, 32, 2, 8
+    x1, x2 = rnd(286, M, E), rnd(287, M, E)
+    w = rnd(288, 3 * H * D, E)
+    a = oracle.qkv_proj(2.5 * x1 + x2, w, H, D)
+    b1 = oracle.qkv_proj(x1, w, H, D)
+    b2 = oracle.qkv_proj(x2, w, H, D)
+    for t, u1, u2 in zip(a, b1, b2):
+        assert np.max(np.abs(t - (2.5 * u1 + u2))) <= 1e-12
+
+
 def test_rejects_invalid_arguments():
     q = rnd(1, 1, 4, 1, 8)
     with pytest.raises(ValueError):

@@ -42,6 +42,11 @@ MUTANTS = {
     "key_mask_inverted": ("kmask[j] == 0", "kmask[j] != 0"),
     "key_mask_on_queries": ("(kmask && kmask[j] == 0)", "(kmask && kmask[i % S_kv] == 0)"),
     "key_mask_of_entry_0_for_all": ("key_mask ? key_mask + (size_t)b * (size_t)S_kv : NULL", "key_mask"),
+    "qkv_weight_read_transposed": ("for (long e = 0; e < E; ++e) acc += xrow[e] * wrow[e];",
+                                   "for (long e = 0; e < E; ++e) acc += xrow[e] * w[(size_t)e * 3 * N + (size_t)c * N + n];"),
+    "qkv_q_and_k_swapped": ("double* out[3] = {q, k, v};", "double* out[3] = {k, q, v};"),
+    "qkv_dropped_last_term": ("for (long e = 0; e < E; ++e) acc += xrow[e] * wrow[e];",
+                              "for (long e = 0; e + 1 < E; ++e) acc += xrow[e] * wrow[e];"),
 }
 
 PINS = [
@@ -64,6 +69,8 @@ PINS = [
     lambda: pins.test_key_mask_matches_sdpa_and_logsumexp_float64(9, 31, True),
     pins.test_key_mask_equals_deleting_the_keys,
     pins.test_key_mask_with_equal_keys_gives_means_of_the_visible_values,
+    pins.test_qkv_proj_matches_numpy_matmul_float64,
+    pins.test_qkv_proj_identity_and_permutation_weights_are_exact,
 ]
 
 
