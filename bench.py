@@ -159,7 +159,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="also time 20 back-to-back calls without the flush")
     ap.add_argument("--skip-extras", action="store_true",
-                    help="leave out the KV-cache, fp16 and key-padding prefill measurements")
+                    help="leave out the KV-cache, fp16, key-padding and Q/K/V projection measurements")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one device copy of MIB MiB (reference for HBM counters)")
     args = ap.parse_args()
@@ -271,7 +271,7 @@ def main() -> int:
                              "flop_per_launch": flop, "mean_launch_us": round(mean * 1e3, 2),
                              "median_launch_us": round(statistics.median(ms) * 1e3, 2)}}
 
-    kv = f16 = kp = None
+    kv = f16 = kp = qp = None
     if not args.skip_extras:
         kc_cfg = workloads.BF16_KVCACHE
         log("KV-cache prefill: generating inputs")
@@ -313,6 +313,17 @@ def main() -> int:
                       f"bf16 key-padding forward B={pc_k.B} H={pc_k.H} S={pc_k.S} D={pc_k.D}, no causal rule, "
                       f"key lengths {lens_k.tolist()} (seed {pc_k.seed}); cold, 20 calls")
         del qk, kk, vk, mk, ok
+
+        # the Q/K/V projection of the bf16_s2048 layer as one GEMM
+        qc = workloads.BF16_QKV
+        log("Q/K/V projection")
+        xq_h, wq_h = workloads.make_qkv_proj(qc)
+        xq, wq = xq_h.to(dev), wq_h.to(dev)
+        outs = [torch.empty(qc.B, qc.S, qc.H, qc.D, dtype=qc.dtype, device=dev) for _ in range(3)]
+        qp = mfma_leg(cold_ms(lambda: attn.qkv_proj(xq, wq, qc.H, qc.D, *outs)), qc.flops(),
+                      f"bf16 Q/K/V projection M={qc.B * qc.S} E={qc.E} N=3x{qc.H * qc.D} (seed {qc.seed}); "
+                      f"cold, 20 calls")
+        del xq, wq, outs
 
     if args.copy_calibration:
         n = args.copy_calibration << 20
@@ -395,6 +406,7 @@ def main() -> int:
         "kvcache_prefill": kv,
         "fp16_prefill": f16,
         "keypad_prefill": kp,
+        "qkv_proj": qp,
         "cpu_baseline": cpu,
         "parity": parity,
     }

@@ -61,6 +61,8 @@ def _load() -> ctypes.CDLL:
     lib.attn_decode.restype = i
     lib.attn_fwd_mask.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i]
     lib.attn_fwd_mask.restype = i
+    lib.attn_qkv_proj.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i]
+    lib.attn_qkv_proj.restype = i
     lib.attn_set_stream.argtypes = [vp]
     lib.attn_set_stream.restype = i
     lib.attn_set_timing_events.argtypes = [vp, vp]
@@ -218,6 +220,43 @@ def attn_fwd_mask(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_mask: t
     return (o, lse) if return_lse else o
 
 
+def qkv_proj(x: torch.Tensor, w: torch.Tensor, H: int, D: int, q: torch.Tensor | None = None,
+             k: torch.Tensor | None = None, v: torch.Tensor | None = None):
+    """Q, K, V projections as one GEMM. x [B,S,E] (or [M,E]); w [3*H*D, E] output-major.
+    Returns (q, k, v), each [B,S,H,D] (or [M,H,D]) in x's dtype (bfloat16 or float16)."""
+    if not isinstance(x, torch.Tensor) or not isinstance(w, torch.Tensor):
+        raise TypeError("x and w must be torch.Tensors")
+    for n, t in (("x", x), ("w", w)):
+        if not t.is_cuda:
+            raise ValueError(f"{n} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    if x.dim() < 2 or w.dim() != 2:
+        raise ValueError("x must be [..., E] and w [3*H*D, E]")
+    if x.dtype != w.dtype:
+        raise TypeError("x and w must share one dtype")
+    E = x.shape[-1]
+    lead = tuple(x.shape[:-1])
+    M = 1
+    for s in lead:
+        M *= s
+    if tuple(w.shape) != (3 * H * D, E):
+        raise ValueError(f"w must be [3*H*D, E] = {(3 * H * D, E)}, got {tuple(w.shape)}")
+    outs = []
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        if t is None:
+            t = torch.empty(lead + (H, D), dtype=x.dtype, device=x.device)
+        else:
+            _dev_tensor(n, t, len(lead) + 2)
+            if tuple(t.shape) != lead + (H, D) or t.dtype != x.dtype:
+                raise ValueError(f"{n} must be {lead + (H, D)} of dtype {x.dtype}")
+        outs.append(t)
+    _set_stream(x.device)
+    _check(load().attn_qkv_proj(x.data_ptr(), w.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(),
+                                outs[2].data_ptr(), M, E, H, D, _dtype_code(x)))
+    return tuple(outs)
+
+
 def attn_decode_workspace_bytes(B: int, H: int, S_cap: int, D: int) -> int:
     return int(load().attn_decode_workspace_bytes(B, H, S_cap, D))
 
@@ -266,6 +305,6 @@ def attn_decode_plan(B: int, H: int, S_cap: int, D: int, dtype: int) -> DecodePl
     return plan
 
 
-__all__ = ["attn_fwd", "attn_fwd_kvcache", "attn_fwd_mask", "attn_decode", "attn_decode_workspace_bytes", "attn_fwd_plan", "attn_decode_plan",
+__all__ = ["attn_fwd", "attn_fwd_kvcache", "attn_fwd_mask", "attn_decode", "qkv_proj", "attn_decode_workspace_bytes", "attn_fwd_plan", "attn_decode_plan",
            "attn_set_timing_events",
            "AttnError", "ATTN_F32", "ATTN_BF16", "ATTN_F16", "lib", "LIB_PATH"]

@@ -25,6 +25,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "fwd_tile.hip"),
     os.path.join(CSRC, "kernels", "fwd_row.hip"),
     os.path.join(CSRC, "kernels", "decode.hip"),
+    os.path.join(CSRC, "kernels", "qkv_proj.hip"),
 ]
 
 ARCH = "gfx950"

@@ -315,4 +315,43 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
     return ok();
 }
 
+int attn_qkv_proj(const void* x, const void* w, void* q, void* k, void* v, int M, int E, int H, int D, int dtype) {
+    hipEvent_t ev_start, ev_stop;
+    take_events(ev_start, ev_stop);
+    if (M < 0 || E <= 0 || H <= 0 || D <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_qkv_proj: sizes must be M >= 0 and E, H, D >= 1");
+    if (dtype != ATTN_BF16 && dtype != ATTN_F16)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_qkv_proj: dtype " + std::to_string(dtype) +
+                                              " not built (ATTN_BF16 or ATTN_F16)");
+    if (E % attn::kGemmBK != 0)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_qkv_proj: E must be a multiple of 64");
+    const long long N = (long long)H * D;
+    if (N % 32 != 0) return fail(ATTN_ERR_UNSUPPORTED, "attn_qkv_proj: H*D must be a multiple of 32");
+    // per-tile descriptors span 256 rows of X or of an output, 192 rows of W
+    if ((long long)attn::kGemmBM * E * 2 > 0x7fffffffLL || (long long)attn::kGemmBM * N * 2 > 0x7fffffffLL ||
+        3 * N > 0x7fffffffLL)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_qkv_proj: E or H*D too large for 32-bit tile offsets");
+    if (tensor_bytes(M, E, 1, 1, 2) < 0 || tensor_bytes(3, N, E, 1, 2) < 0 || tensor_bytes(M, N, 1, 1, 2) < 0 ||
+        attn::qkv_grid(M, (int)N) > 0x7fffffffLL)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_qkv_proj: sizes overflow");
+    if (M == 0) return ok();
+    if (!x || !w || !q || !k || !v) return fail(ATTN_ERR_INVALID_ARG, "attn_qkv_proj: NULL tensor pointer");
+    if (!aligned16(x) || !aligned16(w) || !aligned16(q) || !aligned16(k) || !aligned16(v))
+        return fail(ATTN_ERR_INVALID_ARG, "attn_qkv_proj: tensor pointers must be 16-byte aligned");
+    const long long nx = (long long)M * E * 2, nw = 3 * N * E * 2, no = (long long)M * N * 2;
+    const void* outs[3] = {q, k, v};
+    for (int i = 0; i < 3; ++i) {
+        if (overlap(outs[i], no, x, nx) || overlap(outs[i], no, w, nw))
+            return fail(ATTN_ERR_INVALID_ARG, "attn_qkv_proj: an output overlaps an input");
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], no, outs[j], no))
+                return fail(ATTN_ERR_INVALID_ARG, "attn_qkv_proj: outputs overlap each other");
+    }
+    attn::QkvArgs a{x, w, q, k, v, M, E, (int)N, ev_start, ev_stop};
+    const hipError_t e = attn::launch_qkv_proj(a, elt_of(dtype), t_stream);
+    if (e != hipSuccess)
+        return fail(ATTN_ERR_HIP, std::string("attn_qkv_proj: launch failed: ") + hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

@@ -45,11 +45,24 @@ struct DecodeArgs {
     hipEvent_t ev_stop;    // optional: recorded when the combine kernel ends
 };
 
+struct QkvArgs {
+    const void* x;   // [M, E]
+    const void* w;   // [3N, E], output-major
+    void* q;         // [M, N] each
+    void* k;
+    void* v;
+    int M, E, N;
+    hipEvent_t ev_start;
+    hipEvent_t ev_stop;
+};
+
 // MFMA tile kernel for 16-bit storage (BF16 or F16); D in {32, 64, 128}.
 hipError_t launch_fwd_tile(const FwdArgs& a, Elt t, hipStream_t stream);
 // Row kernel: one wave per query row, any storage type.
 hipError_t launch_fwd_row(const FwdArgs& a, Elt t, hipStream_t stream);
 // Split-KV decode (split + combine kernels), any storage type.
 hipError_t launch_decode(const DecodeArgs& a, Elt t, hipStream_t stream);
+// Q/K/V projection GEMM, 16-bit storage.
+hipError_t launch_qkv_proj(const QkvArgs& a, Elt t, hipStream_t stream);
 
 }  // namespace attn

@@ -129,4 +129,17 @@ ATTN_HD inline size_t decode_workspace_floats(int B, int H, int /*S_cap*/, int D
     return (size_t)decode_records(B) * (size_t)H * (size_t)(D + 2);
 }
 
+// ---------------------------------------------------------------------------
+// Q/K/V projection GEMM: 256 x 192 tiles of C = X W^T, 64-wide K steps,
+// eight waves in a 4 x 2 grid.
+// ---------------------------------------------------------------------------
+constexpr int kGemmBM = 256;
+constexpr int kGemmBN = 192;
+constexpr int kGemmBK = 64;
+constexpr int kGemmThreads = 512;
+
+ATTN_HD inline long long qkv_grid(int M, int N) {
+    return (long long)((M + kGemmBM - 1) / kGemmBM) * ((3LL * N + kGemmBN - 1) / kGemmBN);
+}
+
 }  // namespace attn

@@ -173,6 +173,26 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
                 size_t workspace_bytes);
 
 /*
+ * attn_qkv_proj -- the Q, K and V projections of the input rows as one GEMM
+ * over the stacked weights: Q = X W_Q, K = X W_K, V = X W_V (MMHA page,
+ * section 2), concatenated into a single GEMM ("Week-4 CUDA notes" page,
+ * section 2.1). fp32 accumulation, outputs rounded to the storage type.
+ *
+ *   x       : [M, E]       input rows (M = B*S tokens), DEVICE
+ *   w       : [3*H*D, E]   stacked weights, output-major (the layout of a
+ *                          linear layer's weight): row c*H*D + n holds the E
+ *                          weights of output column n of Q (c = 0), K (1) or
+ *                          V (2), so q[m][n] = sum_e x[m][e] * w[n][e], DEVICE
+ *   q, k, v : [M, H*D] each = [B, S, H, D], the inputs of attn_fwd, DEVICE
+ *   dtype   : ATTN_BF16 or ATTN_F16 for all five (else ATTN_ERR_UNSUPPORTED).
+ *   E must be a multiple of 64 and H*D of 32 (else ATTN_ERR_UNSUPPORTED).
+ *   M == 0 is a valid empty call. Pointers 16-byte aligned; no output may
+ *   overlap an input or another output.
+ */
+int attn_qkv_proj(const void* x, const void* w, void* q, void* k, void* v, int M, int E, int H, int D,
+                  int dtype);
+
+/*
  * attn_set_stream -- set the HIP stream (a hipStream_t passed as void*) that
  * later calls from THIS thread enqueue on; NULL selects the null stream.
  * attn_get_stream returns the current thread's stream.

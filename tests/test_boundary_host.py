@@ -181,6 +181,36 @@ def test_decode_empty_call():
     assert dec(q=0, kc=0, vc=0, sl=0, o=0, ws=0, B=0, wsb=0) == attn.ATTN_OK
 
 
+# ---------------------------------------------------------------------------
+# Q/K/V projection boundary (fake device addresses: every case is rejected
+# on the host before any HIP call)
+# ---------------------------------------------------------------------------
+def qkv(x=A, w=A + 0x1000000, q=A + 0x4000000, k=A + 0x5000000, v=A + 0x6000000, M=100, E=256, H=2, D=64,
+        dtype=attn.ATTN_BF16):
+    return L.attn_qkv_proj(x, w, q, k, v, M, E, H, D, dtype)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=attn.ATTN_F32), attn.ATTN_ERR_UNSUPPORTED, "dtype"),
+    (dict(E=100), attn.ATTN_ERR_UNSUPPORTED, "multiple of 64"),
+    (dict(H=1, D=48), attn.ATTN_ERR_UNSUPPORTED, "multiple of 32"),
+    (dict(M=-1), attn.ATTN_ERR_INVALID_ARG, "sizes"),
+    (dict(E=0), attn.ATTN_ERR_INVALID_ARG, "sizes"),
+    (dict(x=0), attn.ATTN_ERR_INVALID_ARG, "NULL"),
+    (dict(w=A + 0x1000008), attn.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(q=A + 0x100), attn.ATTN_ERR_INVALID_ARG, "overlaps an input"),          # q inside x
+    (dict(k=A + 0x4000000), attn.ATTN_ERR_INVALID_ARG, "each other"),            # k on q
+    (dict(E=1 << 23), attn.ATTN_ERR_UNSUPPORTED, "32-bit"),
+])
+def test_qkv_rejections(kw, status, needle):
+    assert qkv(**kw) == status, L.attn_last_error()
+    assert needle in attn.load().attn_last_error().decode()
+
+
+def test_qkv_empty_call():
+    assert qkv(x=0, w=0, q=0, k=0, v=0, M=0) == attn.ATTN_OK
+
+
 def test_binding_rejects_host_tensors():
     q = torch.zeros(1, 4, 1, 32)
     with pytest.raises(ValueError):

@@ -438,6 +438,60 @@ def test_fp16_prefill_full_size(attn):
 
 
 # ---------------------------------------------------------------------------
+# Q/K/V projection GEMM (attn_qkv_proj)
+# ---------------------------------------------------------------------------
+QKV_CASES = [  # (B, S, E, H, D)
+    (1, 300, 128, 2, 64),       # M not a multiple of the 256-row tile
+    (2, 130, 256, 3, 32),       # 3N = 288: the last 192-column tile is two-thirds empty
+    (1, 512, 512, 4, 128),      # 192-column tiles straddle the Q/K and K/V boundaries
+    (1, 1, 64, 1, 32),          # one row, one K step
+    (3, 77, 1024, 8, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("case", QKV_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_qkv_proj_against_oracle(attn, case, dtype):
+    B, S, E, H, D = case
+    say(f"qkv proj {case} {dtype}")
+    cfg = workloads.QkvProj("edge", dtype, B, S, E, H, D, 900 + E)
+    x, w = workloads.make_qkv_proj(cfg)
+    q, k, v = attn.qkv_proj(x.cuda(), w.cuda(), H, D)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.qkv_proj(x, w, H, D)
+    for name, got, ref in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+        check(got, ref, dtype, f"qkv {case} {name}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
+def test_qkv_proj_identity_weights_copy_x_bitwise(attn, dtype):
+    """W_Q = I, W_K = 2I, W_V = I: fp32 sums of one nonzero product round back exactly."""
+    B, S, H, D = 2, 300, 4, 64
+    E = H * D
+    x = torch.randn(B, S, E, generator=torch.Generator().manual_seed(910)).to(dtype)
+    eye = torch.eye(E)
+    w = torch.cat([eye, 2 * eye, eye], 0).to(dtype)
+    q, k, v = attn.qkv_proj(x.cuda(), w.cuda(), H, D)
+    xs = x.reshape(B, S, H, D)
+    assert torch.equal(q.cpu(), xs) and torch.equal(v.cpu(), xs) and torch.equal(k.cpu(), (2 * xs.float()).to(dtype))
+
+
+def test_qkv_proj_full_size_sampled_rows(attn):
+    """The bf16_qkv workload at full size, in the launch bench.py times; the
+    oracle checks a sample of rows (each row of the output depends on one
+    row of X only)."""
+    cfg = workloads.BF16_QKV
+    say(f"qkv proj full size M={cfg.B * cfg.S} E={cfg.E} N={cfg.H * cfg.D}")
+    x, w = workloads.make_qkv_proj(cfg)
+    q, k, v = attn.qkv_proj(x.cuda(), w.cuda(), cfg.H, cfg.D)
+    torch.cuda.synchronize()
+    rows = [0, 1, 255, 256, 777, 1024, 1535, 2046, 2047]
+    rq, rk, rv = oracle.qkv_proj(x[:, rows], w, cfg.H, cfg.D)
+    for name, got, ref in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+        check(got[:, rows], ref, torch.bfloat16, f"qkv full {name}")
+
+
+# ---------------------------------------------------------------------------
 # Error paths through the binding on a live device
 # ---------------------------------------------------------------------------
 def test_error_paths_on_device(attn):

@@ -28,8 +28,11 @@ The five workloads:
 * ``bf16_keypad``   bf16 key-padding forward: B=8 sequences padded to S=1024,
                     H=32, D=128, no causal rule, key j of entry b visible iff
                     j < len_b with len_b uniform in [256, 1024] (right padding)
+* ``bf16_qkv``      bf16 Q/K/V projection of the bf16_s2048 layer: X [1, 2048,
+                    4096] ~ N(0,1), stacked weights [3*32*128, 4096] ~ N(0,
+                    1/4096) (unit-variance outputs), drawn x then w
 
-Generator: a torch CPU ``Generator`` seeded with ``1000 + index`` (1001..1008).
+Generator: a torch CPU ``Generator`` seeded with ``1000 + index`` (1001..1009).
 Prefill draws q, k, v in that order as ``randn(B,S,H,D) * std``; decode,
 the KV-cache prefill and the key-padding forward draw the lengths first,
 then q, K and V. bf16 tensors are the
@@ -147,6 +150,25 @@ class KeyPadPrefill:
 
 BF16_KEYPAD = KeyPadPrefill("bf16_keypad", torch.bfloat16, 8, 32, 1024, 128, 1008, 256, 1024)
 
+
+@dataclass(frozen=True)
+class QkvProj:
+    name: str
+    dtype: torch.dtype
+    B: int
+    S: int
+    E: int
+    H: int
+    D: int
+    seed: int
+
+    def flops(self) -> int:
+        """2 * M * E * 3HD: one multiply-add per (row, input, output) triple."""
+        return 2 * self.B * self.S * self.E * 3 * self.H * self.D
+
+
+BF16_QKV = QkvProj("bf16_qkv", torch.bfloat16, 1, 2048, 4096, 32, 128, 1009)
+
 PREFILL_CONFIGS = (FP32_TINY, FP32_SMALL, BF16_S2048, BF16_S4096)
 
 
@@ -218,6 +240,21 @@ def make_keypad_prefill(cfg: KeyPadPrefill):
     v = torch.randn(cfg.B, cfg.S, cfg.H, cfg.D, generator=g).to(cfg.dtype)
     mask = torch.arange(cfg.S)[None, :] < lens[:, None]
     return lens, mask, q.contiguous(), k.contiguous(), v.contiguous()
+
+
+def make_qkv_proj(cfg: QkvProj, B: int | None = None, S: int | None = None, E: int | None = None,
+                  H: int | None = None, D: int | None = None):
+    """Draw (x [B,S,E], w [3*H*D, E]) on the CPU; w ~ N(0, 1/E) so the outputs
+    have unit variance."""
+    B = cfg.B if B is None else B
+    S = cfg.S if S is None else S
+    E = cfg.E if E is None else E
+    H = cfg.H if H is None else H
+    D = cfg.D if D is None else D
+    g = torch.Generator().manual_seed(cfg.seed)
+    x = torch.randn(B, S, E, generator=g).to(cfg.dtype)
+    w = (torch.randn(3 * H * D, E, generator=g) / E ** 0.5).to(cfg.dtype)
+    return x.contiguous(), w.contiguous()
 
 
 def make_kvcache_prefill(cfg: KVCachePrefill, nan_fill: bool = False, seqlens=None, S_cap: int | None = None,
