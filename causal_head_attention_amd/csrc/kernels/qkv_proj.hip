@@ -15,7 +15,9 @@
 // One workgroup (8 waves, 2 per SIMD) owns a 256 x 192 tile of C and walks E
 // in steps of 64: both operand tiles go HBM -> registers -> LDS (rows padded
 // to 144 bytes, so the 32 lanes that read one MFMA fragment hit distinct
-// banks), double-buffered, one barrier per step. Wave (wm, wn) of the 4 x 2
+// banks), double-buffered in LDS, one barrier per step. Two register sets
+// carry the loads, so each K slice is requested two steps before it is
+// stored (its L2 / Infinity Cache latency is about one step). Wave (wm, wn) of the 4 x 2
 // grid computes a 64 x 96 sub-tile as 2 x 3 blocks of
 // v_mfma_f32_32x32x16_{bf16,f16}. Workgroup ids are remapped so each XCD gets
 // a contiguous range of logical tiles, M-tile fastest: the workgroups that
@@ -83,32 +85,36 @@ __global__ __launch_bounds__(kGemmThreads) void qkv_proj_kernel(const uint16_t* 
     const __amdgpu_buffer_rsrc_t rb =
         __builtin_amdgcn_make_buffer_rsrc((void*)(W + (size_t)n0 * E), (short)0, rows_b * E * 2, 0x00020000);
 
-    // thread t stages 16-byte chunks c = t + 512 i: row c / 8, chunk c % 8
-    u32x4_t pa[kAChunks], pb[kBChunks];
-    auto gload = [&](int k0) {
+    // thread t stages 16-byte chunks c = t + 512 i: row c / 8, chunk c % 8;
+    // two register sets, so a K slice is loaded two steps before it is stored
+    struct Regs {
+        u32x4_t a[kAChunks], b[kBChunks];
+    };
+    Regs r0, r1;
+    auto gload = [&](Regs& r, int k0) {
 #pragma unroll
         for (int i = 0; i < kAChunks; ++i) {
             const int c = tid + kGemmThreads * i;
-            pa[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, (c >> 3) * E * 2 + k0 * 2 + (c & 7) * 16, 0, 0);
+            r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, (c >> 3) * E * 2 + k0 * 2 + (c & 7) * 16, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < kBChunks; ++i) {
             const int c = tid + kGemmThreads * i;
-            pb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, (c >> 3) * E * 2 + k0 * 2 + (c & 7) * 16, 0, 0);
+            r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, (c >> 3) * E * 2 + k0 * 2 + (c & 7) * 16, 0, 0);
         }
     };
-    auto lstore = [&](int st) {
+    auto lstore = [&](const Regs& r, int st) {
         char* a = lds + st * kStageBytes;
         char* b = a + kABytes;
 #pragma unroll
         for (int i = 0; i < kAChunks; ++i) {
             const int c = tid + kGemmThreads * i;
-            *(u32x4_t*)(a + (c >> 3) * kRowBytes + (c & 7) * 16) = pa[i];
+            *(u32x4_t*)(a + (c >> 3) * kRowBytes + (c & 7) * 16) = r.a[i];
         }
 #pragma unroll
         for (int i = 0; i < kBChunks; ++i) {
             const int c = tid + kGemmThreads * i;
-            *(u32x4_t*)(b + (c >> 3) * kRowBytes + (c & 7) * 16) = pb[i];
+            *(u32x4_t*)(b + (c >> 3) * kRowBytes + (c & 7) * 16) = r.b[i];
         }
     };
 
@@ -126,13 +132,10 @@ __global__ __launch_bounds__(kGemmThreads) void qkv_proj_kernel(const uint16_t* 
     const int b_lane = (wn * 96 + l32) * kRowBytes + g * 16;
 
     const int nk = E / kGemmBK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int s = 0; s < nk; ++s) {
-        if (s + 1 < nk) gload((s + 1) * kGemmBK);
-        const char* a = lds + (s & 1) * kStageBytes + a_lane;
-        const char* b = lds + (s & 1) * kStageBytes + kABytes + b_lane;
+    auto slice = [&](int i) { return (i < nk ? i : nk - 1) * kGemmBK; };   // past the end: reload the last
+    auto compute = [&](int st) {
+        const char* a = lds + st * kStageBytes + a_lane;
+        const char* b = lds + st * kStageBytes + kABytes + b_lane;
 #pragma unroll
         for (int ks = 0; ks < kGemmBK / 16; ++ks) {
             v8 af[2], bf[3];
@@ -145,9 +148,25 @@ __global__ __launch_bounds__(kGemmThreads) void qkv_proj_kernel(const uint16_t* 
 #pragma unroll
                 for (int nb = 0; nb < 3; ++nb) acc[mb][nb] = GemmMma<T>::mfma(af[mb], bf[nb], acc[mb][nb]);
         }
-        // stage s+1's last reader ran before the previous barrier
-        if (s + 1 < nk) lstore((s + 1) & 1);
+    };
+    gload(r0, slice(0));
+    gload(r1, slice(1));
+    lstore(r0, 0);
+    __syncthreads();
+    // steps s (stage 0) and s+1 (stage 1): slice s+2 goes into r0 while stage 0
+    // is read, slice s+1 (in r1 since the previous pair) lands in stage 1;
+    // stores past the last step write a stage no one reads again
+    for (int s = 0; s < nk; s += 2) {
+        gload(r0, slice(s + 2));
+        compute(0);
+        lstore(r1, 1);
         __syncthreads();
+        if (s + 1 < nk) {
+            gload(r1, slice(s + 3));
+            compute(1);
+            lstore(r0, 0);
+            __syncthreads();
+        }
     }
 
     // Epilogue. Lane holds column l32 of each 32 x 32 block and rows
