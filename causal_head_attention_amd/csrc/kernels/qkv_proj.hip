@@ -17,8 +17,8 @@
 // to 144 bytes, so the 32 lanes that read one MFMA fragment hit distinct
 // banks), double-buffered in LDS, one barrier per step. Two register sets
 // carry the loads, so each K slice is requested two steps before it is
-// stored (its L2 / Infinity Cache latency is about one step). Wave (wm, wn) of the 4 x 2
-// grid computes a 64 x 96 sub-tile as 2 x 3 blocks of
+// stored (its L2 / Infinity Cache latency is about one step). Wave (wm, wn)
+// of the 4 x 2 grid computes a 64 x 96 sub-tile as 2 x 3 blocks of
 // v_mfma_f32_32x32x16_{bf16,f16}. Workgroup ids are remapped so each XCD gets
 // a contiguous range of logical tiles, M-tile fastest: the workgroups that
 // share a W tile run on one XCD at the same time and find it in its L2.

@@ -445,6 +445,7 @@ QKV_CASES = [  # (B, S, E, H, D)
     (2, 130, 256, 3, 32),       # 3N = 288: the last 192-column tile is two-thirds empty
     (1, 512, 512, 4, 128),      # 192-column tiles straddle the Q/K and K/V boundaries
     (1, 1, 64, 1, 32),          # one row, one K step
+    (1, 100, 192, 2, 32),       # three K steps: the loop's second half runs once less
     (3, 77, 1024, 8, 64),
 ]
 
