@@ -61,6 +61,8 @@ def _load():
             lib.oracle_attn_fwd_mask_f64.restype = ctypes.c_int
             lib.oracle_qkv_proj_f64.argtypes = [dp, dp, dp, dp, dp] + [ctypes.c_int] * 3
             lib.oracle_qkv_proj_f64.restype = ctypes.c_int
+            lib.oracle_sinusoidal_pe_f64.argtypes = [dp] + [ctypes.c_int] * 3
+            lib.oracle_sinusoidal_pe_f64.restype = ctypes.c_int
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
             _lib = lib
@@ -196,6 +198,15 @@ def qkv_proj(x, w, H: int, D: int):
     if rc != 0:
         raise ValueError(f"oracle_qkv_proj_f64 rejected the arguments (code {rc})")
     return tuple(o.reshape(*lead, H, D) for o in outs)
+
+
+def sinusoidal_pe(S: int, d_model: int, pos0: int = 0):
+    """[S, d_model] fp64 position encoding for positions pos0 .. pos0+S-1."""
+    pe = np.zeros((S, d_model), dtype=np.float64)
+    rc = _load().oracle_sinusoidal_pe_f64(_ptr(pe), S, d_model, pos0)
+    if rc != 0:
+        raise ValueError(f"oracle_sinusoidal_pe_f64 rejected the arguments (code {rc})")
+    return pe
 
 
 def num_threads() -> int:

@@ -288,6 +288,28 @@ int oracle_qkv_proj_f64(const double* x, const double* w, double* q, double* k, 
     return ORACLE_OK;
 }
 
+/*
+ * Sinusoidal position encoding ("Week-4 CUDA notes" page, section 2.3):
+ *   pe[s][2i]   = sin(pos / 10000^(2i/d_model))
+ *   pe[s][2i+1] = cos(pos / 10000^(2i/d_model)),   pos = pos0 + s
+ * for s < S and i < d_model/2, fp64, the formula as written (the power taken
+ * directly). d_model must be even.
+ */
+int oracle_sinusoidal_pe_f64(double* pe, int S, int d_model, int pos0) {
+    if (S <= 0 || d_model <= 0 || (d_model & 1) || pos0 < 0) return ORACLE_EINVAL;
+    long s;
+#pragma omp parallel for schedule(static)
+    for (s = 0; s < S; ++s) {
+        const double pos = (double)pos0 + (double)s;
+        for (long i = 0; i < d_model / 2; ++i) {
+            const double angle = pos / pow(10000.0, (double)(2 * i) / (double)d_model);
+            pe[(size_t)s * (size_t)d_model + (size_t)(2 * i)] = sin(angle);
+            pe[(size_t)s * (size_t)d_model + (size_t)(2 * i + 1)] = cos(angle);
+        }
+    }
+    return ORACLE_OK;
+}
+
 /* Threads the OpenMP runtime will use for the passes above (1 without OpenMP). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

@@ -505,6 +505,48 @@ def test_qkv_proj_is_linear_in_the_input():
         assert np.max(np.abs(t - (2.5 * u1 + u2))) <= 1e-12
 
 
+# ---------------------------------------------------------------------------
+# Sinusoidal position encoding (Week-4 notes page, section 2.3)
+# ---------------------------------------------------------------------------
+def test_pe_position_zero_and_first_pair():
+    """pos 0: every sine is 0 and every cosine 1; dims 0/1 have frequency 1, so
+    they are sin(pos), cos(pos) (math library, float64)."""
+    pe = oracle.sinusoidal_pe(37, 64)
+    assert np.all(pe[0, 0::2] == 0.0) and np.all(pe[0, 1::2] == 1.0)
+    pos = np.arange(37, dtype=np.float64)
+    assert np.max(np.abs(pe[:, 0] - [math.sin(p) for p in pos])) <= 1e-15
+    assert np.max(np.abs(pe[:, 1] - [math.cos(p) for p in pos])) <= 1e-15
+
+
+def test_pe_frequencies_and_unit_pairs():
+    """Pair i oscillates with angular frequency 10000^(-2i/d): the angle
+    atan2(sin, cos) of pair i at position 1 is that frequency (all < pi);
+    every (sin, cos) pair has unit length."""
+    d = 128
+    pe = oracle.sinusoidal_pe(5, d)
+    for i in range(d // 2):
+        w = 10000.0 ** (-2.0 * i / d)
+        assert abs(math.atan2(pe[1, 2 * i], pe[1, 2 * i + 1]) - w) <= 1e-15
+    assert np.max(np.abs(pe[:, 0::2] ** 2 + pe[:, 1::2] ** 2 - 1.0)) <= 1e-15
+
+
+def test_pe_shift_is_a_rotation():
+    """PE(pos + k) is PE(pos) rotated pair by pair by the angle PE(k) holds
+    (the relative-position property): sin(a+b) = sin a cos b + cos a sin b,
+    cos(a+b) = cos a cos b - sin a sin b."""
+    d, k = 96, 17
+    pe = oracle.sinusoidal_pe(60, d)
+    s, c = pe[:-k, 0::2], pe[:-k, 1::2]
+    sk, ck = pe[k, 0::2], pe[k, 1::2]
+    assert np.max(np.abs(pe[k:, 0::2] - (s * ck + c * sk))) <= 1e-12
+    assert np.max(np.abs(pe[k:, 1::2] - (c * ck - s * sk))) <= 1e-12
+
+
+def test_pe_offset_rows_are_the_later_rows():
+    full = oracle.sinusoidal_pe(50, 32)
+    assert np.array_equal(oracle.sinusoidal_pe(20, 32, pos0=30), full[30:])
+
+
 def test_rejects_invalid_arguments():
     q = rnd(1, 1, 4, 1, 8)
     with pytest.raises(ValueError):

@@ -45,6 +45,10 @@ MUTANTS = {
     "qkv_weight_read_transposed": ("for (long e = 0; e < E; ++e) acc += xrow[e] * wrow[e];",
                                    "for (long e = 0; e < E; ++e) acc += xrow[e] * w[(size_t)e * 3 * N + (size_t)c * N + n];"),
     "qkv_q_and_k_swapped": ("double* out[3] = {q, k, v};", "double* out[3] = {k, q, v};"),
+    "pe_sin_cos_swapped": ("+ (size_t)(2 * i)] = sin(angle);", "+ (size_t)(2 * i)] = cos(angle);"),
+    "pe_exponent_over_i": ("(double)(2 * i) / (double)d_model", "(double)(i) / (double)d_model"),
+    "pe_base_1000": ("pow(10000.0,", "pow(1000.0,"),
+    "pe_offset_ignored": ("const double pos = (double)pos0 + (double)s;", "const double pos = (double)s;"),
     "qkv_dropped_last_term": ("for (long e = 0; e < E; ++e) acc += xrow[e] * wrow[e];",
                               "for (long e = 0; e + 1 < E; ++e) acc += xrow[e] * wrow[e];"),
 }
@@ -71,6 +75,9 @@ PINS = [
     pins.test_key_mask_with_equal_keys_gives_means_of_the_visible_values,
     pins.test_qkv_proj_matches_numpy_matmul_float64,
     pins.test_qkv_proj_identity_and_permutation_weights_are_exact,
+    pins.test_pe_position_zero_and_first_pair,
+    pins.test_pe_frequencies_and_unit_pairs,
+    pins.test_pe_offset_rows_are_the_later_rows,
 ]
 
 
