@@ -271,7 +271,7 @@ def main() -> int:
                              "flop_per_launch": flop, "mean_launch_us": round(mean * 1e3, 2),
                              "median_launch_us": round(statistics.median(ms) * 1e3, 2)}}
 
-    kv = f16 = kp = qp = None
+    kv = f16 = kp = qp = pe_leg = None
     if not args.skip_extras:
         kc_cfg = workloads.BF16_KVCACHE
         log("KV-cache prefill: generating inputs")
@@ -324,6 +324,21 @@ def main() -> int:
                       f"bf16 Q/K/V projection M={qc.B * qc.S} E={qc.E} N=3x{qc.H * qc.D} (seed {qc.seed}); "
                       f"cold, 20 calls")
         del xq, wq, outs
+
+        # the sinusoidal position-encoding table (fp32, HBM-bound: one write)
+        log("position encoding table")
+        pe_t = torch.empty(workloads.PE_S, workloads.PE_D, dtype=torch.float32, device=dev)
+        pe_ms = cold_ms(lambda: attn.sinusoidal_pe(workloads.PE_S, workloads.PE_D, 0, out=pe_t))
+        pe_mean = statistics.fmean(pe_ms)
+        pe_bytes = workloads.PE_S * workloads.PE_D * 4
+        pe_gbs = pe_bytes / (pe_mean * 1e-3) / 1e9
+        pe_leg = {"value": round(pe_gbs, 1), "unit": "GB/s",
+                  "workload": f"fp32 sinusoidal position table S={workloads.PE_S} d_model={workloads.PE_D}; "
+                              f"cold, 20 calls",
+                  "roofline": {"bound": "hbm", "achieved": round(pe_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": round(pe_gbs / HBM_PEAK_GBS, 4), "bytes_per_call": pe_bytes,
+                               "mean_launch_us": round(pe_mean * 1e3, 2)}}
+        del pe_t
 
     if args.copy_calibration:
         n = args.copy_calibration << 20
@@ -407,6 +422,7 @@ def main() -> int:
         "fp16_prefill": f16,
         "keypad_prefill": kp,
         "qkv_proj": qp,
+        "position_encoding": pe_leg,
         "cpu_baseline": cpu,
         "parity": parity,
     }

@@ -63,6 +63,8 @@ def _load() -> ctypes.CDLL:
     lib.attn_fwd_mask.restype = i
     lib.attn_qkv_proj.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i]
     lib.attn_qkv_proj.restype = i
+    lib.attn_sinusoidal_pe.argtypes = [vp, i, i, i]
+    lib.attn_sinusoidal_pe.restype = i
     lib.attn_set_stream.argtypes = [vp]
     lib.attn_set_stream.restype = i
     lib.attn_set_timing_events.argtypes = [vp, vp]
@@ -257,6 +259,20 @@ def qkv_proj(x: torch.Tensor, w: torch.Tensor, H: int, D: int, q: torch.Tensor |
     return tuple(outs)
 
 
+def sinusoidal_pe(S: int, d_model: int, pos0: int = 0, out: torch.Tensor | None = None,
+                  device: torch.device | str = "cuda") -> torch.Tensor:
+    """[S, d_model] float32 position encoding for positions pos0 .. pos0+S-1, on the GPU."""
+    if out is None:
+        out = torch.empty(S, d_model, dtype=torch.float32, device=device)
+    else:
+        _dev_tensor("out", out, 2)
+        if tuple(out.shape) != (S, d_model) or out.dtype != torch.float32:
+            raise ValueError(f"out must be float32 [{S}, {d_model}]")
+    _set_stream(out.device)
+    _check(load().attn_sinusoidal_pe(out.data_ptr(), S, d_model, pos0))
+    return out
+
+
 def attn_decode_workspace_bytes(B: int, H: int, S_cap: int, D: int) -> int:
     return int(load().attn_decode_workspace_bytes(B, H, S_cap, D))
 
@@ -305,6 +321,6 @@ def attn_decode_plan(B: int, H: int, S_cap: int, D: int, dtype: int) -> DecodePl
     return plan
 
 
-__all__ = ["attn_fwd", "attn_fwd_kvcache", "attn_fwd_mask", "attn_decode", "qkv_proj", "attn_decode_workspace_bytes", "attn_fwd_plan", "attn_decode_plan",
+__all__ = ["attn_fwd", "attn_fwd_kvcache", "attn_fwd_mask", "attn_decode", "qkv_proj", "sinusoidal_pe", "attn_decode_workspace_bytes", "attn_fwd_plan", "attn_decode_plan",
            "attn_set_timing_events",
            "AttnError", "ATTN_F32", "ATTN_BF16", "ATTN_F16", "lib", "LIB_PATH"]

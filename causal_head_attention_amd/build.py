@@ -26,6 +26,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "fwd_row.hip"),
     os.path.join(CSRC, "kernels", "decode.hip"),
     os.path.join(CSRC, "kernels", "qkv_proj.hip"),
+    os.path.join(CSRC, "kernels", "pe.hip"),
 ]
 
 ARCH = "gfx950"

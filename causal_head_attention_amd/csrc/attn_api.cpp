@@ -315,6 +315,27 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
     return ok();
 }
 
+int attn_sinusoidal_pe(float* pe, int S, int d_model, int pos0) {
+    hipEvent_t ev_start, ev_stop;
+    take_events(ev_start, ev_stop);
+    if (S < 0 || d_model <= 0 || pos0 < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_sinusoidal_pe: sizes must be S >= 0, d_model >= 1, pos0 >= 0");
+    if (d_model & 1)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_sinusoidal_pe: d_model must be even (sine and cosine pairs)");
+    if ((long long)pos0 + S - 1 > 0x7fffffffLL)   // the last position, pos0 + S - 1, is an int
+        return fail(ATTN_ERR_INVALID_ARG, "attn_sinusoidal_pe: positions pos0 + S exceed 2^31 - 1");
+    if (tensor_bytes(S, d_model, 1, 1, 4) < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_sinusoidal_pe: size overflows");
+    if (S == 0) return ok();
+    if (!pe) return fail(ATTN_ERR_INVALID_ARG, "attn_sinusoidal_pe: NULL output pointer");
+    if ((reinterpret_cast<uintptr_t>(pe) & 7u) != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_sinusoidal_pe: output must be 8-byte aligned");
+    const hipError_t e = attn::launch_sinusoidal_pe(pe, S, d_model, pos0, ev_start, ev_stop, t_stream);
+    if (e != hipSuccess)
+        return fail(ATTN_ERR_HIP, std::string("attn_sinusoidal_pe: launch failed: ") + hipGetErrorString(e));
+    return ok();
+}
+
 int attn_qkv_proj(const void* x, const void* w, void* q, void* k, void* v, int M, int E, int H, int D, int dtype) {
     hipEvent_t ev_start, ev_stop;
     take_events(ev_start, ev_stop);

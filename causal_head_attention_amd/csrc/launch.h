@@ -64,5 +64,8 @@ hipError_t launch_fwd_row(const FwdArgs& a, Elt t, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, Elt t, hipStream_t stream);
 // Q/K/V projection GEMM, 16-bit storage.
 hipError_t launch_qkv_proj(const QkvArgs& a, Elt t, hipStream_t stream);
+// Sinusoidal position encoding table, fp32 [S, d_model].
+hipError_t launch_sinusoidal_pe(float* pe, int S, int d_model, int pos0, hipEvent_t ev_start, hipEvent_t ev_stop,
+                                hipStream_t stream);
 
 }  // namespace attn

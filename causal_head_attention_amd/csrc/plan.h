@@ -138,6 +138,12 @@ constexpr int kGemmBN = 192;
 constexpr int kGemmBK = 64;
 constexpr int kGemmThreads = 512;
 
+// Sinusoidal position encoding: 256 threads over the frequency pairs, 4
+// positions per workgroup (a 4096-position table is 1,024 workgroups: 16
+// positions each left one wave per SIMD and the sin/cos latency exposed).
+constexpr int kPeThreads = 256;
+constexpr int kPeRows = 4;
+
 ATTN_HD inline long long qkv_grid(int M, int N) {
     return (long long)((M + kGemmBM - 1) / kGemmBM) * ((3LL * N + kGemmBN - 1) / kGemmBN);
 }

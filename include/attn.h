@@ -193,6 +193,21 @@ int attn_qkv_proj(const void* x, const void* w, void* q, void* k, void* v, int M
                   int dtype);
 
 /*
+ * attn_sinusoidal_pe -- the sinusoidal position encoding table ("Week-4 CUDA
+ * notes" page, section 2.3): pe[s][2i] = sin(pos / 10000^(2i/d_model)),
+ * pe[s][2i+1] = cos(pos / 10000^(2i/d_model)), pos = pos0 + s.
+ *
+ *   pe      : DEVICE float [S, d_model], 8-byte aligned (fp32, as the page
+ *             requires: fp16 cannot hold the small frequencies)
+ *   d_model : even, >= 2 (else ATTN_ERR_INVALID_ARG)
+ *   pos0    : first position (>= 0); the last, pos0 + S - 1, must be <= 2^31 - 1
+ * The angle is formed and reduced modulo 2*pi in fp64, so every element is
+ * within a few fp32 ulp of the exact value at any position. S == 0 is a
+ * valid empty call.
+ */
+int attn_sinusoidal_pe(float* pe, int S, int d_model, int pos0);
+
+/*
  * attn_set_stream -- set the HIP stream (a hipStream_t passed as void*) that
  * later calls from THIS thread enqueue on; NULL selects the null stream.
  * attn_get_stream returns the current thread's stream.

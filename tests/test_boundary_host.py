@@ -211,6 +211,23 @@ def test_qkv_empty_call():
     assert qkv(x=0, w=0, q=0, k=0, v=0, M=0) == attn.ATTN_OK
 
 
+@pytest.mark.parametrize("args,needle", [
+    ((A, 10, 63, 0), "even"),
+    ((A, -1, 64, 0), "sizes"),
+    ((A, 10, 64, -1), "sizes"),
+    ((A, 10, 64, (1 << 31) - 5), "2^31"),
+    ((0, 10, 64, 0), "NULL"),
+    ((A + 4, 10, 64, 0), "aligned"),
+])
+def test_pe_rejections(args, needle):
+    assert L.attn_sinusoidal_pe(*args) == attn.ATTN_ERR_INVALID_ARG
+    assert needle in attn.load().attn_last_error().decode()
+
+
+def test_pe_empty_call():
+    assert L.attn_sinusoidal_pe(0, 0, 64, 0) == attn.ATTN_OK
+
+
 def test_binding_rejects_host_tensors():
     q = torch.zeros(1, 4, 1, 32)
     with pytest.raises(ValueError):

@@ -493,6 +493,38 @@ def test_qkv_proj_full_size_sampled_rows(attn):
 
 
 # ---------------------------------------------------------------------------
+# Sinusoidal position encoding (attn_sinusoidal_pe)
+# Bar: fp32 sin/cos of an angle reduced to [-pi, pi] in fp64 are within
+# about 1 ulp (1.2e-7) plus the rounding of the reduced angle to fp32 (up to
+# 1.9e-7 rad); the fp64 angle itself (in the kernel and in the oracle) is off
+# by up to about 1.1e-16 * pos rad. So: 3e-7 + 2.5e-16 * largest position.
+# ---------------------------------------------------------------------------
+PE_CASES = [  # (S, d_model, pos0)
+    (1, 2, 0),
+    (37, 64, 0),
+    (300, 4096, 0),          # the model width of the bf16_s2048 layer
+    (17, 128, 100_000),      # an offset block of positions (decode steps)
+    (6, 8, (1 << 31) - 6),   # the largest positions the interface allows
+]
+
+
+@pytest.mark.parametrize("case", PE_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_sinusoidal_pe_against_oracle(attn, case):
+    S, d, pos0 = case
+    say(f"pe {case}")
+    pe = attn.sinusoidal_pe(S, d, pos0).cpu().double().numpy()
+    ref = oracle.sinusoidal_pe(S, d, pos0)
+    bar = 3e-7 + 2.5e-16 * (pos0 + S)
+    err = float(np.abs(pe - ref).max())
+    assert err <= bar, f"pe {case}: max abs err {err:.3e} > {bar:.3e}"
+
+
+def test_sinusoidal_pe_position_zero_is_exact(attn):
+    pe = attn.sinusoidal_pe(1, 512).cpu()
+    assert torch.all(pe[0, 0::2] == 0.0) and torch.all(pe[0, 1::2] == 1.0)
+
+
+# ---------------------------------------------------------------------------
 # Error paths through the binding on a live device
 # ---------------------------------------------------------------------------
 def test_error_paths_on_device(attn):

@@ -169,6 +169,10 @@ class QkvProj:
 
 BF16_QKV = QkvProj("bf16_qkv", torch.bfloat16, 1, 2048, 4096, 32, 128, 1009)
 
+# Position-encoding table of the bf16_s2048 layer's width, for 4096 positions
+# (no random draw: the table is a function of its sizes).
+PE_S, PE_D = 4096, 4096
+
 PREFILL_CONFIGS = (FP32_TINY, FP32_SMALL, BF16_S2048, BF16_S4096)
 
 
