@@ -63,6 +63,8 @@ def _load():
             lib.oracle_qkv_proj_f64.restype = ctypes.c_int
             lib.oracle_sinusoidal_pe_f64.argtypes = [dp] + [ctypes.c_int] * 3
             lib.oracle_sinusoidal_pe_f64.restype = ctypes.c_int
+            lib.oracle_masked_softmax_f64.argtypes = [dp, dp] + [ctypes.c_int] * 4 + [ctypes.c_double, ctypes.c_int]
+            lib.oracle_masked_softmax_f64.restype = ctypes.c_int
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
             _lib = lib
@@ -207,6 +209,18 @@ def sinusoidal_pe(S: int, d_model: int, pos0: int = 0):
     if rc != 0:
         raise ValueError(f"oracle_sinusoidal_pe_f64 rejected the arguments (code {rc})")
     return pe
+
+
+def masked_softmax(s, scale: float = 1.0, causal: bool = True):
+    """Row softmax of scale * s [B, H, S_q, S_kv] under the causal rule (bottom-right);
+    masked entries 0, rows with no visible key 0. fp64 numpy."""
+    s = _f64(s)
+    B, H, S_q, S_kv = s.shape
+    p = np.zeros_like(s)
+    rc = _load().oracle_masked_softmax_f64(_ptr(s), _ptr(p), B, H, S_q, S_kv, float(scale), int(bool(causal)))
+    if rc != 0:
+        raise ValueError(f"oracle_masked_softmax_f64 rejected the arguments (code {rc})")
+    return p
 
 
 def num_threads() -> int:

@@ -310,6 +310,46 @@ int oracle_sinusoidal_pe_f64(double* pe, int S, int d_model, int pos0) {
     return ORACLE_OK;
 }
 
+/*
+ * Row softmax of a score matrix under the causal rule, the stage the MMHA
+ * page's section 1 describes on its own (a generic softmax would process
+ * the masked upper triangle too), with the masked positions set to -inf
+ * before it ("Week-4 CUDA notes" page, section 2.2):
+ *   s, p : [B, H, S_q, S_kv] row-major; row i of a (b, h) sees keys
+ *          j <= i + S_kv - S_q when causal, all keys otherwise
+ *   p[i][j] = exp(scale*s[i][j] - m_i) / sum_j' exp(scale*s[i][j'] - m_i)
+ *   over the visible j (m_i their maximum), 0 where masked; a row with no
+ *   visible key is all zeros. Masked scores are never read.
+ */
+int oracle_masked_softmax_f64(const double* s, double* p, int B, int H, int S_q, int S_kv, double scale, int causal) {
+    if (B <= 0 || H <= 0 || S_q <= 0 || S_kv <= 0) return ORACLE_EINVAL;
+    if (causal != 0 && causal != 1) return ORACLE_EINVAL;
+    const long rows = (long)B * H * S_q;
+    const long off = (long)S_kv - S_q;
+    long r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < rows; ++r) {
+        const long i = r % S_q;
+        const double* srow = s + (size_t)r * (size_t)S_kv;
+        double* prow = p + (size_t)r * (size_t)S_kv;
+        long n = causal ? i + off + 1 : S_kv;   /* visible keys 0 .. n-1 */
+        if (n > S_kv) n = S_kv;
+        if (n < 0) n = 0;
+        for (long j = 0; j < S_kv; ++j) prow[j] = 0.0;
+        if (n == 0) continue;
+        double m = -INFINITY;
+        for (long j = 0; j < n; ++j)
+            if (scale * srow[j] > m) m = scale * srow[j];
+        double l = 0.0;
+        for (long j = 0; j < n; ++j) {
+            prow[j] = exp(scale * srow[j] - m);
+            l += prow[j];
+        }
+        for (long j = 0; j < n; ++j) prow[j] = prow[j] / l;
+    }
+    return ORACLE_OK;
+}
+
 /* Threads the OpenMP runtime will use for the passes above (1 without OpenMP). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

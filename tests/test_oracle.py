@@ -547,6 +547,47 @@ def test_pe_offset_rows_are_the_later_rows():
     assert np.array_equal(oracle.sinusoidal_pe(20, 32, pos0=30), full[30:])
 
 
+# ---------------------------------------------------------------------------
+# Standalone masked softmax (MMHA page, section 1; Week-4 notes, section 2.2)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("S_q,S_kv,causal", [(19, 19, True), (7, 30, True), (12, 9, False)])
+def test_masked_softmax_matches_torch_softmax_float64(S_q, S_kv, causal):
+    B, H, scale = 2, 3, 0.37
+    s = rnd(291, B, H, S_q, S_kv, std=3.0)
+    p = oracle.masked_softmax(s, scale, causal)
+    t = torch.from_numpy(s) * scale
+    if causal:
+        i = torch.arange(S_q)[:, None]
+        j = torch.arange(S_kv)[None, :]
+        t = t.masked_fill(j > i + (S_kv - S_q), -math.inf)
+    ref = torch.softmax(t, dim=-1).numpy()
+    assert np.max(np.abs(p - ref)) <= 1e-15
+
+
+def test_masked_softmax_is_the_attention_probabilities():
+    """The probabilities the attention oracle forms from Q K^T / sqrt(D) are the
+    masked softmax of those scores (scores from a float64 numpy matmul)."""
+    B, S, H, D = 2, 23, 2, 16
+    q, k, v = rnd(292, B, S, H, D), rnd(293, B, S, H, D), rnd(294, B, S, H, D)
+    _, P = oracle.attn_fwd(q, k, v, True, return_p=True)
+    scores = np.einsum("bihd,bjhd->bhij", q, k)
+    p = oracle.masked_softmax(scores, 1.0 / math.sqrt(D), True)
+    assert np.max(np.abs(p - P)) <= 1e-14
+
+
+def test_masked_softmax_ignores_masked_scores_and_row_shifts():
+    B, H, S = 1, 2, 11
+    s = rnd(295, B, H, S, S)
+    p = oracle.masked_softmax(s, 1.0, True)
+    t = s.copy()
+    t[..., np.triu_indices(S, 1)[0], np.triu_indices(S, 1)[1]] = np.nan   # masked scores are never read
+    t += 5.0                                                              # a constant per row changes nothing
+    q = oracle.masked_softmax(t, 1.0, True)
+    assert np.all(np.isfinite(q)) and np.max(np.abs(q - p)) <= 1e-15
+    assert np.all(p[..., np.triu_indices(S, 1)[0], np.triu_indices(S, 1)[1]] == 0.0)
+    assert np.max(np.abs(p.sum(-1) - 1.0)) <= 1e-15
+
+
 def test_rejects_invalid_arguments():
     q = rnd(1, 1, 4, 1, 8)
     with pytest.raises(ValueError):

@@ -49,6 +49,8 @@ MUTANTS = {
     "pe_exponent_over_i": ("(double)(2 * i) / (double)d_model", "(double)(i) / (double)d_model"),
     "pe_base_1000": ("pow(10000.0,", "pow(1000.0,"),
     "pe_offset_ignored": ("const double pos = (double)pos0 + (double)s;", "const double pos = (double)s;"),
+    "softmax_mask_off_by_one": ("long n = causal ? i + off + 1 : S_kv;", "long n = causal ? i + off : S_kv;"),
+    "softmax_scale_after_max": ("prow[j] = exp(scale * srow[j] - m);", "prow[j] = exp(srow[j] - m);"),
     "qkv_dropped_last_term": ("for (long e = 0; e < E; ++e) acc += xrow[e] * wrow[e];",
                               "for (long e = 0; e + 1 < E; ++e) acc += xrow[e] * wrow[e];"),
 }
@@ -78,7 +80,21 @@ PINS = [
     pins.test_pe_position_zero_and_first_pair,
     pins.test_pe_frequencies_and_unit_pairs,
     pins.test_pe_offset_rows_are_the_later_rows,
+    lambda: pins.test_masked_softmax_matches_torch_softmax_float64(7, 30, True),
+    pins.test_masked_softmax_is_the_attention_probabilities,
 ]
+
+
+ORACLE_FUNCTIONS = ("oracle_attn_fwd_f64", "oracle_attn_decode_f64", "oracle_attn_fwd_kvcache_f64",
+                    "oracle_attn_fwd_mask_f64", "oracle_qkv_proj_f64", "oracle_sinusoidal_pe_f64",
+                    "oracle_masked_softmax_f64", "oracle_num_threads")
+
+
+def test_every_exported_oracle_function_is_listed():
+    import re
+    text = open(SRC).read()
+    exported = set(re.findall(r"^int (oracle_\w+)\(", text, re.M))
+    assert exported == set(ORACLE_FUNCTIONS)
 
 
 def _compile(tmp_path, name, old, new):
@@ -112,7 +128,8 @@ def test_mutant_is_caught(name, tmp_path, monkeypatch):
     real = oracle._load()
     path = _compile(tmp_path, name, *MUTANTS[name])
     mutant = ctypes.CDLL(path)
-    for fn in ("oracle_attn_fwd_f64", "oracle_attn_decode_f64", "oracle_num_threads"):
+    # every function of the oracle: same argument and result types
+    for fn in ORACLE_FUNCTIONS:
         f, g = getattr(mutant, fn), getattr(real, fn)
         f.argtypes, f.restype = g.argtypes, g.restype
     monkeypatch.setattr(oracle, "_lib", mutant)
