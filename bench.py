@@ -271,7 +271,7 @@ def main() -> int:
                              "flop_per_launch": flop, "mean_launch_us": round(mean * 1e3, 2),
                              "median_launch_us": round(statistics.median(ms) * 1e3, 2)}}
 
-    kv = f16 = kp = qp = pe_leg = None
+    kv = f16 = kp = qp = pe_leg = sm_leg = None
     if not args.skip_extras:
         kc_cfg = workloads.BF16_KVCACHE
         log("KV-cache prefill: generating inputs")
@@ -339,6 +339,24 @@ def main() -> int:
                                "frac": round(pe_gbs / HBM_PEAK_GBS, 4), "bytes_per_call": pe_bytes,
                                "mean_launch_us": round(pe_mean * 1e3, 2)}}
         del pe_t
+
+        # the standalone masked softmax over the bf16_s2048 layer's score
+        # matrix (HBM-bound: visible scores read once, all of P written once)
+        sc = workloads.BF16_SOFTMAX
+        log("masked softmax")
+        s_sm = workloads.make_scores(sc).to(dev)
+        p_sm = torch.empty_like(s_sm)
+        sm_ms = cold_ms(lambda: attn.masked_softmax(s_sm, sc.scale, sc.causal, out=p_sm))
+        sm_mean = statistics.fmean(sm_ms)
+        sm_bytes = sc.algorithmic_bytes()
+        sm_gbs = sm_bytes / (sm_mean * 1e-3) / 1e9
+        sm_leg = {"value": round(sm_gbs, 1), "unit": "GB/s",
+                  "workload": f"bf16 causal score matrix [{sc.B}, {sc.H}, {sc.S_q}, {sc.S_kv}] ~ N(0, 128), "
+                              f"scale 1/sqrt(128) (seed {sc.seed}); cold, 20 calls",
+                  "roofline": {"bound": "hbm", "achieved": round(sm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": round(sm_gbs / HBM_PEAK_GBS, 4), "bytes_per_call": sm_bytes,
+                               "mean_launch_us": round(sm_mean * 1e3, 2)}}
+        del s_sm, p_sm
 
     if args.copy_calibration:
         n = args.copy_calibration << 20
@@ -423,6 +441,7 @@ def main() -> int:
         "keypad_prefill": kp,
         "qkv_proj": qp,
         "position_encoding": pe_leg,
+        "masked_softmax": sm_leg,
         "cpu_baseline": cpu,
         "parity": parity,
     }

@@ -64,6 +64,8 @@ def _load() -> ctypes.CDLL:
     lib.attn_qkv_proj.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i]
     lib.attn_qkv_proj.restype = i
     lib.attn_sinusoidal_pe.argtypes = [vp, i, i, i]
+    lib.attn_masked_softmax.argtypes = [vp, vp, i, i, i, i, ctypes.c_float, i, i]
+    lib.attn_masked_softmax.restype = i
     lib.attn_sinusoidal_pe.restype = i
     lib.attn_set_stream.argtypes = [vp]
     lib.attn_set_stream.restype = i
@@ -273,6 +275,24 @@ def sinusoidal_pe(S: int, d_model: int, pos0: int = 0, out: torch.Tensor | None 
     return out
 
 
+def masked_softmax(s: torch.Tensor, scale: float = 1.0, causal: bool = True,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """Row softmax of scale * s [B,H,S_q,S_kv] under the causal rule (bottom-right); masked
+    entries 0. out may be s itself (in place). float32, bfloat16 or float16."""
+    _dev_tensor("s", s, 4)
+    if out is None:
+        out = torch.empty_like(s)
+    else:
+        _dev_tensor("out", out, 4)
+        if tuple(out.shape) != tuple(s.shape) or out.dtype != s.dtype:
+            raise ValueError(f"out must be {tuple(s.shape)} of dtype {s.dtype}")
+    B, H, S_q, S_kv = s.shape
+    _set_stream(s.device)
+    _check(load().attn_masked_softmax(s.data_ptr(), out.data_ptr(), B, H, S_q, S_kv, float(scale), int(bool(causal)),
+                                      _dtype_code(s)))
+    return out
+
+
 def attn_decode_workspace_bytes(B: int, H: int, S_cap: int, D: int) -> int:
     return int(load().attn_decode_workspace_bytes(B, H, S_cap, D))
 
@@ -321,6 +341,6 @@ def attn_decode_plan(B: int, H: int, S_cap: int, D: int, dtype: int) -> DecodePl
     return plan
 
 
-__all__ = ["attn_fwd", "attn_fwd_kvcache", "attn_fwd_mask", "attn_decode", "qkv_proj", "sinusoidal_pe", "attn_decode_workspace_bytes", "attn_fwd_plan", "attn_decode_plan",
+__all__ = ["attn_fwd", "attn_fwd_kvcache", "attn_fwd_mask", "attn_decode", "qkv_proj", "sinusoidal_pe", "masked_softmax", "attn_decode_workspace_bytes", "attn_fwd_plan", "attn_decode_plan",
            "attn_set_timing_events",
            "AttnError", "ATTN_F32", "ATTN_BF16", "ATTN_F16", "lib", "LIB_PATH"]

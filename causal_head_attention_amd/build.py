@@ -27,6 +27,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "decode.hip"),
     os.path.join(CSRC, "kernels", "qkv_proj.hip"),
     os.path.join(CSRC, "kernels", "pe.hip"),
+    os.path.join(CSRC, "kernels", "softmax.hip"),
 ]
 
 ARCH = "gfx950"

@@ -336,6 +336,43 @@ int attn_sinusoidal_pe(float* pe, int S, int d_model, int pos0) {
     return ok();
 }
 
+int attn_masked_softmax(const void* s, void* p, int B, int H, int S_q, int S_kv, float scale, int causal,
+                        int dtype) {
+    hipEvent_t ev_start, ev_stop;
+    take_events(ev_start, ev_stop);
+    if (B < 0 || H < 0 || S_q < 0 || S_kv < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_masked_softmax: negative size");
+    if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "attn_masked_softmax: causal must be 0 or 1");
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "attn_masked_softmax: scale must be finite");
+    if (!dtype_built(dtype))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_masked_softmax: dtype " + std::to_string(dtype) +
+                                              " not built (ATTN_F32=0, ATTN_BF16=1, ATTN_F16=2)");
+    const int es = elem_size(dtype);
+    const long long row_bytes = (long long)S_kv * es;
+    if (row_bytes > attn::kSmMaxRowBytes)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_masked_softmax: a row of S_kv=" + std::to_string(S_kv) +
+                                              " scores exceeds " + std::to_string(attn::kSmMaxRowBytes) + " bytes");
+    if (row_bytes % 16 != 0)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_masked_softmax: a row must be a whole number of 16-byte chunks "
+                                          "(S_kv a multiple of 4 for fp32, of 8 for 16-bit types)");
+    const long long n = tensor_bytes(B, H, S_q, S_kv, es);
+    if (n < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_masked_softmax: tensor size overflows");
+    const long long rows = (long long)B * H * S_q;
+    if ((rows + attn::kSmRowsPerBlock - 1) / attn::kSmRowsPerBlock * attn::kSmThreads > 0xffffffffLL)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_masked_softmax: B*H*S_q rows exceed the launch grid");
+    if (n == 0) return ok();
+    if (!s || !p) return fail(ATTN_ERR_INVALID_ARG, "attn_masked_softmax: NULL tensor pointer");
+    if (!aligned16(s) || !aligned16(p))
+        return fail(ATTN_ERR_INVALID_ARG, "attn_masked_softmax: tensor pointers must be 16-byte aligned");
+    if (s != p && overlap(s, n, p, n))
+        return fail(ATTN_ERR_INVALID_ARG, "attn_masked_softmax: p overlaps s without being s itself");
+    attn::SoftmaxArgs a{s, p, B, H, S_q, S_kv, causal, (float)((double)scale * 1.4426950408889634), ev_start, ev_stop};
+    const hipError_t e = attn::launch_masked_softmax(a, elt_of(dtype), t_stream);
+    if (e != hipSuccess)
+        return fail(ATTN_ERR_HIP, std::string("attn_masked_softmax: launch failed: ") + hipGetErrorString(e));
+    return ok();
+}
+
 int attn_qkv_proj(const void* x, const void* w, void* q, void* k, void* v, int M, int E, int H, int D, int dtype) {
     hipEvent_t ev_start, ev_stop;
     take_events(ev_start, ev_stop);

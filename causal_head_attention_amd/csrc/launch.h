@@ -56,6 +56,16 @@ struct QkvArgs {
     hipEvent_t ev_stop;
 };
 
+struct SoftmaxArgs {
+    const void* s;   // [B, H, S_q, S_kv] scores
+    void* p;         // same shape; may be s itself
+    int B, H, S_q, S_kv;
+    int causal;
+    float scale_log2;   // scale * log2(e), fp32
+    hipEvent_t ev_start;
+    hipEvent_t ev_stop;
+};
+
 // MFMA tile kernel for 16-bit storage (BF16 or F16); D in {32, 64, 128}.
 hipError_t launch_fwd_tile(const FwdArgs& a, Elt t, hipStream_t stream);
 // Row kernel: one wave per query row, any storage type.
@@ -64,6 +74,8 @@ hipError_t launch_fwd_row(const FwdArgs& a, Elt t, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, Elt t, hipStream_t stream);
 // Q/K/V projection GEMM, 16-bit storage.
 hipError_t launch_qkv_proj(const QkvArgs& a, Elt t, hipStream_t stream);
+// Row softmax of scale * s under the causal rule, any storage type.
+hipError_t launch_masked_softmax(const SoftmaxArgs& a, Elt t, hipStream_t stream);
 // Sinusoidal position encoding table, fp32 [S, d_model].
 hipError_t launch_sinusoidal_pe(float* pe, int S, int d_model, int pos0, hipEvent_t ev_start, hipEvent_t ev_stop,
                                 hipStream_t stream);

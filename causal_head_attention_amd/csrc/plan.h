@@ -144,6 +144,17 @@ constexpr int kGemmThreads = 512;
 constexpr int kPeThreads = 256;
 constexpr int kPeRows = 4;
 
+// Masked softmax: one wave per row, kSmRowsPerBlock rows per workgroup. A
+// lane holds up to kSmChunksMax 16-byte chunks of its row in registers, so a
+// row is at most 64 * 16 * kSmChunksMax bytes (4096 fp32 or 8192 16-bit
+// scores); rows of at most 64 * 16 * kSmChunksSmall bytes use a variant with
+// fewer registers and more waves in flight.
+constexpr int kSmRowsPerBlock = 4;
+constexpr int kSmThreads = kSmRowsPerBlock * 64;
+constexpr int kSmChunksSmall = 4;
+constexpr int kSmChunksMax = 16;
+constexpr long long kSmMaxRowBytes = 64LL * 16 * kSmChunksMax;
+
 ATTN_HD inline long long qkv_grid(int M, int N) {
     return (long long)((M + kGemmBM - 1) / kGemmBM) * ((3LL * N + kGemmBN - 1) / kGemmBN);
 }

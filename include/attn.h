@@ -193,6 +193,35 @@ int attn_qkv_proj(const void* x, const void* w, void* q, void* k, void* v, int M
                   int dtype);
 
 /*
+ * attn_masked_softmax -- row softmax of a materialised score matrix under
+ * the causal rule, the stage the MMHA page's section 1 describes on its
+ * own, with the masked positions at -inf ("Week-4 CUDA notes" page,
+ * section 2.2):
+ *
+ *     p[i][j] = exp(scale*s[i][j] - m_i) / sum_j' exp(scale*s[i][j'] - m_i)
+ *
+ * over the keys j that row i sees (m_i their maximum) and 0 elsewhere.
+ *
+ *   s, p   : DEVICE [B, H, S_q, S_kv], row-major, of the storage type dtype
+ *            (ATTN_F32, ATTN_BF16 or ATTN_F16); p may be s itself (in place)
+ *            but may not overlap it otherwise
+ *   scale  : finite fp32 factor applied to every score (1/sqrt(D) for
+ *            attention scores)
+ *   causal : 1: row i sees keys j <= i + S_kv - S_q (the bottom-right rule of
+ *            the other entry points; with S_q > S_kv the first S_q - S_kv rows
+ *            see no key), 0: every row sees all S_kv keys
+ * A row with no visible key is all zeros. Masked scores are never used, so
+ * they may hold anything (NaN included); beyond the 16-byte chunk that holds
+ * a row's last visible score they are not even read. Arithmetic is fp32; p is rounded to
+ * the storage type. A row must be a whole number of 16-byte chunks and at
+ * most 16 KiB (S_kv a multiple of 4 and <= 4096 for fp32, a multiple of 8
+ * and <= 8192 for 16-bit types), else ATTN_ERR_UNSUPPORTED. An empty tensor
+ * is a valid empty call.
+ */
+int attn_masked_softmax(const void* s, void* p, int B, int H, int S_q, int S_kv, float scale, int causal,
+                        int dtype);
+
+/*
  * attn_sinusoidal_pe -- the sinusoidal position encoding table ("Week-4 CUDA
  * notes" page, section 2.3): pe[s][2i] = sin(pos / 10000^(2i/d_model)),
  * pe[s][2i+1] = cos(pos / 10000^(2i/d_model)), pos = pos0 + s.

@@ -228,6 +228,35 @@ def test_pe_empty_call():
     assert L.attn_sinusoidal_pe(0, 0, 64, 0) == attn.ATTN_OK
 
 
+def sm(s=A, p=A + 0x4000000, B=1, H=2, S_q=64, S_kv=64, scale=0.125, causal=1, dtype=attn.ATTN_BF16):
+    return L.attn_masked_softmax(s, p, B, H, S_q, S_kv, scale, causal, dtype)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=3), attn.ATTN_ERR_UNSUPPORTED, "dtype"),
+    (dict(S_kv=8200), attn.ATTN_ERR_UNSUPPORTED, "exceeds"),
+    (dict(S_kv=4100, dtype=attn.ATTN_F32), attn.ATTN_ERR_UNSUPPORTED, "exceeds"),
+    (dict(S_kv=12), attn.ATTN_ERR_UNSUPPORTED, "16-byte"),
+    (dict(S_kv=6, dtype=attn.ATTN_F32), attn.ATTN_ERR_UNSUPPORTED, "16-byte"),
+    (dict(causal=2), attn.ATTN_ERR_INVALID_ARG, "causal"),
+    (dict(scale=float("inf")), attn.ATTN_ERR_INVALID_ARG, "finite"),
+    (dict(scale=float("nan")), attn.ATTN_ERR_INVALID_ARG, "finite"),
+    (dict(B=-1), attn.ATTN_ERR_INVALID_ARG, "negative"),
+    (dict(s=0), attn.ATTN_ERR_INVALID_ARG, "NULL"),
+    (dict(p=A + 0x4000008), attn.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(p=A + 0x100), attn.ATTN_ERR_INVALID_ARG, "overlaps"),       # p inside s, not s itself
+    (dict(B=1 << 20, H=64, S_q=4, S_kv=8), attn.ATTN_ERR_UNSUPPORTED, "grid"),
+])
+def test_masked_softmax_rejections(kw, status, needle):
+    assert sm(**kw) == status, L.attn_last_error()
+    assert needle in attn.load().attn_last_error().decode()
+
+
+def test_masked_softmax_empty_calls():
+    assert sm(s=0, p=0, B=0) == attn.ATTN_OK
+    assert sm(s=0, p=0, S_kv=0) == attn.ATTN_OK
+
+
 def test_binding_rejects_host_tensors():
     q = torch.zeros(1, 4, 1, 32)
     with pytest.raises(ValueError):

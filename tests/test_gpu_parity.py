@@ -525,6 +525,95 @@ def test_sinusoidal_pe_position_zero_is_exact(attn):
 
 
 # ---------------------------------------------------------------------------
+# Standalone masked softmax (attn_masked_softmax)
+# Bars: the check() bars above; the probabilities lie in [0, 1], so the fp32
+# bar is loose (fp32 exp2 and one division give a few ulp) and the 16-bit bars
+# cover the output rounding (half an ulp of p <= 1). Masked entries must be 0
+# exactly, whatever the input holds there.
+# ---------------------------------------------------------------------------
+SM_CASES = [  # (B, H, S_q, S_kv, causal, scale, std)
+    (1, 1, 1, 8, True, 1.0, 1.0),               # one row, one chunk
+    (2, 3, 37, 64, True, 0.125, 8.0),           # S_q < S_kv; 222 rows: the last workgroup holds 2
+    (1, 2, 64, 64, False, 1.0, 1.0),
+    (1, 1, 100, 40, True, 0.5, 2.0),            # S_q > S_kv: the first 60 rows see no key
+    (1, 2, 300, 1024, True, 0.088, 11.3),       # 4 KiB fp32 rows: the largest small-register variant
+    (1, 1, 130, 2048, True, 0.088, 11.3),       # 4 KiB 16-bit rows / 8 KiB fp32 rows
+    (1, 1, 50, 2056, True, 1.0, 30.0),          # one chunk past 4 KiB (16-bit); logits to +-100
+    (1, 1, 64, "max", True, 0.088, 11.3),       # 16 KiB rows: the largest the interface takes
+    (1, 1, 19, "max", False, 0.088, 11.3),
+]
+
+
+def _sm_skv(S_kv, dtype):
+    return (16384 // torch.empty(0, dtype=dtype).element_size()) if S_kv == "max" else S_kv
+
+
+def _draw_scores(seed, dtype, B, H, S_q, S_kv, std):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(B, H, S_q, S_kv, generator=g) * std).to(dtype)
+
+
+def _visible(S_q, S_kv, causal):
+    i = torch.arange(S_q)[:, None]
+    j = torch.arange(S_kv)[None, :]
+    return (j <= i + (S_kv - S_q)) if causal else torch.ones(S_q, S_kv, dtype=torch.bool)
+
+
+@pytest.mark.parametrize("dtype", ALL_DTYPES, ids=DTYPE_IDS)
+@pytest.mark.parametrize("case", SM_CASES, ids=lambda c: "x".join(map(str, c[:5])))
+def test_masked_softmax_against_oracle(attn, case, dtype):
+    B, H, S_q, S_kv, causal, scale, std = case
+    S_kv = _sm_skv(S_kv, dtype)
+    say(f"masked softmax {(B, H, S_q, S_kv, causal)} {dtype}")
+    s = _draw_scores(1100 + S_q, dtype, B, H, S_q, S_kv, std)
+    p = attn.masked_softmax(s.cuda(), scale, causal).cpu()
+    ref = oracle.masked_softmax(s, scale, causal)
+    check(p, ref, dtype, f"softmax {case}")
+    vis = _visible(S_q, S_kv, causal).expand(B, H, S_q, S_kv)
+    assert torch.all(p[~vis] == 0), "masked entries must be exactly 0"
+    sums = p.double().sum(-1)
+    has = vis.any(-1)
+    tol = 1e-5 if dtype == torch.float32 else 2e-2
+    assert torch.all(sums[~has] == 0) and torch.allclose(sums[has], torch.ones_like(sums[has]), atol=tol)
+
+
+@pytest.mark.parametrize("dtype", ALL_DTYPES, ids=DTYPE_IDS)
+def test_masked_softmax_ignores_masked_inputs_and_runs_in_place(attn, dtype):
+    """NaN and +inf above the causal limit are never read; p may be s itself."""
+    B, H, S_q, S_kv = 2, 2, 48, 64
+    s = _draw_scores(1180, dtype, B, H, S_q, S_kv, 3.0)
+    ref = oracle.masked_softmax(s, 0.5, True)
+    vis = _visible(S_q, S_kv, True)
+    poisoned = s.clone()
+    poisoned[..., ~vis] = float("nan")
+    poisoned[..., 0, -1] = float("inf")
+    g = poisoned.cuda()
+    clean = attn.masked_softmax(s.cuda(), 0.5, True)
+    out = attn.masked_softmax(g, 0.5, True, out=g)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == g.data_ptr()
+    check(out, ref, dtype, "in place, poisoned")
+    assert torch.equal(out.cpu(), clean.cpu()), "the masked inputs changed the result"
+
+
+def test_masked_softmax_full_size_sampled_rows(attn):
+    """The bf16_softmax workload at full size, in the launch bench.py times.
+    Row i of a head depends only on its own visible scores, so the oracle
+    takes each sampled row alone as a one-query softmax over keys 0..i."""
+    cfg = workloads.BF16_SOFTMAX
+    say(f"masked softmax full size {cfg}")
+    s = workloads.make_scores(cfg)
+    p = attn.masked_softmax(s.cuda(), cfg.scale, cfg.causal)
+    torch.cuda.synchronize()
+    samples = [(0, 0), (0, 2047), (5, 1), (13, 640), (31, 2046), (31, 2047), (17, 1023), (22, 1024)]
+    p_rows = p[0, [h for h, _ in samples], [i for _, i in samples]].cpu()
+    for k, (h, i) in enumerate(samples):
+        ref = oracle.masked_softmax(s[0, h, i, : i + 1].reshape(1, 1, 1, i + 1), cfg.scale, True)
+        check(p_rows[k, : i + 1].reshape(1, 1, 1, i + 1), ref, torch.bfloat16, f"row ({h}, {i})")
+        assert torch.all(p_rows[k, i + 1:] == 0)
+
+
+# ---------------------------------------------------------------------------
 # Error paths through the binding on a live device
 # ---------------------------------------------------------------------------
 def test_error_paths_on_device(attn):

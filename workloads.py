@@ -31,8 +31,11 @@ The five workloads:
 * ``bf16_qkv``      bf16 Q/K/V projection of the bf16_s2048 layer: X [1, 2048,
                     4096] ~ N(0,1), stacked weights [3*32*128, 4096] ~ N(0,
                     1/4096) (unit-variance outputs), drawn x then w
+* ``bf16_softmax``  bf16 score matrix of the bf16_s2048 layer, [1, 32, 2048,
+                    2048], entries ~ N(0, 128) (the spread of q.k for unit
+                    q, k of length 128), scale 1/sqrt(128), causal
 
-Generator: a torch CPU ``Generator`` seeded with ``1000 + index`` (1001..1009).
+Generator: a torch CPU ``Generator`` seeded with ``1000 + index`` (1001..1010).
 Prefill draws q, k, v in that order as ``randn(B,S,H,D) * std``; decode,
 the KV-cache prefill and the key-padding forward draw the lengths first,
 then q, K and V. bf16 tensors are the
@@ -168,6 +171,38 @@ class QkvProj:
 
 
 BF16_QKV = QkvProj("bf16_qkv", torch.bfloat16, 1, 2048, 4096, 32, 128, 1009)
+
+@dataclass(frozen=True)
+class Scores:
+    """A materialised score matrix [B, H, S_q, S_kv] for the standalone softmax."""
+    name: str
+    dtype: torch.dtype
+    B: int
+    H: int
+    S_q: int
+    S_kv: int
+    causal: bool
+    seed: int
+    std: float
+    scale: float
+
+    def algorithmic_bytes(self) -> int:
+        """Visible scores read once, every probability (zeros included) written once."""
+        es = torch.empty(0, dtype=self.dtype).element_size()
+        rows = self.B * self.H
+        return es * rows * (visible_pairs(self.S_q, self.S_kv, self.causal) + self.S_q * self.S_kv)
+
+
+BF16_SOFTMAX = Scores("bf16_softmax", torch.bfloat16, 1, 32, 2048, 2048, True, 1010,
+                      std=128 ** 0.5, scale=128 ** -0.5)
+
+
+def make_scores(cfg: Scores) -> torch.Tensor:
+    """Draw s = randn(B, H, S_q, S_kv) * std on the CPU, cast to cfg.dtype."""
+    g = torch.Generator().manual_seed(cfg.seed)
+    s = torch.randn(cfg.B, cfg.H, cfg.S_q, cfg.S_kv, generator=g) * cfg.std
+    return s.to(cfg.dtype).contiguous()
+
 
 # Position-encoding table of the bf16_s2048 layer's width, for 4096 positions
 # (no random draw: the table is a function of its sizes).
