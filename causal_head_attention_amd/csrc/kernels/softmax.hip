@@ -12,8 +12,10 @@
 // and never used). One wave owns one row: lane t holds 16-byte chunks t,
 // t + 64, ... of the visible part in registers, the row maximum and the sum
 // of exponentials are reduced with cross-lane shuffles (no LDS, no barrier),
-// and the whole row is written back in 16-byte stores. The score matrix is
-// read once and the probabilities written once: the kernel is bound by HBM.
+// and the whole row is written back in 16-byte stores, the all-zero chunks
+// before the loads complete. The score matrix is read once and the
+// probabilities written once: the kernel is bound by HBM (a plain streaming
+// kernel with the same one-to-two read/write mix is the practical ceiling).
 #include <hip/hip_runtime.h>
 
 #include "../launch.h"
@@ -23,6 +25,8 @@ namespace attn {
 namespace {
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kNonTemporal = 2;   // buffer-load cache policy: nt
 
 template <typename T>
 struct Chunk;   // 16 bytes of T <-> floats
@@ -92,13 +96,25 @@ __global__ __launch_bounds__(kSmThreads) void masked_softmax_kernel(const T* s, 
         (void*)(p + (size_t)row * S_kv), (short)0, S_kv * (int)sizeof(T), 0x00020000);
     const int n_chunks = S_kv / E;   // the row is a whole number of chunks (host-checked)
 
+    // chunks past the last visible key hold zeros only: store them first,
+    // so these writes overlap the loads below
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+        const int c = lane + 64 * k;
+        if (c >= n_chunks) break;
+        if (c * E >= n) __builtin_amdgcn_raw_buffer_store_b128(zero, rp, c * 16, 0, 0);
+    }
+
+    // the scores are read once: non-temporal loads (cache policy nt) keep
+    // them from displacing the probabilities being written in L2
     float x[NC][E];
     float m = -INFINITY;
 #pragma unroll
     for (int k = 0; k < NC; ++k) {
         const int c = lane + 64 * k;
         u32x4_t raw = {0u, 0u, 0u, 0u};
-        if (c * E < n) raw = __builtin_amdgcn_raw_buffer_load_b128(rs, c * 16, 0, 0);
+        if (c * E < n) raw = __builtin_amdgcn_raw_buffer_load_b128(rs, c * 16, 0, kNonTemporal);
         C::unpack(raw, x[k]);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -125,6 +141,7 @@ __global__ __launch_bounds__(kSmThreads) void masked_softmax_kernel(const T* s, 
     for (int k = 0; k < NC; ++k) {
         const int c = lane + 64 * k;
         if (c >= n_chunks) break;
+        if (c * E >= n) continue;   // stored as zeros above
 #pragma unroll
         for (int e = 0; e < E; ++e) x[k][e] *= inv;
         __builtin_amdgcn_raw_buffer_store_b128(C::pack(x[k]), rp, c * 16, 0, 0);
