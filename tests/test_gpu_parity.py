@@ -266,6 +266,33 @@ def test_decode_balanced_segments(attn, case, dtype):
     assert torch.equal(o2.cpu(), oc)   # fixed merge order: the same bits every run
 
 
+def test_decode_workspace_reused_across_shapes_ignores_stale_contents(attn):
+    """One workspace buffer, sized for the largest call and filled with NaN
+    bytes first, serves calls of different shapes in turn: whatever an
+    earlier call (or the fill) left in it never reaches a result. Each
+    result matches the oracle and the rows of empty sequences are zero."""
+    shapes = [  # seed, B, H, S_cap, D, dtype, length range
+        (411, 16, 32, 300, 128, torch.bfloat16, (0, 300)),
+        (412, 5, 8, 64, 64, torch.float32, (-1, 64)),
+        (413, 300, 2, 8, 32, torch.float16, (0, 8)),
+        (414, 16, 32, 300, 128, torch.bfloat16, (200, 300)),
+    ]
+    need = max(attn.attn_decode_workspace_bytes(B, H, S, D) for _, B, H, S, D, _, _ in shapes)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    for seed, B, H, S_cap, D, dtype, (lo, hi) in shapes:
+        say(f"decode workspace reuse seed={seed} B={B} H={H} S_cap={S_cap} D={D} {dtype}")
+        g = torch.Generator().manual_seed(seed)
+        sl = torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int32)
+        q = torch.randn(B, 1, H, D, generator=g).to(dtype)
+        kc = torch.randn(B, S_cap, H, D, generator=g).to(dtype)
+        vc = torch.randn(B, S_cap, H, D, generator=g).to(dtype)
+        o = torch.full((B, 1, H, D), float("nan"), dtype=dtype, device="cuda")
+        attn.attn_decode(q.cuda(), kc.cuda(), vc.cuda(), sl.cuda(), o=o, workspace=ws)
+        torch.cuda.synchronize()
+        check(o, oracle.attn_decode(q, kc, vc, sl.numpy()), dtype, f"decode reuse seed={seed}")
+        assert torch.all(o.cpu()[sl <= 0] == 0)
+
+
 def test_decode_matches_forward_with_one_query(attn):
     """attn_decode row b equals attn_fwd(S_q = 1, S_kv = len_b) on the same data."""
     B, H, S_cap, D = 4, 4, 700, 128
