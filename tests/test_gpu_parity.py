@@ -455,13 +455,29 @@ def test_key_mask_row_kernel_cross_check(attn, monkeypatch):
 
 
 def test_fp16_prefill_full_size(attn):
-    """The bf16_s2048 shape (B=1, H=32, S=2048, D=128, causal) in fp16."""
-    q, k, v = workloads.make_prefill_shape(1003, torch.float16, 1, 32, 2048, 2048, 128)
+    """The fp16_s2048 workload (the bf16_s2048 shape, B=1 H=32 S=2048 D=128,
+    causal, in fp16) at full size, the data and launch bench.py times."""
+    q, k, v = workloads.make_prefill(workloads.FP16_S2048)
     say("fp16 prefill B=1 H=32 S=2048 D=128")
     o = attn.attn_fwd(q.cuda(), k.cuda(), v.cuda(), causal=True)
     torch.cuda.synchronize()
     max_abs, rel = check(o, oracle.attn_fwd(q, k, v, True), torch.float16, "fp16 s2048")
     say(f"  fp16 s2048: max abs {max_abs:.3e} rel L2 {rel:.3e}")
+
+
+def test_keypad_prefill_full_size(attn):
+    """The bf16_keypad workload (B=8 right-padded entries of S=1024, H=32,
+    D=128, no causal rule) at full size, the data and launch bench.py times,
+    with its log-sum-exp."""
+    cfg = workloads.BF16_KEYPAD
+    lens, mask, q, k, v = workloads.make_keypad_prefill(cfg)
+    say(f"key-padding prefill full size, lengths {lens.tolist()}")
+    o, lse = attn.attn_fwd_mask(q.cuda(), k.cuda(), v.cuda(), mask.cuda(), causal=False, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rlse = oracle.attn_fwd_mask(q, k, v, mask.numpy(), False)
+    max_abs, rel = check(o, ro, torch.bfloat16, "keypad full size")
+    check_lse(lse, rlse, torch.bfloat16, "keypad full size")
+    say(f"  keypad: max abs {max_abs:.3e} rel L2 {rel:.3e}")
 
 
 # ---------------------------------------------------------------------------
@@ -544,6 +560,17 @@ def test_sinusoidal_pe_against_oracle(attn, case):
     bar = 3e-7 + 2.5e-16 * (pos0 + S)
     err = float(np.abs(pe - ref).max())
     assert err <= bar, f"pe {case}: max abs err {err:.3e} > {bar:.3e}"
+
+
+def test_sinusoidal_pe_full_size(attn):
+    """The table bench.py times: 4096 positions x d_model 4096."""
+    S, d = workloads.PE_S, workloads.PE_D
+    say(f"pe full size {S} x {d}")
+    pe = attn.sinusoidal_pe(S, d).cpu().double().numpy()
+    ref = oracle.sinusoidal_pe(S, d, 0)
+    bar = 3e-7 + 2.5e-16 * S
+    err = float(np.abs(pe - ref).max())
+    assert err <= bar, f"pe full size: max abs err {err:.3e} > {bar:.3e}"
 
 
 def test_sinusoidal_pe_position_zero_is_exact(attn):
