@@ -145,6 +145,18 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, copy_mib: int = 256) -
     return out
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the baseline record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def main() -> int:
     if len(sys.argv) >= 2 and sys.argv[1] == "--traffic-from":
         # bench.py --traffic-from FETCH_CSV WRITE_CSV: write profiles/traffic.json
@@ -384,7 +396,7 @@ def main() -> int:
         ref = oracle.attn_fwd(q_h, k_h, v_h, True)
         cpu_s = time.perf_counter() - t
         cpu = {"value": flops / cpu_s / 1e12, "unit": "TFLOPS", "cores": oracle.num_threads(),
-               "kind": "oracle",
+               "kind": "oracle", "cpu_model": cpu_model(),
                "sample": f"full prefill workload (B=1 H=32 S=2048 D=128 causal), one fp64 pass in "
                          f"{cpu_s:.2f} s; rate uses the same algorithmic FLOP count as the GPU figure"}
         err = np.abs(o_h - ref)

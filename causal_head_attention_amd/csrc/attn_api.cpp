@@ -9,6 +9,8 @@
 // section 4.1). An environment switch picks the implementation, as the
 // depthwise-convolution page's section 6.2 suggests for bisecting:
 //   ATTN_ALGO=auto (default) | tile | row
+// and ATTN_CHECK=1 turns on a debug check of the device-side lengths (a
+// synchronous copy to the host before the launch).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -16,6 +18,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/attn.h"
 #include "launch.h"
@@ -82,6 +85,28 @@ Algo algo_from_env() {
     return kAuto;
 }
 
+// ATTN_CHECK=1: the device-side lengths are copied to the host (synchronising
+// with this thread's stream) and any value the kernels would clamp -- below 0
+// or above the cache capacity -- is rejected before the launch.
+bool check_lengths_on() {
+    const char* s = std::getenv("ATTN_CHECK");
+    return s && !std::strcmp(s, "1");
+}
+
+int check_lengths(const char* fn, const int32_t* lens, int B, int cap) {
+    std::vector<int32_t> h((size_t)B);
+    hipError_t e = hipMemcpyAsync(h.data(), lens, (size_t)B * sizeof(int32_t), hipMemcpyDeviceToHost, t_stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(t_stream);
+    if (e != hipSuccess)
+        return fail(ATTN_ERR_HIP, std::string(fn) + ": ATTN_CHECK could not read the lengths: " + hipGetErrorString(e));
+    for (int i = 0; i < B; ++i)
+        if (h[(size_t)i] < 0 || h[(size_t)i] > cap)
+            return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + ": ATTN_CHECK: length[" + std::to_string(i) +
+                                                  "] = " + std::to_string(h[(size_t)i]) + " lies outside [0, " +
+                                                  std::to_string(cap) + "]");
+    return ATTN_OK;
+}
+
 // Checks shared by attn_fwd, attn_fwd_kvcache, attn_fwd_mask and
 // attn_fwd_plan (sizes and flags only). With kvcache, S_kv is the cache capacity and the per-entry
 // lengths may be shorter than S_q (rows that see no key come out as 0).
@@ -144,6 +169,10 @@ int run_fwd(const char* fn, const void* q, const void* k, const void* v, const i
     if (overlap(lse, nlse, q, nq) || overlap(lse, nlse, k, nkv) || overlap(lse, nlse, v, nkv) ||
         overlap(lse, nlse, kv_lens, nlen) || overlap(lse, nlse, key_mask, nmask))
         return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + ": lse overlaps an input");
+    if (kv_lens && check_lengths_on()) {
+        const int cs = check_lengths(fn, kv_lens, B, S_kv);
+        if (cs != ATTN_OK) return cs;
+    }
 
     attn::FwdArgs a{q, k, v, o, B, H, S_q, S_kv, D, causal,
                     (float)(1.0f / std::sqrt((float)D)) * 1.4426950408889634f, ev_start, ev_stop, kv_lens, lse,
@@ -305,6 +334,10 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
     if (overlap(workspace, nws, q, nq) || overlap(workspace, nws, kcache, nkv) ||
         overlap(workspace, nws, vcache, nkv) || overlap(workspace, nws, seqlens, nsl))
         return fail(ATTN_ERR_INVALID_ARG, "attn_decode: workspace overlaps an input");
+    if (check_lengths_on()) {
+        const int cs = check_lengths("attn_decode", seqlens, B, S_cap);
+        if (cs != ATTN_OK) return cs;
+    }
 
     attn::DecodeArgs a{q, kcache, vcache, seqlens, o, B, H, S_cap, D,
                        (float)(1.0f / std::sqrt((float)D)) * 1.4426950408889634f, (float*)workspace, ev_start,

@@ -34,6 +34,12 @@
  *    with S_q <= S_kv places the S_q queries at the END of the key sequence:
  *    query i is at absolute position i + (S_kv - S_q) and sees keys
  *    j <= i + S_kv - S_q. With S_q == S_kv this is exactly j <= i.
+ *  - Debug check: with the environment variable ATTN_CHECK=1, attn_decode
+ *    and attn_fwd_kvcache first copy their device-side lengths to the host
+ *    (a synchronous copy on the calling thread's stream, so not for code
+ *    under graph capture) and reject with ATTN_ERR_INVALID_ARG any length
+ *    below 0 or above the cache capacity, values the kernels would otherwise
+ *    clamp. The check runs after the other argument checks, before the launch.
  *  - Arithmetic: scores, softmax and accumulation in fp32 whatever the
  *    storage type (MMHA page, section 3.3); the scale 1/sqrt(D) is an fp32
  *    value. bf16 results are rounded to nearest even.

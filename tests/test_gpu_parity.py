@@ -670,6 +670,34 @@ def test_masked_softmax_full_size_sampled_rows(attn):
 # ---------------------------------------------------------------------------
 # Error paths through the binding on a live device
 # ---------------------------------------------------------------------------
+def test_length_check_env_rejects_clamped_lengths(attn, monkeypatch):
+    """ATTN_CHECK=1: lengths the kernels would clamp (below 0, above the cache
+    capacity) are rejected on the host before any launch; valid lengths give
+    the same bits as without the check."""
+    B, H, S_cap, D = 3, 2, 40, 64
+    g = torch.Generator().manual_seed(420)
+    q = torch.randn(B, 1, H, D, generator=g).to(torch.bfloat16).cuda()
+    kc = torch.randn(B, S_cap, H, D, generator=g).to(torch.bfloat16).cuda()
+    vc = torch.randn(B, S_cap, H, D, generator=g).to(torch.bfloat16).cuda()
+    good = torch.tensor([0, 17, S_cap], dtype=torch.int32, device="cuda")
+    plain = attn.attn_decode(q, kc, vc, good)
+    qs = torch.randn(B, 8, H, D, generator=g).to(torch.bfloat16).cuda()
+    plain_kv = attn.attn_fwd_kvcache(qs, kc, vc, good, causal=True)
+    monkeypatch.setenv("ATTN_CHECK", "1")
+    checked = attn.attn_decode(q, kc, vc, good)
+    checked_kv = attn.attn_fwd_kvcache(qs, kc, vc, good, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(plain.cpu(), checked.cpu()) and torch.equal(plain_kv.cpu(), checked_kv.cpu())
+    for bad in ([5, -1, 3], [5, S_cap + 1, 3]):
+        lens = torch.tensor(bad, dtype=torch.int32, device="cuda")
+        with pytest.raises(attn.AttnError) as e:
+            attn.attn_decode(q, kc, vc, lens)
+        assert e.value.status == attn.ATTN_ERR_INVALID_ARG and "ATTN_CHECK" in str(e.value)
+        with pytest.raises(attn.AttnError) as e:
+            attn.attn_fwd_kvcache(qs, kc, vc, lens, causal=True)
+        assert e.value.status == attn.ATTN_ERR_INVALID_ARG and "length[1]" in str(e.value)
+
+
 def test_error_paths_on_device(attn):
     q = torch.zeros(1, 8, 2, 128, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(attn.AttnError) as e:
