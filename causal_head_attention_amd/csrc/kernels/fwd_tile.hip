@@ -1,9 +1,11 @@
 // fwd_tile.hip -- fused causal attention forward on gfx950 matrix cores
 // (bf16 or fp16 storage, fp32 arithmetic).
 //
-// One workgroup (8 waves) owns one (b, h, block of 128 queries); with the
-// causal mask it owns two blocks, r and n-1-r, run one after the other so
-// every workgroup walks the same number of KV tiles. Per 64-key tile:
+// One workgroup (8 waves) owns two blocks of 128 queries of one (b, h), r
+// and n-1-r, run one after the other: with the causal mask every workgroup
+// then walks the same number of KV tiles, and without it each pays the fixed
+// costs of a block once for two (with per-entry cache lengths, one block per
+// workgroup). Per 64-key tile:
 //
 //   K tile  : HBM -> registers -> LDS  (row-major, rows padded by 16 bytes)
 //   V tile  : HBM -> registers -> transposed in registers -> LDS as V^T

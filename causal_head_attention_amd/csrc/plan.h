@@ -79,14 +79,19 @@ struct TileGrid {
 };
 
 // Pairing evens out the causal triangle of a square (or nearly square)
-// problem, where query block j sees about j+1 key tiles. With per-entry cache
-// lengths the chunk is usually short against the cache, every block of an
-// entry sees nearly the same number of tiles, and pairing would only double
-// the longest workgroup; such launches run one block per workgroup.
+// problem, where query block j sees about j+1 key tiles. Without the causal
+// rule every block sees the same tiles; pairing then halves the number of
+// workgroups, so each one pays the fixed costs of a block (the opening loads,
+// a key-mask scan) once for two blocks and loads its second block under the
+// first one's merge. With per-entry cache lengths the chunk is usually short
+// against the cache, every block of an entry sees nearly the same number of
+// tiles, and pairing only doubles the longest workgroup; such launches run
+// one block per workgroup.
 ATTN_HD inline TileGrid tile_grid(int B, int H, int S_q, int causal, bool kv_lengths = false) {
+    (void)causal;
     TileGrid g;
     g.n_qblk = (S_q + kTileM - 1) / kTileM;
-    g.paired = (causal && !kv_lengths) ? 1 : 0;
+    g.paired = kv_lengths ? 0 : 1;
     g.items_per_bh = g.paired ? (g.n_qblk + 1) / 2 : g.n_qblk;
     g.n_items = (long long)B * H * g.items_per_bh;
     return g;

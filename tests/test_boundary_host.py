@@ -72,7 +72,7 @@ def test_fwd_empty_calls_are_ok_and_launch_nothing():
 
 def test_non_causal_allows_more_queries_than_keys_in_validation():
     p = attn.attn_fwd_plan(1, 2, 100, 50, 64, False, attn.ATTN_BF16)
-    assert p.kernel == 1 and p.paired == 0
+    assert p.kernel == 1 and p.grid == 2 and p.max_tiles == 1   # one block per head: nothing to pair
 
 
 def test_status_strings():
@@ -115,7 +115,8 @@ def test_plan_bf16_s4096_and_odd_block_counts():
 
 def test_plan_non_causal_and_fp32():
     p = attn.attn_fwd_plan(2, 8, 512, 512, 64, False, attn.ATTN_BF16)
-    assert p.paired == 0 and p.grid == 2 * 8 * 4 and p.max_tiles == p.min_tiles == 8
+    # no causal rule: blocks 3+0 and 2+1 of each head share a workgroup
+    assert p.paired == 1 and p.grid == 2 * 8 * 2 and p.max_tiles == p.min_tiles == 16
     p = attn.attn_fwd_plan(2, 8, 512, 512, 64, True, attn.ATTN_F32)
     assert p.kernel == 2 and p.grid == 2 * 8 * 512
 
