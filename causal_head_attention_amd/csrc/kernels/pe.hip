@@ -5,8 +5,10 @@
 //
 // The page computes the table in fp32, with the frequencies precomputed
 // once and each element one multiply and one sin or cos. Here a workgroup
-// covers kPeRows positions: each thread takes frequency pairs i, computes
-// w_i once (fp64) and reuses it for those rows; the angle pos * w_i is formed
+// covers kPeRows positions and kPeThreads frequency pairs (a 2-D grid, so
+// the chip holds many waves to hide the fp64 and sincos latency): each
+// thread takes one pair i, computes w_i once (fp64) and reuses it for those
+// rows; the angle pos * w_i is formed
 // and reduced modulo 2*pi in fp64 (Cody and Waite's two-part constant), so
 // that fp32 sin/cos of the reduced angle stay accurate to a few ulp at any
 // position (an fp32 product pos * w_i alone would lose about 2^-24 * pos
@@ -31,20 +33,20 @@ __global__ __launch_bounds__(kPeThreads) void sinusoidal_pe_kernel(float* __rest
                                                                    int pos0) {
     const int half = d_model / 2;
     const int s0 = blockIdx.x * kPeRows;
-    for (int i = threadIdx.x; i < half; i += kPeThreads) {
-        const double w = exp2(-((double)(2 * i) / (double)d_model) * kLog2Base);
-#pragma unroll 4
-        for (int r = 0; r < kPeRows; ++r) {
-            const int s = s0 + r;
-            if (s >= S) break;
-            const double angle = (double)(pos0 + s) * w;
-            const double k = rint(angle * kInvTwoPi);
-            const double red = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, angle));   // in [-pi, pi] up to rounding
-            float sn, cs;
-            sincosf((float)red, &sn, &cs);
-            const f32x2_t pair = {sn, cs};
-            *(f32x2_t*)(pe + (size_t)s * d_model + 2 * i) = pair;
-        }
+    const int i = blockIdx.y * kPeThreads + threadIdx.x;   // frequency pair
+    if (i >= half) return;
+    const double w = exp2(-((double)(2 * i) / (double)d_model) * kLog2Base);
+#pragma unroll
+    for (int r = 0; r < kPeRows; ++r) {
+        const int s = s0 + r;
+        if (s >= S) break;
+        const double angle = (double)(pos0 + s) * w;
+        const double k = rint(angle * kInvTwoPi);
+        const double red = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, angle));   // in [-pi, pi] up to rounding
+        float sn, cs;
+        sincosf((float)red, &sn, &cs);
+        const f32x2_t pair = {sn, cs};
+        *(f32x2_t*)(pe + (size_t)s * d_model + 2 * i) = pair;
     }
 }
 
@@ -52,9 +54,10 @@ __global__ __launch_bounds__(kPeThreads) void sinusoidal_pe_kernel(float* __rest
 
 hipError_t launch_sinusoidal_pe(float* pe, int S, int d_model, int pos0, hipEvent_t ev_start, hipEvent_t ev_stop,
                                 hipStream_t stream) {
-    const unsigned grid = (unsigned)((S + kPeRows - 1) / kPeRows);
-    hipExtLaunchKernelGGL(sinusoidal_pe_kernel, dim3(grid), dim3(kPeThreads), 0, stream, ev_start, ev_stop, 0, pe, S,
-                          d_model, pos0);
+    const unsigned rows = (unsigned)((S + kPeRows - 1) / kPeRows);
+    const unsigned chunks = (unsigned)((d_model / 2 + kPeThreads - 1) / kPeThreads);
+    hipExtLaunchKernelGGL(sinusoidal_pe_kernel, dim3(rows, chunks), dim3(kPeThreads), 0, stream, ev_start, ev_stop, 0,
+                          pe, S, d_model, pos0);
     return hipGetLastError();
 }
 

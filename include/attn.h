@@ -236,6 +236,8 @@ int attn_masked_softmax(const void* s, void* p, int B, int H, int S_q, int S_kv,
  *             requires: fp16 cannot hold the small frequencies)
  *   d_model : even, >= 2 (else ATTN_ERR_INVALID_ARG)
  *   pos0    : first position (>= 0); the last, pos0 + S - 1, must be <= 2^31 - 1
+ *   S <= 67,108,860 and d_model <= 33,553,920 (the launch grid), else
+ *   ATTN_ERR_UNSUPPORTED
  * The angle is formed and reduced modulo 2*pi in fp64, so every element is
  * within a few fp32 ulp of the exact value at any position. S == 0 is a
  * valid empty call.

@@ -225,6 +225,15 @@ def test_pe_rejections(args, needle):
     assert needle in attn.load().attn_last_error().decode()
 
 
+@pytest.mark.parametrize("args,needle", [
+    ((A, 1 << 30, 2, 0), "S exceeds"),
+    ((A, 1, 1 << 26, 0), "d_model exceeds"),
+])
+def test_pe_grid_limits(args, needle):
+    assert L.attn_sinusoidal_pe(*args) == attn.ATTN_ERR_UNSUPPORTED
+    assert needle in attn.load().attn_last_error().decode()
+
+
 def test_pe_empty_call():
     assert L.attn_sinusoidal_pe(0, 0, 64, 0) == attn.ATTN_OK
 
