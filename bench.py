@@ -391,13 +391,16 @@ def main() -> int:
     parity = None
     if not args.no_cpu_baseline:
         import oracle
-        log("CPU baseline: fp64 oracle on the full prefill workload")
-        t = time.perf_counter()
-        ref = oracle.attn_fwd(q_h, k_h, v_h, True)
-        cpu_s = time.perf_counter() - t
-        cpu = {"value": flops / cpu_s / 1e12, "unit": "TFLOPS", "cores": oracle.num_threads(),
+        log("CPU baseline: fp64 oracle on the full prefill workload, repeated for >= 10 s")
+        passes, cpu_s = 0, 0.0
+        while passes < 30 and (cpu_s < 10.0 or passes == 0):
+            t = time.perf_counter()
+            ref = oracle.attn_fwd(q_h, k_h, v_h, True)
+            cpu_s += time.perf_counter() - t
+            passes += 1
+        cpu = {"value": passes * flops / cpu_s / 1e12, "unit": "TFLOPS", "cores": oracle.num_threads(),
                "kind": "oracle", "cpu_model": cpu_model(),
-               "sample": f"full prefill workload (B=1 H=32 S=2048 D=128 causal), one fp64 pass in "
+               "sample": f"full prefill workload (B=1 H=32 S=2048 D=128 causal), {passes} fp64 passes in "
                          f"{cpu_s:.2f} s; rate uses the same algorithmic FLOP count as the GPU figure"}
         err = np.abs(o_h - ref)
         parity = {"prefill_max_abs": float(err.max()),
