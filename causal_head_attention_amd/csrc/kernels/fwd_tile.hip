@@ -8,7 +8,8 @@
 // workgroup). Per 64-key tile:
 //
 //   K tile  : HBM -> registers -> LDS  (row-major, rows padded by 16 bytes)
-//   V tile  : HBM -> registers -> transposed in registers -> LDS as V^T
+//   V tile  : HBM -> registers -> LDS (key rows, as loaded); the P.V
+//             operands V^T come from transposing LDS reads (ds_read_b64_tr_b16)
 //   S^T     = K . Q^T            v_mfma_f32_32x32x16_bf16, fp32 accumulate
 //   mask    : on tiles that cross the diagonal or the ragged key end, and
 //             on every tile when a key-padding mask is given
@@ -68,6 +69,8 @@ namespace {
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 // The 16-bit storage types and their matrix-core / dot-product forms.
 template <typename T>
@@ -95,11 +98,6 @@ __device__ __forceinline__ int swap_bits23(int x) {
     return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
-__device__ __forceinline__ unsigned half_of(u32x4_t x, int e) {
-    // 16-bit element e (0..7) of a 16-byte vector
-    return (x[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-}
-
 // LDS layout of one stage (padded rows instead of XOR swizzles, so every
 // MFMA operand read is a base register plus an immediate offset):
 //   K tile : 64 rows of D bf16, row stride 2*D + 16 bytes. Key r of the tile
@@ -107,20 +105,22 @@ __device__ __forceinline__ unsigned half_of(u32x4_t x, int e) {
 //            reads LDS row 32*half + lane%32 gets key swap_bits23(lane%32)
 //            and 8 (or 16) consecutive lanes read 8 (16) consecutive rows:
 //            with the 16-byte pad those fall in distinct banks.
-//   V^T    : D rows of 64 keys, row stride 144 bytes (consecutive head dims
-//            -> consecutive rows -> distinct banks for the P.V reads).
+//   V tile : 64 key rows of D bf16 in key order, as loaded, row stride
+//            tile_vrow_bytes(D). The P.V operands (V^T) come from the
+//            transposing LDS read ds_read_b64_tr_b16: in each 16-lane group,
+//            lane j addresses 4 head dims of key row j/4, and the read hands
+//            lane j one head dim for those 4 keys. The stride puts the 4 rows
+//            of a half-wave's read in distinct 64-byte bank windows.
 template <int D>
 struct TileCfg {
     static constexpr int KCH = D / 8;            // 16-byte chunks per K row
     static constexpr int KS = D / 16;            // MFMA k-steps for S^T
     static constexpr int DB = D / 32;            // 32-row blocks of O^T
-    static constexpr int KR = D / 32;            // keys per V-transposer thread
-    static constexpr int NKQ = kTileN / KR;      // key groups per V tile
     static constexpr int NPRE = D / 32;          // 16-byte prefetch registers per thread
     static constexpr int KROW = 2 * D + 16;
-    static constexpr int VROW = 2 * kTileN + 16;
+    static constexpr int VROW = tile_vrow_bytes(D);
     static constexpr int K_BYTES = kTileN * KROW;
-    static constexpr int V_BYTES = D * VROW;
+    static constexpr int V_BYTES = kTileN * VROW;
     static constexpr int LDS = tile_lds_bytes(D);
     static_assert(2 * (K_BYTES + V_BYTES) <= LDS, "stages fit");
 };
@@ -156,9 +156,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base
     return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, bytes > 0 ? bytes : 0, 0x00020000);
 }
 
-// Loader roles: waves 0-3 stage K tiles (16 lanes per key row), waves 4-7
-// stage V tiles: thread (c8, kq) loads KR keys x 8 head dims and writes them
-// transposed, so the 16-lane groups of one LDS store fill one 128-byte V^T row.
+// Loader roles: waves 0-3 stage K tiles, waves 4-7 stage V tiles, each 16
+// bytes of a key row per lane and load (D/8 lanes per row).
 template <int D>
 __device__ __forceinline__ void load_k(u32x4_t (&pre)[TileCfg<D>::NPRE], __amdgpu_buffer_rsrc_t rt, int H,
                                        int tid) {
@@ -175,11 +174,12 @@ template <int D>
 __device__ __forceinline__ void load_v(u32x4_t (&pre)[TileCfg<D>::NPRE], __amdgpu_buffer_rsrc_t rt, int H,
                                        int tid) {
     using C = TileCfg<D>;
-    const int u = tid - 256;
-    const int kq = u % C::NKQ, c8 = u / C::NKQ;
 #pragma unroll
-    for (int kk = 0; kk < C::KR; ++kk)
-        pre[kk] = __builtin_amdgcn_raw_buffer_load_b128(rt, tok_off<D>(kq * C::KR + kk, c8, H), 0, 0);
+    for (int it = 0; it < C::NPRE; ++it) {
+        const int ci = (tid - 256) + 256 * it;
+        const int row = ci / C::KCH, ch = ci % C::KCH;
+        pre[it] = __builtin_amdgcn_raw_buffer_load_b128(rt, tok_off<D>(row, ch, H), 0, 0);
+    }
 }
 
 template <int D>
@@ -195,24 +195,13 @@ __device__ __forceinline__ void store_k(const u32x4_t (&pre)[TileCfg<D>::NPRE], 
 }
 
 template <int D>
-__device__ __forceinline__ void store_v(const u32x4_t (&pre)[TileCfg<D>::NPRE], char* vt, int tid) {
+__device__ __forceinline__ void store_v(const u32x4_t (&pre)[TileCfg<D>::NPRE], char* vst, int tid) {
     using C = TileCfg<D>;
-    const int u = tid - 256;
-    const int kq = u % C::NKQ, c8 = u / C::NKQ;
-    char* base = vt + 8 * c8 * C::VROW + 2 * C::KR * kq;
 #pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-        char* dst = base + dd * C::VROW;
-        if constexpr (C::KR == 4) {
-            u32x2_t w;
-            w[0] = half_of(pre[0], dd) | (half_of(pre[1], dd) << 16);
-            w[1] = half_of(pre[2], dd) | (half_of(pre[3], dd) << 16);
-            *(u32x2_t*)dst = w;
-        } else if constexpr (C::KR == 2) {
-            *(unsigned*)dst = half_of(pre[0], dd) | (half_of(pre[1], dd) << 16);
-        } else {
-            *(unsigned short*)dst = (unsigned short)half_of(pre[0], dd);
-        }
+    for (int it = 0; it < C::NPRE; ++it) {
+        const int ci = (tid - 256) + 256 * it;
+        const int row = ci / C::KCH, ch = ci % C::KCH;
+        *(u32x4_t*)(vst + row * C::VROW + 16 * ch) = pre[it];
     }
 }
 
@@ -290,6 +279,14 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_kernel(
     const v2 kOnes2 = {(T)1.0f, (T)1.0f};
     using C = TileCfg<D>;
     __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+    // an MFMA A operand of V^T: two transposing reads, keys +0..3 and +4..7
+    auto vt_operand = [](const char* p) {
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * C::VROW));
+        const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+        const u32x4_t w = {l2[0], l2[1], h2[0], h2[1]};
+        return __builtin_bit_cast(v8, w);
+    };
     // stages: K0 K1 V0 V1, then four key-mask stages (tile of step u in u % 4)
     auto kst = [&](int i) { return lds + i * C::K_BYTES; };
     auto vst = [&](int i) { return lds + 2 * C::K_BYTES + i * C::V_BYTES; };
@@ -305,7 +302,13 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_kernel(
     const bool k_loader = tid < 256;
     // per-lane operand offsets inside a stage (the k-steps / blocks are immediates)
     const int k_lane = (32 * half + l32) * C::KROW + 16 * g;
-    const int v_lane = l32 * C::VROW + 16 * (4 * half + g);
+    // transposing V^T reads: lane j of 16-lane group grp addresses head dims
+    // 16*(grp&1) + 4*(j&3) .. +3 of key row j/4 (+ 8*(grp>>1), + 32*half), so
+    // lane (l32, g) gets head dim l32 of a 32-dim block for keys 8g..8g+3 of
+    // a 16-key step (and 8g+4..8g+7 from the read 4 rows on): the key order of
+    // its P registers
+    const int v_lane = (32 * half + 8 * (lane >> 5) + ((lane & 15) >> 2)) * C::VROW + 32 * ((lane >> 4) & 1) +
+                       8 * (lane & 3);
 
     int bh, p;
     if (KMASK && !kv_lens) {
@@ -556,7 +559,7 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_kernel(
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) va[db][s2] = *(const v8*)(vt + 32 * db * C::VROW + 32 * s2);
+                    for (int s2 = 0; s2 < 2; ++s2) va[db][s2] = vt_operand(vt + 64 * db + 16 * s2 * C::VROW);
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -581,7 +584,7 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_kernel(
                 // schedule: the V^T operand reads, the P.V MFMAs each followed by
                 // a slice of the softmax VALU work, then the K operand reads and
                 // the S(t+1) MFMAs, likewise interleaved
-                __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::DB, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 4 * C::DB, 0);
 #pragma unroll
                 for (int i = 0; i < 2 * C::DB; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -617,7 +620,7 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_kernel(
             for (int db = 0; db < C::DB; ++db)
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2)
-                    acc[db] = Mma<T>::mfma(*(const v8*)(vt + 32 * db * C::VROW + 32 * s2), pb_prev[s2], acc[db]);
+                    acc[db] = Mma<T>::mfma(vt_operand(vt + 64 * db + 16 * s2 * C::VROW), pb_prev[s2], acc[db]);
         }
         lds_barrier();   // every wave's reads of the stages are done before the merge reuses them
 

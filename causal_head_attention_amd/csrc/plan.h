@@ -47,14 +47,19 @@ ATTN_HD inline int xcd_remap(int x, int n) {
 // Key-mask stages of the tile kernel: four tiles of kTileN bytes.
 constexpr int kMaskStageBytes = 4 * kTileN;
 
+// Row stride of a V tile in LDS (key rows of D 16-bit values): 64 or 192
+// bytes past a multiple of 256, so the 4 rows one half-wave's transposing
+// read touches fall in distinct 64-byte bank windows.
+ATTN_HD constexpr int tile_vrow_bytes(int D) { return 2 * D == 64 ? 64 : 2 * D + 64; }
+
 // LDS bytes of the tile kernel for head dim D: two stages of (K tile with
-// rows padded to 2*D+16 bytes, V^T tile with rows of 2*kTileN+16 bytes), or
+// rows padded to 2*D+16 bytes, V tile with rows of tile_vrow_bytes(D)), or
 // the end-of-block exchange of the partial softmax states of four waves
 // (64 lanes x (2 + D/2) floats each), whichever is larger; then the
 // key-mask stages.
 ATTN_HD constexpr int tile_stage_bytes(int D) {
-    return (2 * (kTileN * (2 * D + 16) + D * (2 * kTileN + 16))) > (4 * 64 * (2 + D / 2) * 4)
-               ? (2 * (kTileN * (2 * D + 16) + D * (2 * kTileN + 16)))
+    return (2 * kTileN * ((2 * D + 16) + tile_vrow_bytes(D))) > (4 * 64 * (2 + D / 2) * 4)
+               ? (2 * kTileN * ((2 * D + 16) + tile_vrow_bytes(D)))
                : (4 * 64 * (2 + D / 2) * 4);
 }
 ATTN_HD constexpr int tile_lds_bytes(int D) { return tile_stage_bytes(D) + kMaskStageBytes; }
