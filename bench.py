@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 BF16_MFMA_PEAK_TFLOPS = 2516.6   # MI355X dense bf16: 256 CU x 4096 FLOP/clk x 2.4 GHz
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+FP32_VALU_PEAK_TFLOPS = 157.3    # MI355X fp32 vector
 FLUSH_BYTES = 512 << 20
 TILE_SRC = os.path.join(ROOT, "causal_head_attention_amd", "csrc", "kernels", "fwd_tile.hip")
 DECODE_SRC = os.path.join(ROOT, "causal_head_attention_amd", "csrc", "kernels", "decode.hip")
@@ -283,7 +284,7 @@ def main() -> int:
                              "flop_per_launch": flop, "mean_launch_us": round(mean * 1e3, 2),
                              "median_launch_us": round(statistics.median(ms) * 1e3, 2)}}
 
-    kv = f16 = kp = qp = pe_leg = sm_leg = None
+    kv = f16 = kp = qp = pe_leg = sm_leg = f32 = None
     if not args.skip_extras:
         kc_cfg = workloads.BF16_KVCACHE
         log("KV-cache prefill: generating inputs")
@@ -369,6 +370,23 @@ def main() -> int:
                                "frac": round(sm_gbs / HBM_PEAK_GBS, 4), "bytes_per_call": sm_bytes,
                                "mean_launch_us": round(sm_mean * 1e3, 2)}}
         del s_sm, p_sm
+
+        # the fp32 configuration (row kernel on the vector ALUs), for information
+        # against the fp32 vector peak
+        c32 = workloads.FP32_SMALL
+        log("fp32 prefill")
+        q32, k32, v32 = (t.to(dev) for t in workloads.make_prefill(c32))
+        o32 = torch.empty_like(q32)
+        f32_ms = cold_ms(lambda: attn.attn_fwd(q32, k32, v32, o32, causal=True))
+        f32_mean = statistics.fmean(f32_ms)
+        f32_tf = c32.flops() / (f32_mean * 1e-3) / 1e12
+        f32 = {"value": round(f32_tf, 3), "unit": "TFLOPS",
+               "workload": f"fp32 causal prefill B={c32.B} H={c32.H} S={c32.S_q} D={c32.D} (seed {c32.seed}), "
+                           f"one wave per query row on the vector ALUs; cold, 20 calls",
+               "roofline": {"bound": "alu", "achieved": round(f32_tf, 3), "peak": FP32_VALU_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(f32_tf / FP32_VALU_PEAK_TFLOPS, 4),
+                            "flop_per_launch": c32.flops(), "mean_launch_us": round(f32_mean * 1e3, 2)}}
+        del q32, k32, v32, o32
 
     if args.copy_calibration:
         n = args.copy_calibration << 20
@@ -457,6 +475,7 @@ def main() -> int:
         "qkv_proj": qp,
         "position_encoding": pe_leg,
         "masked_softmax": sm_leg,
+        "fp32_prefill": f32,
         "cpu_baseline": cpu,
         "parity": parity,
     }

@@ -3,8 +3,8 @@
 // Serves the fp32 forward (gfx950 has no reduced-precision fp32 matrix
 // path, and fp32 inputs are held to a 1e-4 absolute bound) and, under
 // ATTN_ALGO=row, a bf16 / fp16 cross-check of the tile kernel. Each iteration takes
-// 64 keys: lane j computes the score of key j0+j (one K row, 16-byte
-// loads), the wave reduces max and sum with cross-lane shuffles, and the
+// 64 keys: lane j computes the score of key j0+j (one K row, read in
+// 16-byte pieces), the wave reduces max and sum with cross-lane shuffles, and the
 // lanes switch to owning head dims to accumulate p_j * V[j0+j, :] with
 // coalesced V-row loads.
 //
@@ -29,6 +29,31 @@ __device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(_Float16 x) { return (float)x; }
 template <typename T>
 __device__ __forceinline__ T from_f32(float x) { return (T)x; }
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Element e of a 16-byte piece, widened to fp32 (the word is copied out
+// first: bit-casting a vector-element lvalue reads element 0 with this
+// compiler).
+template <typename T>
+__device__ __forceinline__ float elem_of(const u32x4_t& w, int e);
+template <>
+__device__ __forceinline__ float elem_of<float>(const u32x4_t& w, int e) {
+    const unsigned u = w[e];
+    return __builtin_bit_cast(float, u);
+}
+template <>
+__device__ __forceinline__ float elem_of<__bf16>(const u32x4_t& w, int e) {
+    const unsigned u = w[e >> 1];
+    return __builtin_bit_cast(float, (u >> (16 * (e & 1))) << 16);
+}
+template <>
+__device__ __forceinline__ float elem_of<_Float16>(const u32x4_t& w, int e) {
+    const unsigned u = w[e >> 1];
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(u >> (16 * (e & 1))));
+}
+
+constexpr int kRowVBatch = 16;   // V-row loads in flight together in the P.V phase
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -72,10 +97,17 @@ __global__ __launch_bounds__(kRowThreads) void fwd_row_kernel(const T* __restric
         float s = -INFINITY;
         // key j is hidden when the key-padding mask says so ([B, S_cap] bytes)
         if (j < n_keys && (!key_mask || key_mask[(size_t)b * S_cap + j] != 0)) {
-            const T* krow = K + ((size_t)((size_t)b * S_cap + j) * H + h) * D;
+            // the lane's K row in 16-byte pieces (rows are 16-byte aligned): one
+            // load instruction then covers 64 rows once, not once per head dim
+            const u32x4_t* krow = (const u32x4_t*)(K + ((size_t)((size_t)b * S_cap + j) * H + h) * D);
+            constexpr int E = 16 / (int)sizeof(T);   // elements per piece
             float dot = 0.f;
-#pragma unroll 8
-            for (int d = 0; d < D; ++d) dot = __builtin_fmaf(qs[d], to_f32(krow[d]), dot);
+#pragma unroll 4
+            for (int pc = 0; pc < D / E; ++pc) {
+                const u32x4_t w = krow[pc];
+#pragma unroll
+                for (int e = 0; e < E; ++e) dot = __builtin_fmaf(qs[E * pc + e], elem_of<T>(w, e), dot);
+            }
             s = dot * c;
         }
         const float m_new = fmaxf(m_run, wave_max(s));
@@ -88,13 +120,37 @@ __global__ __launch_bounds__(kRowThreads) void fwd_row_kernel(const T* __restric
 #pragma unroll
         for (int e = 0; e < DPL; ++e) acc[e] *= alpha;
         const int nj = min(64, n_keys - j0);
-        for (int jj = 0; jj < nj; ++jj) {
-            const float p = __shfl(pj, jj);
-            const T* vrow = V + ((size_t)((size_t)b * S_cap + j0 + jj) * H + h) * D;
+        if (nj == 64) {
+            // a full chunk: V rows in batches of 16 loads in flight, then their
+            // FMAs (same key order as the loop below)
+#pragma unroll 1
+            for (int jb = 0; jb < 64; jb += kRowVBatch) {
+                float vv[kRowVBatch][DPL];
 #pragma unroll
-            for (int e = 0; e < DPL; ++e) {
-                const int d = lane + 64 * e;
-                if (d < D) acc[e] = __builtin_fmaf(p, to_f32(vrow[d]), acc[e]);
+                for (int u = 0; u < kRowVBatch; ++u) {
+                    const T* vrow = V + ((size_t)((size_t)b * S_cap + j0 + jb + u) * H + h) * D;
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e) {
+                        const int d = lane + 64 * e;
+                        vv[u][e] = d < D ? to_f32(vrow[d]) : 0.f;
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kRowVBatch; ++u) {
+                    const float p = __shfl(pj, jb + u);
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e) acc[e] = __builtin_fmaf(p, vv[u][e], acc[e]);
+                }
+            }
+        } else {
+            for (int jj = 0; jj < nj; ++jj) {
+                const float p = __shfl(pj, jj);
+                const T* vrow = V + ((size_t)((size_t)b * S_cap + j0 + jj) * H + h) * D;
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) {
+                    const int d = lane + 64 * e;
+                    if (d < D) acc[e] = __builtin_fmaf(p, to_f32(vrow[d]), acc[e]);
+                }
             }
         }
     }
