@@ -284,7 +284,7 @@ def main() -> int:
                              "flop_per_launch": flop, "mean_launch_us": round(mean * 1e3, 2),
                              "median_launch_us": round(statistics.median(ms) * 1e3, 2)}}
 
-    kv = f16 = kp = qp = pe_leg = sm_leg = f32 = None
+    kv = f16 = kp = qp = pe_leg = sm_leg = f32 = nc = None
     if not args.skip_extras:
         kc_cfg = workloads.BF16_KVCACHE
         log("KV-cache prefill: generating inputs")
@@ -370,6 +370,16 @@ def main() -> int:
                                "frac": round(sm_gbs / HBM_PEAK_GBS, 4), "bytes_per_call": sm_bytes,
                                "mean_launch_us": round(sm_mean * 1e3, 2)}}
         del s_sm, p_sm
+
+        # the bf16_s2048 data without the causal rule: every query block walks
+        # all 32 key tiles (two blocks per workgroup)
+        log("non-causal prefill")
+        ncf = workloads.visible_pairs(pc.S_q, pc.S_kv, False) * 4 * pc.B * pc.H * pc.D
+        onc = torch.empty_like(q)
+        nc = mfma_leg(cold_ms(lambda: attn.attn_fwd(q, k, v, onc, causal=False)), ncf,
+                      f"bf16 non-causal prefill B={pc.B} H={pc.H} S={pc.S_q} D={pc.D} (the bf16_s2048 data, "
+                      f"seed {pc.seed}); cold, 20 calls")
+        del onc
 
         # the fp32 configuration (row kernel on the vector ALUs), for information
         # against the fp32 vector peak
@@ -476,6 +486,7 @@ def main() -> int:
         "position_encoding": pe_leg,
         "masked_softmax": sm_leg,
         "fp32_prefill": f32,
+        "noncausal_prefill": nc,
         "cpu_baseline": cpu,
         "parity": parity,
     }

@@ -465,6 +465,17 @@ def test_fp16_prefill_full_size(attn):
     say(f"  fp16 s2048: max abs {max_abs:.3e} rel L2 {rel:.3e}")
 
 
+def test_noncausal_prefill_full_size(attn):
+    """The bf16_s2048 data without the causal rule, the launch bench.py times
+    (two query blocks per workgroup, every block walking all 32 key tiles)."""
+    q, k, v = workloads.make_prefill(workloads.BF16_S2048)
+    say("bf16 non-causal prefill B=1 H=32 S=2048 D=128")
+    o = attn.attn_fwd(q.cuda(), k.cuda(), v.cuda(), causal=False)
+    torch.cuda.synchronize()
+    max_abs, rel = check(o, oracle.attn_fwd(q, k, v, False), torch.bfloat16, "non-causal s2048")
+    say(f"  non-causal s2048: max abs {max_abs:.3e} rel L2 {rel:.3e}")
+
+
 def test_keypad_prefill_full_size(attn):
     """The bf16_keypad workload (B=8 right-padded entries of S=1024, H=32,
     D=128, no causal rule) at full size, the data and launch bench.py times,
