@@ -523,13 +523,24 @@ __global__ __launch_bounds__(kTileThreads) void fwd_tile_kernel(
                     const u32x2_t m0 = *(const u32x2_t*)mrow;
                     const u32x2_t m1 = *(const u32x2_t*)(mrow + 16);
                     const unsigned w4[4] = {m0[0], m0[1], m1[0], m1[1]};
+                    // fast path: a tile off the diagonal and the key end whose
+                    // mask bytes are all nonzero for every lane of the wave hides
+                    // nothing (a word has a zero byte iff (w - 0x01010101) & ~w &
+                    // 0x80808080 is nonzero; bytes past S_kv read as 0)
+                    const bool tile_edge = (causal && kbase + 31 > q0 + off) || (kbase + 32 > S_kv);
+                    unsigned zb = 0u;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kbase + 16 * (r >> 3) + 8 * g + (r & 7);
-                        const unsigned byte = (w4[r >> 2] >> (8 * (r & 3))) & 0xFFu;
-                        // branch-free: one compare chain and a select per register
-                        const bool hide = (key > lane_key_limit) | (key >= S_kv) | (byte == 0u);
-                        s_c[r] = hide ? -INFINITY : s_c[r];
+                    for (int x = 0; x < 4; ++x) zb |= (w4[x] - 0x01010101u) & ~w4[x] & 0x80808080u;
+                    const bool any_hidden = __builtin_amdgcn_ballot_w64(zb != 0u) != 0;
+                    if (tile_edge || any_hidden) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = kbase + 16 * (r >> 3) + 8 * g + (r & 7);
+                            const unsigned byte = (w4[r >> 2] >> (8 * (r & 3))) & 0xFFu;
+                            // branch-free: one compare chain and a select per register
+                            const bool hide = (key > lane_key_limit) | (key >= S_kv) | (byte == 0u);
+                            s_c[r] = hide ? -INFINITY : s_c[r];
+                        }
                     }
                 } else {
                     if ((causal && kbase + 31 > q0 + off) || (kbase + 32 > S_kv)) {
