@@ -420,10 +420,10 @@ int attn_qkv_proj(const void* x, const void* w, void* q, void* k, void* v, int M
         return fail(ATTN_ERR_UNSUPPORTED, "attn_qkv_proj: dtype " + std::to_string(dtype) +
                                               " not built (ATTN_BF16 or ATTN_F16)");
     if (E % attn::kGemmBK != 0)
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_qkv_proj: E must be a multiple of 64");
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_qkv_proj: E must be a multiple of " + std::to_string(attn::kGemmBK));
     const long long N = (long long)H * D;
     if (N % 32 != 0) return fail(ATTN_ERR_UNSUPPORTED, "attn_qkv_proj: H*D must be a multiple of 32");
-    // per-tile descriptors span 256 rows of X or of an output, 192 rows of W
+    // per-tile descriptors span 256 rows of X or of an output, 384 rows of W
     if ((long long)attn::kGemmBM * E * 2 > 0x7fffffffLL || (long long)attn::kGemmBM * N * 2 > 0x7fffffffLL ||
         3 * N > 0x7fffffffLL)
         return fail(ATTN_ERR_UNSUPPORTED, "attn_qkv_proj: E or H*D too large for 32-bit tile offsets");

@@ -12,15 +12,17 @@
 // operands, 128-bit loads, double buffering ("Week-4 CUDA notes" page,
 // sections 1.2-1.3).
 //
-// One workgroup (8 waves, 2 per SIMD) owns a 256 x 192 tile of C and walks E
-// in steps of 64: both operand tiles go HBM -> registers -> LDS (rows padded
-// to 144 bytes, so the 32 lanes that read one MFMA fragment hit distinct
+// One workgroup (8 waves, 2 per SIMD) owns a 256 x 384 tile of C and walks E
+// in steps of 32: both operand tiles go HBM -> registers -> LDS (rows padded
+// to 80 bytes, so the lanes that read one MFMA fragment spread over the
 // banks), double-buffered in LDS, one barrier per step. Two register sets
 // carry the loads, so each K slice is requested two steps before it is
 // stored (its L2 / Infinity Cache latency is about one step). Wave (wm, wn)
-// of the 4 x 2 grid computes a 64 x 96 sub-tile as 2 x 3 blocks of
-// v_mfma_f32_32x32x16_{bf16,f16}. Workgroup ids are remapped so each XCD gets
-// a contiguous range of logical tiles, M-tile fastest: the workgroups that
+// of the 2 x 4 grid computes a 128 x 96 sub-tile as 4 x 3 blocks of
+// v_mfma_f32_32x32x16_{bf16,f16}: per k-step 7 fragment reads feed 12 MFMAs.
+// The 2,048 x 12,288 projection of a 4,096-wide model is 8 x 32 = 256 tiles,
+// one workgroup per CU. Workgroup ids are remapped so each XCD gets a
+// contiguous range of logical tiles, M-tile fastest: the workgroups that
 // share a W tile run on one XCD at the same time and find it in its L2.
 #include <hip/hip_runtime.h>
 
@@ -50,12 +52,16 @@ struct GemmMma<_Float16> {
     }
 };
 
-constexpr int kRowBytes = kGemmBK * 2 + 16;            // one padded LDS row (64 elements + 16 B)
+constexpr int kRowBytes = kGemmBK * 2 + 16;            // one padded LDS row (32 elements + 16 B)
+constexpr int kRowChunks = kGemmBK * 2 / 16;           // 16-byte chunks of a row
 constexpr int kABytes = kGemmBM * kRowBytes;
 constexpr int kBBytes = kGemmBN * kRowBytes;
 constexpr int kStageBytes = kABytes + kBBytes;
-constexpr int kAChunks = kGemmBM * kGemmBK * 2 / 16 / kGemmThreads;   // 16-byte loads per thread
-constexpr int kBChunks = kGemmBN * kGemmBK * 2 / 16 / kGemmThreads;
+constexpr int kAChunks = kGemmBM * kRowChunks / kGemmThreads;   // 16-byte loads per thread
+constexpr int kBChunks = kGemmBN * kRowChunks / kGemmThreads;
+constexpr int kWaveM = kGemmBM / kGemmWavesM, kWaveN = kGemmBN / kGemmWavesN;   // outputs of one wave
+constexpr int kMB = kWaveM / 32, kNB = kWaveN / 32;                           // its 32 x 32 blocks
+static_assert(kMB * 32 == kWaveM && kNB * 32 == kWaveN, "waves own whole 32 x 32 blocks");
 static_assert(kAChunks * kGemmThreads * 16 == kGemmBM * kGemmBK * 2, "A tile splits evenly");
 static_assert(kBChunks * kGemmThreads * 16 == kGemmBN * kGemmBK * 2, "B tile splits evenly");
 static_assert(2 * kStageBytes <= 160 * 1024, "two stages fit in LDS");
@@ -70,7 +76,7 @@ __global__ __launch_bounds__(kGemmThreads) void qkv_proj_kernel(const uint16_t* 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, g = lane >> 5;
-    const int wm = wave & 3, wn = wave >> 2;
+    const int wm = wave % kGemmWavesM, wn = wave / kGemmWavesM;
 
     const int tiles_m = (M + kGemmBM - 1) / kGemmBM;
     const int item = xcd_remap(blockIdx.x, gridDim.x);
@@ -85,7 +91,7 @@ __global__ __launch_bounds__(kGemmThreads) void qkv_proj_kernel(const uint16_t* 
     const __amdgpu_buffer_rsrc_t rb =
         __builtin_amdgcn_make_buffer_rsrc((void*)(W + (size_t)n0 * E), (short)0, rows_b * E * 2, 0x00020000);
 
-    // thread t stages 16-byte chunks c = t + 512 i: row c / 8, chunk c % 8;
+    // thread t stages 16-byte chunks c = t + 512 i: row c / 4, chunk c % 4;
     // two register sets, so a K slice is loaded two steps before it is stored
     struct Regs {
         u32x4_t a[kAChunks], b[kBChunks];
@@ -95,12 +101,14 @@ __global__ __launch_bounds__(kGemmThreads) void qkv_proj_kernel(const uint16_t* 
 #pragma unroll
         for (int i = 0; i < kAChunks; ++i) {
             const int c = tid + kGemmThreads * i;
-            r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, (c >> 3) * E * 2 + k0 * 2 + (c & 7) * 16, 0, 0);
+            r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, (c / kRowChunks) * E * 2 + k0 * 2 + (c % kRowChunks) * 16,
+                                                      0, 0);
         }
 #pragma unroll
         for (int i = 0; i < kBChunks; ++i) {
             const int c = tid + kGemmThreads * i;
-            r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, (c >> 3) * E * 2 + k0 * 2 + (c & 7) * 16, 0, 0);
+            r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, (c / kRowChunks) * E * 2 + k0 * 2 + (c % kRowChunks) * 16,
+                                                      0, 0);
         }
     };
     auto lstore = [&](const Regs& r, int st) {
@@ -109,27 +117,27 @@ __global__ __launch_bounds__(kGemmThreads) void qkv_proj_kernel(const uint16_t* 
 #pragma unroll
         for (int i = 0; i < kAChunks; ++i) {
             const int c = tid + kGemmThreads * i;
-            *(u32x4_t*)(a + (c >> 3) * kRowBytes + (c & 7) * 16) = r.a[i];
+            *(u32x4_t*)(a + (c / kRowChunks) * kRowBytes + (c % kRowChunks) * 16) = r.a[i];
         }
 #pragma unroll
         for (int i = 0; i < kBChunks; ++i) {
             const int c = tid + kGemmThreads * i;
-            *(u32x4_t*)(b + (c >> 3) * kRowBytes + (c & 7) * 16) = r.b[i];
+            *(u32x4_t*)(b + (c / kRowChunks) * kRowBytes + (c % kRowChunks) * 16) = r.b[i];
         }
     };
 
-    f32x16_t acc[2][3];
+    f32x16_t acc[kMB][kNB];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 3; ++nb)
+        for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
 
     // A fragment: lane holds row l32 of a 32-row block, elements 8g..8g+7 of
     // the 16-wide k-step; B fragment likewise for a row of W (a column of C)
-    const int a_lane = (wm * 64 + l32) * kRowBytes + g * 16;
-    const int b_lane = (wn * 96 + l32) * kRowBytes + g * 16;
+    const int a_lane = (wm * kWaveM + l32) * kRowBytes + g * 16;
+    const int b_lane = (wn * kWaveN + l32) * kRowBytes + g * 16;
 
     const int nk = E / kGemmBK;
     auto slice = [&](int i) { return (i < nk ? i : nk - 1) * kGemmBK; };   // past the end: reload the last
@@ -138,15 +146,15 @@ __global__ __launch_bounds__(kGemmThreads) void qkv_proj_kernel(const uint16_t* 
         const char* b = lds + st * kStageBytes + kABytes + b_lane;
 #pragma unroll
         for (int ks = 0; ks < kGemmBK / 16; ++ks) {
-            v8 af[2], bf[3];
+            v8 af[kMB], bf[kNB];
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) af[mb] = *(const v8*)(a + mb * 32 * kRowBytes + ks * 32);
+            for (int mb = 0; mb < kMB; ++mb) af[mb] = *(const v8*)(a + mb * 32 * kRowBytes + ks * 32);
 #pragma unroll
-            for (int nb = 0; nb < 3; ++nb) bf[nb] = *(const v8*)(b + nb * 32 * kRowBytes + ks * 32);
+            for (int nb = 0; nb < kNB; ++nb) bf[nb] = *(const v8*)(b + nb * 32 * kRowBytes + ks * 32);
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < 3; ++nb) acc[mb][nb] = GemmMma<T>::mfma(af[mb], bf[nb], acc[mb][nb]);
+                for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = GemmMma<T>::mfma(af[mb], bf[nb], acc[mb][nb]);
         }
     };
     gload(r0, slice(0));
@@ -174,8 +182,8 @@ __global__ __launch_bounds__(kGemmThreads) void qkv_proj_kernel(const uint16_t* 
     // Q, K, V because N is a multiple of 32. Rows past M fall outside the
     // output descriptor and are dropped.
 #pragma unroll
-    for (int nb = 0; nb < 3; ++nb) {
-        const int cb = n0 + wn * 96 + nb * 32;   // first column of the block in C
+    for (int nb = 0; nb < kNB; ++nb) {
+        const int cb = n0 + wn * kWaveN + nb * 32;   // first column of the block in C
         if (cb >= NN) continue;
         const int which = cb / N;
         T* out = which == 0 ? Qo : (which == 1 ? Ko : Vo);
@@ -183,10 +191,10 @@ __global__ __launch_bounds__(kGemmThreads) void qkv_proj_kernel(const uint16_t* 
         const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(out + (size_t)m0 * N), (short)0, rows_a * N * 2, 0x00020000);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = wm * 64 + mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                const int row = wm * kWaveM + mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
                 const T x = (T)acc[mb][nb][r];
                 __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), ro,
                                                       (row * N + col) * 2, 0, 0);

@@ -140,13 +140,15 @@ ATTN_HD inline size_t decode_workspace_floats(int B, int H, int /*S_cap*/, int D
 }
 
 // ---------------------------------------------------------------------------
-// Q/K/V projection GEMM: 256 x 192 tiles of C = X W^T, 64-wide K steps,
-// eight waves in a 4 x 2 grid.
+// Q/K/V projection GEMM: 256 x 384 tiles of C = X W^T, 32-wide K steps,
+// eight waves in a 2 x 4 grid (128 x 96 outputs each).
 // ---------------------------------------------------------------------------
 constexpr int kGemmBM = 256;
-constexpr int kGemmBN = 192;
-constexpr int kGemmBK = 64;
-constexpr int kGemmThreads = 512;
+constexpr int kGemmBN = 384;
+constexpr int kGemmBK = 32;
+constexpr int kGemmWavesM = 2;
+constexpr int kGemmWavesN = 4;
+constexpr int kGemmThreads = kGemmWavesM * kGemmWavesN * 64;
 
 // Sinusoidal position encoding: 256 threads over the frequency pairs, 4
 // positions per workgroup (a 4096-position table is 1,024 workgroups: 16

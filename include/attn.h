@@ -191,7 +191,7 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
  *                          V (2), so q[m][n] = sum_e x[m][e] * w[n][e], DEVICE
  *   q, k, v : [M, H*D] each = [B, S, H, D], the inputs of attn_fwd, DEVICE
  *   dtype   : ATTN_BF16 or ATTN_F16 for all five (else ATTN_ERR_UNSUPPORTED).
- *   E must be a multiple of 64 and H*D of 32 (else ATTN_ERR_UNSUPPORTED).
+ *   E must be a multiple of 32 and H*D of 32 (else ATTN_ERR_UNSUPPORTED).
  *   M == 0 is a valid empty call. Pointers 16-byte aligned; no output may
  *   overlap an input or another output.
  */

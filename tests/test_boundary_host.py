@@ -193,7 +193,7 @@ def qkv(x=A, w=A + 0x1000000, q=A + 0x4000000, k=A + 0x5000000, v=A + 0x6000000,
 
 @pytest.mark.parametrize("kw,status,needle", [
     (dict(dtype=attn.ATTN_F32), attn.ATTN_ERR_UNSUPPORTED, "dtype"),
-    (dict(E=100), attn.ATTN_ERR_UNSUPPORTED, "multiple of 64"),
+    (dict(E=100), attn.ATTN_ERR_UNSUPPORTED, "multiple of 32"),
     (dict(H=1, D=48), attn.ATTN_ERR_UNSUPPORTED, "multiple of 32"),
     (dict(M=-1), attn.ATTN_ERR_INVALID_ARG, "sizes"),
     (dict(E=0), attn.ATTN_ERR_INVALID_ARG, "sizes"),

@@ -496,10 +496,11 @@ def test_keypad_prefill_full_size(attn):
 # ---------------------------------------------------------------------------
 QKV_CASES = [  # (B, S, E, H, D)
     (1, 300, 128, 2, 64),       # M not a multiple of the 256-row tile
-    (2, 130, 256, 3, 32),       # 3N = 288: the last 192-column tile is two-thirds empty
-    (1, 512, 512, 4, 128),      # 192-column tiles straddle the Q/K and K/V boundaries
-    (1, 1, 64, 1, 32),          # one row, one K step
-    (1, 100, 192, 2, 32),       # three K steps: the loop's second half runs once less
+    (2, 130, 256, 3, 32),       # 3N = 288: one 384-column tile, its last wave column past 3N
+    (1, 512, 512, 4, 128),      # 384-column tiles straddle the Q/K and K/V boundaries
+    (1, 1, 32, 1, 32),          # one row, one K step
+    (1, 100, 96, 2, 32),        # three K steps: the loop's second half runs once less
+    (1, 100, 192, 2, 32),
     (3, 77, 1024, 8, 64),
 ]
 
