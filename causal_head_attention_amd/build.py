@@ -24,6 +24,7 @@ SOURCES = [
     os.path.join(CSRC, "attn_api.cpp"),
     os.path.join(CSRC, "kernels", "fwd_tile.hip"),
     os.path.join(CSRC, "kernels", "fwd_row.hip"),
+    os.path.join(CSRC, "kernels", "fwd_f32.hip"),
     os.path.join(CSRC, "kernels", "decode.hip"),
     os.path.join(CSRC, "kernels", "qkv_proj.hip"),
     os.path.join(CSRC, "kernels", "pe.hip"),

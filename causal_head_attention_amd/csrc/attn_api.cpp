@@ -13,6 +13,7 @@
 // synchronous copy to the host before the launch).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -179,10 +180,12 @@ int run_fwd(const char* fn, const void* q, const void* k, const void* v, const i
                     key_mask};
     const Algo algo = algo_from_env();
     hipError_t e;
-    if (dtype != ATTN_F32 && algo != kRow)
-        e = attn::launch_fwd_tile(a, elt_of(dtype), t_stream);
-    else
+    if (algo == kRow)
         e = attn::launch_fwd_row(a, elt_of(dtype), t_stream);
+    else if (dtype == ATTN_F32)
+        e = attn::launch_fwd_f32(a, t_stream);
+    else
+        e = attn::launch_fwd_tile(a, elt_of(dtype), t_stream);
     if (e != hipSuccess)
         return fail(ATTN_ERR_HIP, std::string(fn) + ": launch failed: " + hipGetErrorString(e));
     return ok();
@@ -230,6 +233,27 @@ int attn_fwd_plan(int B, int H, int S_q, int S_kv, int D, int causal, int dtype,
     if (st != ATTN_OK) return st;
     if ((long long)B * H * S_q == 0) return ok();
     const Algo algo = algo_from_env();
+    if (algo != kRow && dtype == ATTN_F32) {
+        const int n_qblk = (S_q + attn::kF32Q - 1) / attn::kF32Q;
+        plan->kernel = 3;
+        plan->block_m = attn::kF32Q;
+        plan->block_n = attn::kF32N;
+        plan->paired = 0;
+        plan->grid = (int)((long long)B * H * n_qblk);
+        plan->threads = attn::kF32Threads;
+        plan->lds_bytes = (attn::kF32Threads / 64) * 64 * (2 + D / 2) * 4;
+        int mx = 0, mn = 1 << 30;
+        for (int qb = 0; qb < n_qblk; ++qb) {
+            const int q_last = std::min(qb * attn::kF32Q + attn::kF32Q - 1, S_q - 1);
+            const int kend = causal ? std::min(S_kv, std::max(0, q_last + 1 + S_kv - S_q)) : S_kv;
+            const int n = (kend + attn::kF32N - 1) / attn::kF32N;
+            mx = n > mx ? n : mx;
+            mn = n < mn ? n : mn;
+        }
+        plan->max_tiles = mx;
+        plan->min_tiles = mn;
+        return ok();
+    }
     const bool tile = dtype != ATTN_F32 && algo != kRow;
     if (tile) {
         const attn::TileGrid g = attn::tile_grid(B, H, S_q, causal);

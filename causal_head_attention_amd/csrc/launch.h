@@ -70,6 +70,8 @@ struct SoftmaxArgs {
 hipError_t launch_fwd_tile(const FwdArgs& a, Elt t, hipStream_t stream);
 // Row kernel: one wave per query row, any storage type.
 hipError_t launch_fwd_row(const FwdArgs& a, Elt t, hipStream_t stream);
+// fp32 kernel on the fp32 matrix cores; D in {32, 64, 128}.
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 // Split-KV decode (split + combine kernels), any storage type.
 hipError_t launch_decode(const DecodeArgs& a, Elt t, hipStream_t stream);
 // Q/K/V projection GEMM, 16-bit storage.

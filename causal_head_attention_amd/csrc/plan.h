@@ -103,9 +103,18 @@ ATTN_HD inline TileGrid tile_grid(int B, int H, int S_q, int causal, bool kv_len
 }
 
 // ---------------------------------------------------------------------------
-// Row kernel (fp32 path, and the bf16 cross-check path): one wave per query.
+// Row kernel (the ATTN_ALGO=row cross-check path, any storage type): one
+// wave per query.
 // ---------------------------------------------------------------------------
 constexpr int kRowThreads = 64;
+
+// ---------------------------------------------------------------------------
+// fp32 MFMA kernel: one workgroup per (b, h, block of kF32Q queries); its
+// eight waves take the block's kF32N-key tiles round-robin.
+// ---------------------------------------------------------------------------
+constexpr int kF32Q = 32;
+constexpr int kF32N = 32;
+constexpr int kF32Threads = 512;
 
 // ---------------------------------------------------------------------------
 // Split-KV decode.

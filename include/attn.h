@@ -276,7 +276,8 @@ const char* attn_status_string(int status);
  * without a GPU. Returns the same status attn_fwd would return for these
  * sizes (pointer checks excluded).
  *   kernel      : 0 none (empty call), 1 MFMA tile kernel (bf16 or fp16), 2 row kernel
- *   block_m     : queries per work item phase (tile kernel), 1 (row kernel)
+ *                 (ATTN_ALGO=row), 3 fp32 MFMA kernel (fp32)
+ *   block_m     : queries per work item phase (tile kernels), 1 (row kernel)
  *   block_n     : keys per KV tile
  *   paired      : 1 when each work item runs query block r and n-1-r
  *   grid        : workgroups launched

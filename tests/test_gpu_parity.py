@@ -308,13 +308,33 @@ def test_decode_matches_forward_with_one_query(attn):
         assert d <= 2e-2, (b, n, d)
 
 
+@pytest.mark.parametrize("shape", [(1, 2, 300, 300, 128, True), (2, 3, 130, 200, 64, True),
+                                   (1, 1, 77, 77, 32, False), (1, 2, 33, 1000, 64, True)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_fp32_mfma_kernel_against_row_kernel(attn, shape, monkeypatch):
+    """fp32: the MFMA kernel (default) and the row kernel (ATTN_ALGO=row) both meet the 1e-4 bar."""
+    B, H, S_q, S_kv, D, causal = shape
+    say(f"fp32 mfma vs row {shape}")
+    q, k, v = workloads.make_prefill_shape(11, torch.float32, B, H, S_q, S_kv, D)
+    ref = oracle.attn_fwd(q, k, v, causal)
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    assert attn.attn_fwd_plan(B, H, S_q, S_kv, D, causal, attn.ATTN_F32).kernel == 3
+    o_mfma = attn.attn_fwd(qc, kc, vc, causal=causal)
+    monkeypatch.setenv("ATTN_ALGO", "row")
+    assert attn.attn_fwd_plan(B, H, S_q, S_kv, D, causal, attn.ATTN_F32).kernel == 2
+    o_row = attn.attn_fwd(qc, kc, vc, causal=causal)
+    torch.cuda.synchronize()
+    check(o_mfma, ref, torch.float32, "mfma")
+    check(o_row, ref, torch.float32, "row")
+
+
 # ---------------------------------------------------------------------------
 # KV-cache prefill (chunk of queries, per-entry lengths) and its log-sum-exp.
 # LSE bars: the kernels add up the probabilities as rounded for P.V, so in
 # bf16 the row sum carries a relative error up to 2^-9 and the log of it an
 # absolute error up to about 2e-3 (plus fp32 rounding of the scores): bar
 # 4e-3; in fp16 the relative error is up to 2^-11, the log error about 5e-4:
-# bar 1e-3. fp32 inputs go through the row kernel (fp32 throughout): bar 1e-5.
+# bar 1e-3. fp32 inputs go through the fp32 MFMA kernel (fp32 throughout): bar 1e-5.
 # ---------------------------------------------------------------------------
 LSE_ATOL = {torch.bfloat16: 4e-3, torch.float16: 1e-3, torch.float32: 1e-5}
 
