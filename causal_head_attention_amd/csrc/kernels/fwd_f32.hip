@@ -108,20 +108,49 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __res
     float m_run = -INFINITY;   // running max of score * c for query qi
     float l_run = 0.f;         // this lane's share of the running sum (its 16 keys per tile)
 
-    for (int t = wave; t < ntiles; t += W) {
+    // one tile's operands: the K rows (dims as in qf), the V^T operands of
+    // the 16 key steps of each O^T block, and the key-mask bytes
+    struct TileOps {
+        f32x4_t k[NF4];
+        float v[DB][16];
+        unsigned mb[16];
+    };
+    auto load_tile = [&](int t, TileOps& x) {
         const int k0 = t * kF32N;
-        // K operand: key k0 + l32, the same dims as qf
-        f32x4_t kf[NF4];
 #pragma unroll
         for (int m = 0; m < NF4; ++m)
-            kf[m] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    rk, (k0 + l32) * row_bytes + (8 * m + 4 * g) * 4, 0, 0));
-        unsigned mb[16];
+            x.k[m] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rk, (k0 + l32) * row_bytes + (8 * m + 4 * g) * 4, 0, 0));
+        // V^T operand of key step j of block db: key k0 + 8*(j/4) + 4g + j%4, dim 32*db + l32
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int key = k0 + 8 * (j >> 2) + 4 * g + (j & 3);
+                x.v[db][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                           rv, key * row_bytes + (32 * db + l32) * 4, 0, 0));
+            }
         if constexpr (KMASK) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                mb[r] = __builtin_amdgcn_raw_buffer_load_b8(rm, k0 + 8 * (r >> 2) + 4 * g + (r & 3), 0, 0);
+                x.mb[r] = __builtin_amdgcn_raw_buffer_load_b8(rm, k0 + 8 * (r >> 2) + 4 * g + (r & 3), 0, 0);
         }
+    };
+    // where the registers hold two tiles (D = 32; D = 64 without the mask
+    // bytes) the next tile's operands load while this one computes
+    constexpr bool kPrefetch = D <= 32 || (D <= 64 && !KMASK);
+    TileOps cur, nxt;
+    if (wave < ntiles) load_tile(wave, cur);   // in flight with the Q loads
+
+    for (int t = wave; t < ntiles; t += W) {
+        const int k0 = t * kF32N;
+        if constexpr (kPrefetch) {
+            if (t + W < ntiles) load_tile(t + W, nxt);
+        } else {
+            if (t != wave) load_tile(t, cur);
+        }
+        const f32x4_t (&kf)[NF4] = cur.k;
+        const unsigned (&mb)[16] = cur.mb;
         f32x16_t s;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = 0.f;
@@ -164,17 +193,10 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __res
 
         // O^T += V^T . P^T; k-step j: key k0 + 8*(j/4) + 4g + j%4, dim 32*db + l32
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            float va[16];
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int key = k0 + 8 * (j >> 2) + 4 * g + (j & 3);
-                va[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                      rv, key * row_bytes + (32 * db + l32) * 4, 0, 0));
-            }
-#pragma unroll
-            for (int j = 0; j < 16; ++j) acc[db] = mfma_f32(va[j], x[j], acc[db]);
-        }
+            for (int j = 0; j < 16; ++j) acc[db] = mfma_f32(cur.v[db][j], x[j], acc[db]);
+        if constexpr (kPrefetch) cur = nxt;
     }
 
     // ---- merge the eight waves' states
