@@ -284,7 +284,7 @@ def main() -> int:
                              "flop_per_launch": flop, "mean_launch_us": round(mean * 1e3, 2),
                              "median_launch_us": round(statistics.median(ms) * 1e3, 2)}}
 
-    kv = f16 = kp = qp = pe_leg = sm_leg = f32 = nc = None
+    kv = f16 = kp = qp = pe_leg = sm_leg = f32 = nc = s4k = None
     if not args.skip_extras:
         kc_cfg = workloads.BF16_KVCACHE
         log("KV-cache prefill: generating inputs")
@@ -380,6 +380,17 @@ def main() -> int:
                       f"bf16 non-causal prefill B={pc.B} H={pc.H} S={pc.S_q} D={pc.D} (the bf16_s2048 data, "
                       f"seed {pc.seed}); cold, 20 calls")
         del onc
+
+        # bf16 causal S=4096 with Q, K ~ N(0, 4^2): logits up to about +-100,
+        # the softmax-stability workload at twice the sequence length
+        c4k = workloads.BF16_S4096
+        log("S=4096 prefill")
+        q4, k4, v4 = (t.to(dev) for t in workloads.make_prefill(c4k))
+        o4 = torch.empty_like(q4)
+        s4k = mfma_leg(cold_ms(lambda: attn.attn_fwd(q4, k4, v4, o4, causal=True)), c4k.flops(),
+                       f"bf16 causal prefill B={c4k.B} H={c4k.H} S={c4k.S_q} D={c4k.D}, Q and K ~ N(0, 4^2) "
+                       f"(seed {c4k.seed}); cold, 20 calls")
+        del q4, k4, v4, o4
 
         # the fp32 configuration (fp32 MFMA kernel), against the dense fp32
         # matrix peak
@@ -488,6 +499,7 @@ def main() -> int:
         "masked_softmax": sm_leg,
         "fp32_prefill": f32,
         "noncausal_prefill": nc,
+        "s4096_prefill": s4k,
         "cpu_baseline": cpu,
         "parity": parity,
     }

@@ -64,7 +64,11 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __res
     constexpr int NF4 = D / 8;   // 16-byte pieces of a lane's K or Q row (dims 8m + 4g .. +3)
     constexpr int DB = D / 32;   // 32-row blocks of O^T
     constexpr int W = kF32Threads / 64;
-    __shared__ __attribute__((aligned(16))) float xs[W * 64 * (2 + DB * 16)];
+    // merge slots: per wave and lane, m, l and the DB*16 accumulator registers,
+    // at an odd stride so that lanes writing one register, and the threads of
+    // the final pass reading consecutive dims, fall in distinct banks
+    constexpr int SL = 2 + DB * 16 + 1;
+    __shared__ __attribute__((aligned(16))) float xs[W * 64 * SL];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -200,13 +204,13 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __res
     }
 
     // ---- merge the eight waves' states
-    float* slot = xs + wave * 64 * (2 + DB * 16);
-    slot[lane] = m_run;
-    slot[64 + lane] = l_run;
+    float* slot = xs + (wave * 64 + lane) * SL;
+    slot[0] = m_run;
+    slot[1] = l_run;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) slot[128 + (db * 16 + r) * 64 + lane] = acc[db][r];
+        for (int r = 0; r < 16; ++r) slot[2 + db * 16 + r] = acc[db][r];
     __syncthreads();
 
     // output (query qq, dim d): lane qq + 32 * ((d % 32) / 4 % 2), register
@@ -220,15 +224,15 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __res
         const int reg = (d >> 5) * 16 + 4 * (dd >> 3) + (dd & 3);
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < W; ++w) M = fmaxf(M, xs[w * 64 * (2 + DB * 16) + qq]);
+        for (int w = 0; w < W; ++w) M = fmaxf(M, xs[(w * 64 + qq) * SL]);
         const float mu = M == -INFINITY ? 0.f : M;
         float L = 0.f, o = 0.f;
 #pragma unroll
         for (int w = 0; w < W; ++w) {
-            const float* sw = xs + w * 64 * (2 + DB * 16);
-            const float a = __builtin_amdgcn_exp2f(sw[qq] - mu);   // 0 for a wave that saw no key
-            L += a * (sw[64 + qq] + sw[64 + qq + 32]);
-            o += a * sw[128 + reg * 64 + ln];
+            const float* sw = xs + w * 64 * SL;
+            const float a = __builtin_amdgcn_exp2f(sw[qq * SL] - mu);   // 0 for a wave that saw no key
+            L += a * (sw[qq * SL + 1] + sw[(qq + 32) * SL + 1]);
+            o += a * sw[ln * SL + 2 + reg];
         }
         // a row that sees no key (a KV-cache entry shorter than the chunk) is 0
         O[((size_t)((size_t)b * S_q + q0 + qq) * H + h) * D + d] = L > 0.f ? o / L : 0.f;
