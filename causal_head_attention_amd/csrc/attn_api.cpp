@@ -9,6 +9,8 @@
 // section 4.1). An environment switch picks the implementation, as the
 // depthwise-convolution page's section 6.2 suggests for bisecting:
 //   ATTN_ALGO=auto (default) | tile | row
+// (auto and tile: the MFMA kernels -- the 16-bit tile kernel or the fp32
+// kernel; row: the per-query row kernel for every storage type)
 // and ATTN_CHECK=1 turns on a debug check of the device-side lengths (a
 // synchronous copy to the host before the launch).
 #include <hip/hip_runtime.h>
