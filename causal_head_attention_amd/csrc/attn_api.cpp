@@ -243,7 +243,7 @@ int attn_fwd_plan(int B, int H, int S_q, int S_kv, int D, int causal, int dtype,
         plan->paired = 0;
         plan->grid = (int)((long long)B * H * n_qblk);
         plan->threads = attn::kF32Threads;
-        plan->lds_bytes = (attn::kF32Threads / 64) * 64 * (2 + D / 2 + 1) * 4;
+        plan->lds_bytes = ((attn::kF32Threads / 64) * 64 * (2 + D / 2 + 1) + attn::kF32Q * (attn::kF32Threads / 64)) * 4;
         int mx = 0, mn = 1 << 30;
         for (int qb = 0; qb < n_qblk; ++qb) {
             const int q_last = std::min(qb * attn::kF32Q + attn::kF32Q - 1, S_q - 1);

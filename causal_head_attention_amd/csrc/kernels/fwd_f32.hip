@@ -69,6 +69,7 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __res
     // the final pass reading consecutive dims, fall in distinct banks
     constexpr int SL = 2 + DB * 16 + 1;
     __shared__ __attribute__((aligned(16))) float xs[W * 64 * SL];
+    __shared__ float wts[kF32Q][W];   // per query: each wave's merge weight, already divided by the sum
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -213,6 +214,32 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __res
         for (int r = 0; r < 16; ++r) slot[2 + db * 16 + r] = acc[db][r];
     __syncthreads();
 
+    // per query: the common maximum M, the waves' weights 2^(m_w - M) / L
+    // with L the total sum, and the log-sum-exp
+    if (tid < kF32Q) {
+        const int qq = tid;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < W; ++w) M = fmaxf(M, xs[(w * 64 + qq) * SL]);
+        const float mu = M == -INFINITY ? 0.f : M;
+        float a[W], L = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const float* sw = xs + w * 64 * SL;
+            a[w] = __builtin_amdgcn_exp2f(sw[qq * SL] - mu);   // 0 for a wave that saw no key
+            L += a[w] * (sw[qq * SL + 1] + sw[(qq + 32) * SL + 1]);
+        }
+        // a row that sees no key (a KV-cache entry shorter than the chunk) is 0
+        const float inv = L > 0.f ? 1.0f / L : 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) wts[qq][w] = a[w] * inv;
+        // log of the softmax denominator, natural units: ln 2 * (M + log2 L)
+        if (lse && q0 + qq < S_q)
+            lse[((size_t)b * H + h) * S_q + q0 + qq] =
+                L > 0.f ? (M + __builtin_log2f(L)) * 0.69314718055994531f : -INFINITY;
+    }
+    __syncthreads();
+
     // output (query qq, dim d): lane qq + 32 * ((d % 32) / 4 % 2), register
     // 4 * ((d % 32) / 8) + d % 4 of block d / 32; consecutive threads take
     // consecutive dims so the stores coalesce
@@ -222,24 +249,10 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __res
         const int dd = d & 31;
         const int ln = qq + 32 * ((dd >> 2) & 1);
         const int reg = (d >> 5) * 16 + 4 * (dd >> 3) + (dd & 3);
-        float M = -INFINITY;
+        float o = 0.f;
 #pragma unroll
-        for (int w = 0; w < W; ++w) M = fmaxf(M, xs[(w * 64 + qq) * SL]);
-        const float mu = M == -INFINITY ? 0.f : M;
-        float L = 0.f, o = 0.f;
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-            const float* sw = xs + w * 64 * SL;
-            const float a = __builtin_amdgcn_exp2f(sw[qq * SL] - mu);   // 0 for a wave that saw no key
-            L += a * (sw[qq * SL + 1] + sw[(qq + 32) * SL + 1]);
-            o += a * sw[ln * SL + 2 + reg];
-        }
-        // a row that sees no key (a KV-cache entry shorter than the chunk) is 0
-        O[((size_t)((size_t)b * S_q + q0 + qq) * H + h) * D + d] = L > 0.f ? o / L : 0.f;
-        // log of the softmax denominator, natural units: ln 2 * (M + log2 L)
-        if (lse && d == 0)
-            lse[((size_t)b * H + h) * S_q + q0 + qq] =
-                L > 0.f ? (M + __builtin_log2f(L)) * 0.69314718055994531f : -INFINITY;
+        for (int w = 0; w < W; ++w) o = __builtin_fmaf(wts[qq][w], xs[(w * 64 + ln) * SL + 2 + reg], o);
+        O[((size_t)((size_t)b * S_q + q0 + qq) * H + h) * D + d] = o;
     }
 }
 

@@ -121,7 +121,7 @@ def test_plan_non_causal_and_fp32():
     # head sees j + 1 tiles of 32 keys
     p = attn.attn_fwd_plan(2, 8, 512, 512, 64, True, attn.ATTN_F32)
     assert p.kernel == 3 and p.grid == 2 * 8 * 16 and (p.block_m, p.block_n) == (32, 32)
-    assert (p.max_tiles, p.min_tiles) == (16, 1) and p.threads == 512 and p.lds_bytes == 8 * 64 * 35 * 4
+    assert (p.max_tiles, p.min_tiles) == (16, 1) and p.threads == 512 and p.lds_bytes == (8 * 64 * 35 + 32 * 8) * 4
     p = attn.attn_fwd_plan(1, 2, 100, 300, 32, True, attn.ATTN_F32)     # bottom-right: block 0 sees 232 keys
     assert p.grid == 2 * 4 and (p.max_tiles, p.min_tiles) == (10, 8)
     p = attn.attn_fwd_plan(1, 1, 70, 50, 128, False, attn.ATTN_F32)
