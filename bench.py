@@ -44,19 +44,25 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def sha256(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+def build_sha256(path: str) -> str:
+    """Fingerprint of a kernel as built: its source text and the device flags
+    it is compiled with (include paths left out, as they differ per machine)."""
+    from causal_head_attention_amd import build as B
+    name = os.path.basename(path)
+    flags = [f for f in B.COMMON if f != "-I" and not os.path.isabs(f)]
+    flags += B.DEVICE_FLAGS + B.PER_SOURCE_FLAGS.get(name, [])
+    return hashlib.sha256(open(path, "rb").read() + " ".join(flags).encode()).hexdigest()
 
 
 def measured_traffic(kernel: str, src: str):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or None
-    if they were taken on a different version of the kernel source."""
+    if they were taken on a different build of the kernel (source or flags)."""
     try:
         doc = json.load(open(TRAFFIC_JSON))
         ent = doc[kernel]
     except (OSError, KeyError, ValueError):
         return None
-    if ent.get("source_sha256") != sha256(src):
+    if ent.get("build_sha256") != build_sha256(src):
         return None
     return ent.get("bytes_per_launch")
 
@@ -139,9 +145,9 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, copy_mib: int = 256) -
     db = round(((split["fetch_kib"] + comb["fetch_kib"]) * f_scale + (split["write_kib"] + comb["write_kib"]) * w_scale)
                * 1024)
     out["fwd_tile"] = {"bytes_per_launch": pb, "algorithmic_bytes": 4 * 2048 * 32 * 128 * 2,
-                            "counters_kib": prefill, "source_sha256": sha256(TILE_SRC)}
+                            "counters_kib": prefill, "build_sha256": build_sha256(TILE_SRC)}
     out["decode"] = {"bytes_per_launch": db, "counters_kib": {"split": split, "combine": comb},
-                     "source_sha256": sha256(DECODE_SRC), "note": "one call = split + combine kernels"}
+                     "build_sha256": build_sha256(DECODE_SRC), "note": "one call = split + combine kernels"}
     out["scales"] = {"fetch": f_scale, "write": w_scale}
     return out
 

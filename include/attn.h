@@ -43,6 +43,11 @@
  *  - Arithmetic: scores, softmax and accumulation in fp32 whatever the
  *    storage type (MMHA page, section 3.3); the scale 1/sqrt(D) is an fp32
  *    value. bf16 results are rounded to nearest even.
+ *  - Inputs are finite numbers. The bf16 / fp16 forward kernel assumes no
+ *    NaN (its row maximum skips NaN handling): a NaN in the visible part of
+ *    Q, K or V gives an unspecified output row. Memory past the valid rows
+ *    (cache rows past a length, padded tails) is never used and may hold
+ *    anything, NaN included.
  */
 #ifndef ATTN_GFX950_H
 #define ATTN_GFX950_H
