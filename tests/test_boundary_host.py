@@ -307,3 +307,29 @@ def test_kernels_use_no_scratch():
     assert any("fwd_tile_kernel" in k for k in res), "report lists the tile kernel"
     bad = {k: v for k, v in res.items() if v.get("ScratchSize", 0) or v.get("VGPRs Spill", 0)}
     assert not bad, bad
+
+
+def _bench_module():
+    import importlib.util
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(root, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_traffic_record_matches_the_current_build_and_goes_stale(monkeypatch, tmp_path):
+    """profiles/traffic.json is keyed by each kernel's source and device flags:
+    the committed record matches this build, and a changed flag or source nulls it."""
+    from causal_head_attention_amd import build as B
+    bench = _bench_module()
+    import json
+    doc = json.load(open(bench.TRAFFIC_JSON))
+    assert bench.measured_traffic("fwd_tile", bench.TILE_SRC) == doc["fwd_tile"]["bytes_per_launch"]
+    assert bench.measured_traffic("decode", bench.DECODE_SRC) == doc["decode"]["bytes_per_launch"]
+    monkeypatch.setitem(B.PER_SOURCE_FLAGS, "fwd_tile.hip", [])
+    assert bench.measured_traffic("fwd_tile", bench.TILE_SRC) is None
+    monkeypatch.undo()
+    edited = tmp_path / "decode.hip"
+    edited.write_bytes(open(bench.DECODE_SRC, "rb").read() + b"\n// edited\n")
+    assert bench.measured_traffic("decode", str(edited)) is None
