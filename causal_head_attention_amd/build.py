@@ -23,6 +23,7 @@ LIB = os.path.join(PKG, "libattn.so")
 SOURCES = [
     os.path.join(CSRC, "attn_api.cpp"),
     os.path.join(CSRC, "kernels", "fwd_tile.hip"),
+    os.path.join(CSRC, "kernels", "fwd_prefill.hip"),
     os.path.join(CSRC, "kernels", "fwd_row.hip"),
     os.path.join(CSRC, "kernels", "fwd_f32.hip"),
     os.path.join(CSRC, "kernels", "decode.hip"),

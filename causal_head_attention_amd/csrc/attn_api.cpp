@@ -186,8 +186,10 @@ int run_fwd(const char* fn, const void* q, const void* k, const void* v, const i
         e = attn::launch_fwd_row(a, elt_of(dtype), t_stream);
     else if (dtype == ATTN_F32)
         e = attn::launch_fwd_f32(a, t_stream);
-    else
+    else if (key_mask)
         e = attn::launch_fwd_tile(a, elt_of(dtype), t_stream);
+    else
+        e = attn::launch_fwd_prefill(a, elt_of(dtype), t_stream);
     if (e != hipSuccess)
         return fail(ATTN_ERR_HIP, std::string(fn) + ": launch failed: " + hipGetErrorString(e));
     return ok();
@@ -265,7 +267,7 @@ int attn_fwd_plan(int B, int H, int S_q, int S_kv, int D, int causal, int dtype,
         plan->paired = g.paired;
         plan->grid = (int)g.n_items;
         plan->threads = attn::kTileThreads;
-        plan->lds_bytes = attn::tile_lds_bytes(D);
+        plan->lds_bytes = attn::prefill_lds_bytes(D);   // attn_fwd runs the prefill kernel
         int mx = 0, mn = 1 << 30;
         for (int p = 0; p < g.items_per_bh; ++p) {
             const int qa = g.n_qblk - 1 - p;

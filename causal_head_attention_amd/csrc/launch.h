@@ -68,6 +68,8 @@ struct SoftmaxArgs {
 
 // MFMA tile kernel for 16-bit storage (BF16 or F16); D in {32, 64, 128}.
 hipError_t launch_fwd_tile(const FwdArgs& a, Elt t, hipStream_t stream);
+// MFMA prefill kernel for 16-bit storage without a key mask; D in {32, 64, 128}.
+hipError_t launch_fwd_prefill(const FwdArgs& a, Elt t, hipStream_t stream);
 // Row kernel: one wave per query row, any storage type.
 hipError_t launch_fwd_row(const FwdArgs& a, Elt t, hipStream_t stream);
 // fp32 kernel on the fp32 matrix cores; D in {32, 64, 128}.

@@ -64,6 +64,23 @@ ATTN_HD constexpr int tile_stage_bytes(int D) {
 }
 ATTN_HD constexpr int tile_lds_bytes(int D) { return tile_stage_bytes(D) + kMaskStageBytes; }
 
+// Prefill kernel (attn_fwd, attn_fwd_kvcache; fwd_prefill.hip): the same
+// items, waves and tiles as above, with K and V tiles loaded straight into a
+// ring of kPrefillStages LDS stages. K rows are padded by 16 bytes; V rows are
+// unpadded (their 16-byte chunks swizzled instead). The key-half merge goes
+// through its own region in rounds of prefill_merge_db(D) 32-row blocks of
+// the accumulator, one record of prefill_merge_rec_floats(D) floats per lane.
+constexpr int kPrefillStages = 3;
+ATTN_HD constexpr int prefill_krow_bytes(int D) { return 2 * D + 16; }
+ATTN_HD constexpr int prefill_k_stage_bytes(int D) { return kTileN * (2 * D + 16); }
+ATTN_HD constexpr int prefill_v_stage_bytes(int D) { return kTileN * 2 * D; }
+ATTN_HD constexpr int prefill_merge_db(int D) { return D / 32 < 2 ? D / 32 : 2; }
+ATTN_HD constexpr int prefill_merge_rec_floats(int D) { return 16 * prefill_merge_db(D) + 4; }
+ATTN_HD constexpr int prefill_lds_bytes(int D) {
+    return kPrefillStages * (prefill_k_stage_bytes(D) + prefill_v_stage_bytes(D)) +
+           4 * 64 * prefill_merge_rec_floats(D) * 4;
+}
+
 // Number of KV tiles query block qb must visit.
 ATTN_HD inline int tiles_for_block(int qb, int S_q, int S_kv, int causal) {
     const int n_all = (S_kv + kTileN - 1) / kTileN;

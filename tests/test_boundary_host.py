@@ -101,7 +101,8 @@ def test_plan_bf16_s2048():
     assert (p.kernel, p.block_m, p.block_n, p.paired, p.threads) == (1, 128, 64, 1, 512)
     assert p.grid == 32 * 8                 # 16 query blocks per head, paired
     assert p.max_tiles == p.min_tiles == 34  # (2r+2) + (2(15-r)+2) for every r
-    assert p.lds_bytes <= 160 * 1024 // 2    # two workgroups fit in one CU's LDS
+    # one workgroup per CU: three K/V stages (rows padded / swizzled) and the merge region
+    assert p.lds_bytes == 3 * (64 * 272 + 64 * 256) + 4 * 64 * 36 * 4 <= 160 * 1024
 
 
 def test_plan_bf16_s4096_and_odd_block_counts():
