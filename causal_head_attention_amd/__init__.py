@@ -314,9 +314,23 @@ def attn_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, seq
         raise TypeError("q and the caches must share one dtype")
     if o is None:
         o = torch.empty_like(q)
+    else:
+        _dev_tensor("o", o, 4)
+        if tuple(o.shape) != tuple(q.shape) or o.dtype != q.dtype or o.device != q.device:
+            raise ValueError("o must match q in shape, dtype and device")
     need = attn_decode_workspace_bytes(B, H, S_cap, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    else:
+        if not isinstance(workspace, torch.Tensor):
+            raise TypeError("workspace must be a torch.Tensor")
+        if not workspace.is_cuda or workspace.device != q.device:
+            raise ValueError("workspace must be a GPU tensor on q's device")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        if workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
+                             f"{need} needed")
     _set_stream(q.device)
     _check(load().attn_decode(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), seqlens.data_ptr(),
                            o.data_ptr(), B, H, S_cap, D, _dtype_code(q), workspace.data_ptr(),

@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -307,9 +308,22 @@ int attn_fwd_kvcache(const void* q, const void* kcache, const void* vcache, cons
                    dtype, true);
 }
 
+// Per-call flag value for the decode kernel: a process-wide call counter
+// passed through the SplitMix64 finaliser (Steele, Lea and Flood, 2014), so
+// consecutive calls get unrelated 64-bit values; never zero, the value a
+// consumed flag is reset to.
+static unsigned long long next_decode_tag() {
+    static std::atomic<unsigned long long> calls{0};
+    unsigned long long z = calls.fetch_add(1, std::memory_order_relaxed) + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return z ? z : 1ull;
+}
+
 size_t attn_decode_workspace_bytes(int B, int H, int S_cap, int D) {
     if (B <= 0 || H <= 0 || S_cap <= 0 || D <= 0) return 0;
-    return attn::decode_workspace_floats(B, H, S_cap, D) * sizeof(float);
+    return attn::decode_workspace_bytes(B, H, S_cap, D);
 }
 
 int attn_decode_plan(int B, int H, int S_cap, int D, int dtype, attn_decode_plan_t* plan) {
@@ -327,6 +341,13 @@ int attn_decode_plan(int B, int H, int S_cap, int D, int dtype, attn_decode_plan
         return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: one sequence's cache spans more than 2 GiB");
     if (tensor_bytes(B, S_cap, H, D, elem_size(dtype)) < 0 || attn::decode_records(B) * H > 0x7fffffffLL)
         return fail(ATTN_ERR_INVALID_ARG, "attn_decode: sizes overflow");
+    // the kernel counts the valid keys of all sequences, laid end to end, in 32 bits
+    if ((long long)B * S_cap > 0x7fffffffLL)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: B * S_cap = " + std::to_string((long long)B * S_cap) +
+                                              " keys in all, beyond 32-bit token counts");
+    // a merge addresses up to kDecodeSplitWGs consecutive records with 32-bit offsets
+    if ((long long)attn::kDecodeSplitWGs * H * attn::decode_record_floats(D) * 4 > 0x7fffffffLL)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: H=" + std::to_string(H) + " heads beyond the merge's 32-bit offsets");
     plan->split_workgroups = attn::kDecodeSplitWGs;
     plan->records = (int)attn::decode_records(B);
     plan->threads = attn::kDecodeThreads;
@@ -368,8 +389,8 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
     }
 
     attn::DecodeArgs a{q, kcache, vcache, seqlens, o, B, H, S_cap, D,
-                       (float)(1.0f / std::sqrt((float)D)) * 1.4426950408889634f, (float*)workspace, ev_start,
-                       ev_stop};
+                       (float)(1.0f / std::sqrt((float)D)) * 1.4426950408889634f, workspace, ev_start,
+                       ev_stop, next_decode_tag()};
     const hipError_t e = attn::launch_decode(a, elt_of(dtype), t_stream);
     if (e != hipSuccess)
         return fail(ATTN_ERR_HIP, std::string("attn_decode: launch failed: ") + hipGetErrorString(e));

@@ -1,6 +1,6 @@
 // decode.hip -- single-query attention against a KV cache, split along the keys.
 //
-// Split kernel: the valid keys of all sequences, laid end to end, form one
+// One kernel. The valid keys of all sequences, laid end to end, form one
 // token space; workgroup w of kDecodeSplitWGs (one per CU) streams an equal
 // share of it, for ALL heads, one segment per sequence its share touches.
 // The cache is [B, S_cap, H, D], so one token's H head rows are one
@@ -9,14 +9,16 @@
 // the workgroup together sweep whole token rows. A head's D elements sit in
 // one group of D*sizeof(T)/16 lanes ("a row"), so the dot product reduces
 // with DPP inside the row and the head's softmax state (max, sum, D
-// accumulators) lives in that row; each (segment, h) leaves one partial
-// record in the workspace. Equal shares keep every CU streaming until the
-// end (a fixed number of keys per workgroup left a partly idle second wave
-// of workgroups and many that only found their sequence already ended).
-// Combine kernel: per (b, h), rescale each segment's partial state to the
-// common maximum, add, divide by the common sum, in one pass over the
-// records. Segments are merged in a fixed order, so results do not change
-// from run to run.
+// accumulators) lives in that row. Equal shares keep every CU streaming
+// until the end (a fixed number of keys per workgroup left a partly idle
+// second wave of workgroups and many that only found their sequence
+// already ended).
+// A segment that holds a whole sequence divides by its sum and writes the
+// output. Any other segment leaves one partial record per head; the wave
+// that finds all segments of its sequence done (flags, below) rescales each
+// record to the common maximum, adds, and divides by the common sum, in
+// segment order, so results do not change from run to run. The merge runs
+// on the CUs that just finished streaming, without a second launch.
 //
 // Method: per-query (GEMV-shaped) mapping, dot products and softmax fused
 // with the score row kept on chip ("Hand-written Masked Multi-Head
@@ -76,6 +78,11 @@ constexpr int kNonTemporal = 2;   // buffer-load cache policy: nt
 
 __device__ __forceinline__ int clamp_len(int n, int S_cap) { return n < 0 ? 0 : (n > S_cap ? S_cap : n); }
 
+// Values every lane of a wave holds alike but the compiler cannot prove so
+// (they come out of LDS): taken from lane 0 into scalar registers, so that
+// buffer descriptors built from them need no per-lane loop.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // DPP lane moves inside 16-lane rows (gfx9 encodings).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -106,17 +113,16 @@ struct DecCfg {
 };
 
 // Sum over the workgroup; every thread gets it. `red` holds one slot per wave.
-template <int NT = kDecodeThreads>
-__device__ __forceinline__ long long block_sum(long long x, long long* red) {
+__device__ __forceinline__ int block_sum(int x, int* red) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
     __syncthreads();   // earlier readers of red are done
     if (lane == 0) red[wave] = x;
     __syncthreads();
-    long long t = 0;
+    int t = 0;
 #pragma unroll
-    for (int w = 0; w < NT / 64; ++w) t += red[w];
+    for (int w = 0; w < kDecodeWaves; ++w) t += red[w];
     return t;
 }
 
@@ -127,59 +133,257 @@ __device__ __forceinline__ long long block_sum(long long x, long long* red) {
 // workgroup w's range, which ends where w+1's begins, reaches into b.
 __device__ __forceinline__ int record_of(int w, int b) { return w + b; }
 
-template <typename T, int D>
-__global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(const T* __restrict__ q,
-                                                                      const T* __restrict__ kc,
-                                                                      const T* __restrict__ vc,
-                                                                      const int32_t* __restrict__ seqlens,
-                                                                      float* __restrict__ ws, int B, int H, int S_cap,
-                                                                      float c) {
-    using C = DecCfg<T, D>;
-    constexpr int E = C::E, LPH = C::LPH, HPI = C::HPI;
-    constexpr bool k16 = sizeof(T) == 2;   // bf16 or fp16: packed v_dot2 paths
-    __shared__ long long red[kDecodeThreads / 64];
-    __shared__ long long incl_s[kDecodeScanLds];   // inclusive prefix sums of the lengths
+// The lane's E fp32 outputs converted to the storage type (round to
+// nearest even) and packed for one 16-byte store.
+template <typename T, int E>
+__device__ __forceinline__ u32x4_t pack_row(const float (&x)[E]) {
+    u32x4_t r;
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = __builtin_bit_cast(unsigned, x[e]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const unsigned lo = __builtin_bit_cast(unsigned short, (T)x[2 * i]);
+            const unsigned hi = __builtin_bit_cast(unsigned short, (T)x[2 * i + 1]);
+            r[i] = lo | (hi << 16);
+        }
+    }
+    return r;
+}
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int w = blockIdx.x, G = gridDim.x;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Cache-policy bits of buffer loads and stores on this chip: sc1 makes an
+// access coherent at device scope (stores write through the per-XCD L2,
+// loads do not take a line another XCD's L2 may have made stale), the same
+// encoding the compiler gives device-scope atomic loads and stores.
+constexpr int kDeviceScope = 16;
+
+// Partial records move between workgroups that may sit on different XCDs.
+// They are written and read with device-scope accesses, so the hand-off
+// needs no cache write-back or invalidation (which would be one whole-L2
+// operation per wave), only a wait for the writer's stores to complete.
+__device__ __forceinline__ void store_record(__amdgpu_buffer_rsrc_t r, int off, f32x4_t x) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), r, off, 0, kDeviceScope);
+}
+__device__ __forceinline__ f32x4_t load_record(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceScope));
+}
+
+// Partial merge of sequence b's records for one head over the segments
+// first, first + step, ... below ns, in that order: rescale each segment's
+// state to the running maximum and add. This lane owns dims E*sub ..
+// E*sub+E-1 of head h. Segment s is record w0 + s + b.
+template <typename T, int D>
+__device__ __forceinline__ void merge_part(const float* __restrict__ ws, int b, int h, int sub, int H, int w0,
+                                           int first, int step, int ns, float& M, float& L,
+                                           float (&A)[DecCfg<T, D>::E]) {
+    constexpr int E = DecCfg<T, D>::E, RF = decode_record_floats(D), PER = kDecodeMergeBatch;
+    const int stride = H * RF * 4;   // bytes between consecutive records
+    // records w0+b .. w0+b+ns-1, head h; offsets fit 32 bits (checked on the host)
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(ws + (size_t)record_of(w0, b) * H * RF), (short)0, ns * stride, 0x00020000);
+    const int base = h * RF * 4;
+    for (int s0 = first; s0 < ns; s0 += PER * step) {
+        f32x4_t ml[PER], xx[PER][E / 4];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int s = s0 + j * step < ns ? s0 + j * step : s0;   // in range; unused past ns
+            const int off = base + s * stride;
+            ml[j] = load_record(rr, off);
+#pragma unroll
+            for (int v = 0; v < E / 4; ++v) xx[j][v] = load_record(rr, off + 4 * (4 + E * sub + 4 * v));
+        }
+        __builtin_amdgcn_sched_barrier(0);   // every load of the batch in flight first
+        float mn = M;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) mn = fmaxf(mn, ml[j][0]);   // finite: segment s0 exists
+        const float a = __builtin_amdgcn_exp2f(M - mn);           // 0 while M is -inf
+        L *= a;
+#pragma unroll
+        for (int e = 0; e < E; ++e) A[e] *= a;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const float wj = s0 + j * step < ns ? __builtin_amdgcn_exp2f(ml[j][0] - mn) : 0.f;
+            L = __builtin_fmaf(wj, ml[j][1], L);
+#pragma unroll
+            for (int e = 0; e < E; ++e) A[e] = __builtin_fmaf(wj, xx[j][e / 4][e % 4], A[e]);
+        }
+        M = mn;
+    }
+}
+
+// Workgroups 0 .. kDecodeSplitWGs-1 stream (one per CU): (1) prefix sums
+// of the clamped lengths and the zero rows of empty sequences, (2) the
+// workgroup's token range and the first sequence in it, (3) per segment and
+// head group the streamed dot products and online softmax; a segment that
+// holds a whole sequence writes the output rows, any other one writes its
+// partial records and (4) raises its flags. The workgroups after them merge:
+// each takes (sequence, head group) pairs cut into several segments, its
+// waves split the segments, wait for their flags, merge them, and the
+// workgroup combines the waves' partial states in LDS.
+//
+// Hand-off: a segment's wave sets its flag for (segment, head group) to this
+// call's tag once its records are complete (device-scope stores, then a wait
+// for their completion); the merging wave waits until its segments' flags
+// carry the tag, merges, and resets them to zero, so every flag is zero again
+// when the kernel ends (a replay with the same tag finds zeros; stale garbage
+// matches a tag with odds 2^-64). Streaming workgroups never wait, and
+// merging ones wait only for streaming ones, which have lower indices:
+// workgroups start in index order, so each one waited for is already running
+// or done. The wait is bounded all the same (kDecodeSpinLimit polls); if it
+// ever ran out, the rows would be NaN.
+template <typename T, int D>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const T* __restrict__ q, const T* __restrict__ kc,
+                                                                const T* __restrict__ vc,
+                                                                const int32_t* __restrict__ seqlens,
+                                                                T* __restrict__ o, float* __restrict__ ws,
+                                                                unsigned long long* __restrict__ flags, int B, int H,
+                                                                int S_cap, float c, unsigned long long tag) {
+    using C = DecCfg<T, D>;
+    constexpr int E = C::E, LPH = C::LPH, HPI = C::HPI, RF = decode_record_floats(D);
+    constexpr bool k16 = sizeof(T) == 2;   // bf16 or fp16: packed v_dot2 paths
+    __shared__ int red[kDecodeWaves];
+    __shared__ int incl_s[kDecodeScanLds];   // inclusive prefix sums of the lengths
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
+    const int w = blockIdx.x;
     const bool scan_in_lds = B <= kDecodeScanLds;
 
     // (1) prefix sums of the clamped lengths (the token space), one read of seqlens
-    long long run = 0;
+    int run = 0;
     for (int base = 0; base < B; base += kDecodeThreads) {
         const int bb = base + tid;
-        const long long len = bb < B ? clamp_len(seqlens[bb], S_cap) : 0;
-        long long incl = len;
+        const int len = bb < B ? clamp_len(seqlens[bb], S_cap) : 0;
+        int incl = len;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
-            const long long y = __shfl_up(incl, o);
+            const int y = __shfl_up(incl, o);
             if (lane >= o) incl += y;
         }
         __syncthreads();
         if (lane == 63) red[wave] = incl;
         __syncthreads();
-        long long wpre = 0, ctot = 0;
+        int wpre = 0, ctot = 0;
 #pragma unroll
-        for (int x = 0; x < kDecodeThreads / 64; ++x) {
+        for (int x = 0; x < kDecodeWaves; ++x) {
             ctot += red[x];
             if (x < wave) wpre += red[x];
         }
         if (scan_in_lds && bb < B) incl_s[bb] = incl + wpre + run;
         run += ctot;
     }
-    const long long Ttot = run;
+    const int Ttot = uni(run);
+    __syncthreads();   // incl_s complete
+    constexpr int G = kDecodeSplitWGs;   // streaming workgroups
+    const int n_groups = (H + HPI - 1) / HPI;
+    const int sub = lane % LPH, hl = lane / LPH;
+
+    if (w >= G) {   // uniform: a merging workgroup
+        if (Ttot == 0) return;
+        __shared__ float part_acc[kDecodeWaves][64 * E];
+        __shared__ float part_ml[kDecodeWaves][64][2];
+        __shared__ int part_ok[kDecodeWaves];
+        const int Ct = (Ttot + G - 1) / G;
+        const int m = w - G, GM = gridDim.x - G;
+        for (int p = m; p < B * n_groups; p += GM) {
+            const int b = p / n_groups, grp = p % n_groups;
+            int Pb;
+            int len;
+            if (scan_in_lds) {
+                Pb = b > 0 ? incl_s[b - 1] : 0;
+                len = (int)(incl_s[b] - Pb);
+            } else {
+                int t = 0;
+                for (int bb = tid; bb < b; bb += kDecodeThreads) t += clamp_len(seqlens[bb], S_cap);
+                Pb = block_sum(t, red);
+                len = clamp_len(seqlens[b], S_cap);
+            }
+            Pb = uni(Pb);
+            len = uni(len);
+            if (len == 0) continue;   // uniform
+            const int w0 = (int)(Pb / Ct), ns = (int)((Pb + len - 1) / Ct) - w0 + 1;
+            if (ns == 1) continue;   // uniform: one workgroup held it whole
+            // this wave's segments: wave, wave + kDecodeWaves, ...
+            bool ready = false;
+            for (int spin = 0; spin < kDecodeSpinLimit && !ready; ++spin) {
+                bool all = true;
+                for (int s0 = wave; s0 < ns; s0 += 64 * kDecodeWaves) {
+                    const int s = s0 + kDecodeWaves * lane;
+                    const unsigned long long f = __hip_atomic_load(
+                        &flags[(size_t)record_of(w0 + (s < ns ? s : s0), b) * H + grp], __ATOMIC_RELAXED,
+                        __HIP_MEMORY_SCOPE_AGENT);
+                    all = __all(s >= ns || f == tag) && all;
+                }
+                ready = all;
+                if (!ready) __builtin_amdgcn_s_sleep(8);
+            }
+            const int h = grp * HPI + hl;
+            float M = -INFINITY, L = 0.f, A[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) A[e] = 0.f;
+            if (ready) merge_part<T, D>(ws, b, h < H ? h : 0, sub, H, w0, wave, kDecodeWaves, ns, M, L, A);
+            part_ml[wave][lane][0] = M;
+            part_ml[wave][lane][1] = L;
+#pragma unroll
+            for (int e = 0; e < E; ++e) part_acc[wave][lane * E + e] = A[e];
+            if (lane == 0) part_ok[wave] = ready;
+            __syncthreads();
+            if (wave == 0 && h < H) {
+                // the waves' partial states, in wave order
+                bool ok = true;
+                float Mt = -INFINITY;
+#pragma unroll
+                for (int v = 0; v < kDecodeWaves; ++v) {
+                    ok = ok && part_ok[v];
+                    Mt = fmaxf(Mt, part_ml[v][lane][0]);   // finite: wave 0 has segment 0
+                }
+                float Lt = 0.f, out[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) out[e] = 0.f;
+#pragma unroll
+                for (int v = 0; v < kDecodeWaves; ++v) {
+                    const float wv = __builtin_amdgcn_exp2f(part_ml[v][lane][0] - Mt);   // 0 for a wave with none
+                    Lt = __builtin_fmaf(wv, part_ml[v][lane][1], Lt);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) out[e] = __builtin_fmaf(wv, part_acc[v][lane * E + e], out[e]);
+                }
+#pragma unroll
+                for (int e = 0; e < E; ++e) out[e] = ok ? out[e] / Lt : __builtin_nanf("");
+                *(u32x4_t*)(o + ((size_t)b * H + h) * D + E * sub) = pack_row<T, E>(out);
+            }
+            for (int s = wave + kDecodeWaves * lane; s < ns; s += 64 * kDecodeWaves)
+                __hip_atomic_store(&flags[(size_t)record_of(w0 + s, b) * H + grp], 0ull, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();   // the partial-state LDS is reused by the next pair
+        }
+        return;
+    }
+
+    // a sequence with no keys gives a zero row; workgroup w writes those of
+    // sequences w, w + G, ...
+    const int n16 = H * D * (int)sizeof(T) / 16;   // 16-byte chunks per sequence's output
+    for (int b = w; b < B; b += G) {
+        const int len =
+            scan_in_lds ? incl_s[b] - (b > 0 ? incl_s[b - 1] : 0) : clamp_len(seqlens[b], S_cap);
+        if (len == 0) {   // uniform
+            const u32x4_t zero = {0u, 0u, 0u, 0u};
+            u32x4_t* out = (u32x4_t*)(o + (size_t)b * H * D);
+            for (int i = tid; i < n16; i += kDecodeThreads) out[i] = zero;
+        }
+    }
     if (Ttot == 0) return;   // uniform
-    const long long Ct = (Ttot + G - 1) / G;
-    const long long lo = (long long)w * Ct;
-    const long long hi = lo + Ct < Ttot ? lo + Ct : Ttot;
+    const int Ct = (Ttot + G - 1) / G;
+    const int lo = w * Ct;
+    const int hi = lo + Ct < Ttot ? lo + Ct : Ttot;
     if (lo >= hi) return;   // uniform
 
     // (2) first sequence reaching into [lo, hi): the number of sequences
     // that end at or before lo, and where it starts
     int b_first;
-    long long P;
+    int P;
     if (scan_in_lds) {
-        __syncthreads();
         int n = 0, span = B;   // binary search: incl_s is non-decreasing
         while (span > 0) {
             const int half = span >> 1;
@@ -193,23 +397,23 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(const T* _
         b_first = n;
         P = n > 0 ? incl_s[n - 1] : 0;
     } else {
-        long long n_before = 0, t_before = 0;
+        int n_before = 0, t_before = 0;
         run = 0;
         for (int base = 0; base < B; base += kDecodeThreads) {
             const int bb = base + tid;
-            const long long len = bb < B ? clamp_len(seqlens[bb], S_cap) : 0;
-            long long incl = len;
+            const int len = bb < B ? clamp_len(seqlens[bb], S_cap) : 0;
+            int incl = len;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
-                const long long y = __shfl_up(incl, o);
+                const int y = __shfl_up(incl, o);
                 if (lane >= o) incl += y;
             }
             __syncthreads();
             if (lane == 63) red[wave] = incl;
             __syncthreads();
-            long long wpre = 0, ctot = 0;
+            int wpre = 0, ctot = 0;
 #pragma unroll
-            for (int x = 0; x < kDecodeThreads / 64; ++x) {
+            for (int x = 0; x < kDecodeWaves; ++x) {
                 ctot += red[x];
                 if (x < wave) wpre += red[x];
             }
@@ -219,20 +423,26 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(const T* _
             }
             run += ctot;
         }
-        b_first = (int)block_sum<kDecodeThreads>(n_before, red);
-        P = block_sum<kDecodeThreads>(t_before, red);
+        b_first = (int)block_sum(n_before, red);
+        P = block_sum(t_before, red);
     }
+    b_first = uni(b_first);
+    P = uni(P);
 
-    // (3) one segment per sequence the range touches
-    const int sub = lane % LPH, hl = lane / LPH;
+    // (3) one segment per sequence the range touches; each wave streams the
+    // keys of its head groups in batches of NB, all loads of a batch in flight
+    // together.
+    constexpr int NB = kDecodeBatch;
     const int key_bytes = H * D * (int)sizeof(T);
-    const int n_groups = (H + HPI - 1) / HPI;
+    const int P0 = P;   // where sequence b_first starts
+    int last_b = b_first;
     for (int b = b_first; b < B && P < hi; ++b) {
-        const int len = scan_in_lds ? (int)(incl_s[b] - P) : clamp_len(seqlens[b], S_cap);
+        const int len = uni(scan_in_lds ? incl_s[b] - P : clamp_len(seqlens[b], S_cap));
         if (len > 0) {
-            const int k0 = (int)((lo > P ? lo : P) - P);
-            const int k1 = (int)((hi < P + len ? hi : P + len) - P);
-            const int rec_id = record_of(w, b);
+            last_b = b;
+            const int k0 = (lo > P ? lo : P) - P;
+            const int k1 = (hi < P + len ? hi : P + len) - P;
+            const bool whole = k0 == 0 && k1 == len;   // uniform
             // descriptors over sequence b's rows that end at key k1: loads
             // past it return zeros without touching memory
             const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -256,26 +466,33 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(const T* _
                 float m_run = -INFINITY, l_run = 0.f, acc[E];
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[e] = 0.f;
-                for (int kb = k0; kb < k1; kb += kDecodeBatch) {
-                    u32x4_t kr[kDecodeBatch], vr[kDecodeBatch];
+                for (int kb = k0; kb < k1; kb += NB) {
+                    u32x4_t kr[NB], vr[NB];
+                    // read-once stream: non-temporal, so the loads do not allocate in
+                    // the caches (and do not evict whatever is resident there); K
+                    // first, so the scores can start while V is still arriving
 #pragma unroll
-                    for (int it = 0; it < kDecodeBatch; ++it) {
-                        const int off = lane_off + (kb + it) * key_bytes;
-                        // read-once stream: non-temporal, so the loads do not allocate
-                        // in the caches (and do not evict whatever is resident there)
-                        kr[it] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kNonTemporal);
-                        vr[it] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, kNonTemporal);
-                    }
-                    float s[kDecodeBatch];
+                    for (int it = 0; it < NB; ++it)
+                        kr[it] = __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off + (kb + it) * key_bytes, 0,
+                                                                       kNonTemporal);
 #pragma unroll
-                    for (int it = 0; it < kDecodeBatch; ++it) {
+                    for (int it = 0; it < NB; ++it)
+                        vr[it] = __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off + (kb + it) * key_bytes, 0,
+                                                                       kNonTemporal);
+                    // keep all 2*NB loads ahead of their first use: left alone, the
+                    // scheduler sinks loads toward their uses to save registers and
+                    // the batch degenerates to one or two loads in flight
+                    __builtin_amdgcn_sched_barrier(0);
+                    float s[NB];
+#pragma unroll
+                    for (int it = 0; it < NB; ++it) {
                         float d = 0.f;
                         if constexpr (k16) {
 #pragma unroll
-                            for (int w = 0; w < 4; ++w) {
+                            for (int x = 0; x < 4; ++x) {
                                 // scalar copies first (bit-casting a vector-element lvalue
                                 // reads element 0 with this compiler)
-                                const unsigned kw = kr[it][w], qw = qx[w];
+                                const unsigned kw = kr[it][x], qw = qx[x];
                                 d = Elem<T>::dot2(__builtin_bit_cast(typename Elem<T>::v2, kw),
                                                   __builtin_bit_cast(typename Elem<T>::v2, qw), d);
                             }
@@ -286,17 +503,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(const T* _
                         d = row_sum<LPH>(d) * c;
                         s[it] = (kb + it < k1) ? d : -INFINITY;
                     }
-                    // slots past the length may hold anything (even NaN): their
-                    // probability is 0, and their values must not reach the sums
-                    if (kb + kDecodeBatch > k1) {
-                        const u32x4_t zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-                        for (int it = 0; it < kDecodeBatch; ++it)
-                            if (kb + it >= k1) vr[it] = zero;
-                    }
+                    // keys past k1 read as zeros (descriptor bound): their
+                    // probability is 0 and their V rows add nothing
                     float mx = s[0];
 #pragma unroll
-                    for (int it = 1; it < kDecodeBatch; ++it) mx = fmaxf(mx, s[it]);
+                    for (int it = 1; it < NB; ++it) mx = fmaxf(mx, s[it]);
                     const float m_new = fmaxf(m_run, mx);   // finite: key kb < k1 is valid
                     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
                     l_run *= alpha;
@@ -307,7 +518,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(const T* _
                         // pairs of keys: P rounded to the storage type, V pairs packed per head dim,
                         // one v_dot2 per (pair, dim); the sum adds the same rounded P
 #pragma unroll
-                        for (int it = 0; it < kDecodeBatch; it += 2) {
+                        for (int it = 0; it < NB; it += 2) {
                             typedef typename Elem<T>::v2 v2;
                             const v2 pp = {(T)__builtin_amdgcn_exp2f(s[it] - m_new),
                                            (T)__builtin_amdgcn_exp2f(s[it + 1] - m_new)};
@@ -322,7 +533,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(const T* _
                         }
                     } else {
 #pragma unroll
-                        for (int it = 0; it < kDecodeBatch; ++it) {
+                        for (int it = 0; it < NB; ++it) {
                             const float p = __builtin_amdgcn_exp2f(s[it] - m_new);
                             l_run += p;
 #pragma unroll
@@ -330,124 +541,65 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(const T* _
                         }
                     }
                 }
-                // one partial record per (segment, h): [max, sum, D accumulators]
                 if (h_ok) {
-                    float* rec = ws + ((size_t)rec_id * H + h) * (D + 2);
-                    if (sub == 0) {
-                        rec[0] = m_run;
-                        rec[1] = l_run;
-                    }
+                    if (whole) {
+                        // the whole sequence in one segment: its output row, with
+                        // the merge's arithmetic for one record (acc / l)
+                        float out[E];
 #pragma unroll
-                    for (int e = 0; e < E; ++e) rec[2 + E * sub + e] = acc[e];
+                        for (int e = 0; e < E; ++e) out[e] = acc[e] / l_run;
+                        *(u32x4_t*)(o + ((size_t)b * H + h) * D + E * sub) = pack_row<T, E>(out);
+                    } else {
+                        // one partial record per (segment, h): [max, sum, 0, 0, D accumulators]
+                        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+                            (void*)(ws + (size_t)record_of(w, b) * H * RF), (short)0, H * RF * 4, 0x00020000);
+                        const int off = h * RF * 4;
+                        if (sub == 0) store_record(rw, off, f32x4_t{m_run, l_run, 0.f, 0.f});
+#pragma unroll
+                        for (int v = 0; v < E / 4; ++v)
+                            store_record(rw, off + 4 * (4 + E * sub + 4 * v),
+                                         f32x4_t{acc[4 * v], acc[4 * v + 1], acc[4 * v + 2], acc[4 * v + 3]});
+                    }
                 }
             }
         }
         P += len;
     }
-}
 
-// Combine: one workgroup per (b, h). Sequence b's segments belong to split
-// workgroups w0..w1; thread (part, d) merges head dim d of the segments
-// s = part, part + NP, ... online (running maximum), with all of its loads
-// issued before the first use, and the NP parts are merged in LDS. Fixed
-// order throughout, so the result is deterministic.
-template <typename T, int D>
-__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const float* __restrict__ ws,
-                                                                         const int32_t* __restrict__ seqlens,
-                                                                         T* __restrict__ o, int B, int H, int S_cap,
-                                                                         int G) {
-    constexpr int NP = kCombineThreads / D;       // parts
-    constexpr int PER = 16;                       // segments in flight per thread per round
-    __shared__ float part_m[NP], part_l[NP];
-    __shared__ float part_acc[NP][D];
-    const int bh = blockIdx.x;
-    const int b = bh / H, h = bh % H;
-    const int tid = threadIdx.x, lane = tid & 63;
-    T* out = o + (size_t)bh * D;   // [B, 1, H, D]: the (b, h) row is bh
-    // token-space geometry (total, start of sequence b, its length): every
-    // wave sums the lengths itself, so no barrier precedes the record loads
-    long long all = 0, before = 0, mine = 0;
-    for (int bb = lane; bb < B; bb += 64) {
-        const long long l = clamp_len(seqlens[bb], S_cap);
-        all += l;
-        if (bb < b) before += l;
-        if (bb == b) mine = l;
-    }
-#pragma unroll
-    for (int x = 32; x >= 1; x >>= 1) {
-        all += __shfl_xor(all, x);
-        before += __shfl_xor(before, x);
-        mine += __shfl_xor(mine, x);
-    }
-    const long long Ttot = all, Pb = before;
-    const int len = (int)mine;
-    if (len == 0) {   // uniform; a sequence with no keys gives a zero row
-        for (int d = tid; d < D; d += kCombineThreads) out[d] = (T)0.f;
-        return;
-    }
-    const long long Ct = (Ttot + G - 1) / G;
-    const int w0 = (int)(Pb / Ct), w1 = (int)((Pb + len - 1) / Ct);
-    const int ns = w1 - w0 + 1;
-    const size_t stride = (size_t)H * (D + 2);   // between consecutive records
-    const float* rec = ws + ((size_t)record_of(w0, b) * H + h) * (D + 2);
-
-    const int d = tid % D, part = tid / D;
-    float M = -INFINITY, L = 0.f, A = 0.f;
-    for (int s0 = part; s0 < ns; s0 += NP * PER) {
-        float mm[PER], ll[PER], xx[PER];
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int s = s0 + j * NP;
-            const bool ok = s < ns;
-            mm[j] = ok ? rec[(size_t)s * stride] : -INFINITY;
-            ll[j] = ok ? rec[(size_t)s * stride + 1] : 0.f;
-            xx[j] = ok ? rec[(size_t)s * stride + 2 + d] : 0.f;
+    // (4) flags. Only the first and the last segment of the range can be
+    // part of a longer sequence: the first when that sequence starts before
+    // lo, the last when it runs past hi.
+    const bool first_cut = P0 < lo;   // sequence b_first starts before the range
+    const bool last_cut = P > hi;     // sequence last_b runs past it
+    if (!first_cut && !last_cut) return;   // uniform: every segment was whole
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's records are complete
+    if (lane == 0) {
+        for (int grp = wave; grp < n_groups; grp += kDecodeWaves) {
+            if (first_cut)
+                __hip_atomic_store(&flags[(size_t)record_of(w, b_first) * H + grp], tag, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            if (last_cut && !(last_b == b_first && first_cut))
+                __hip_atomic_store(&flags[(size_t)record_of(w, last_b) * H + grp], tag, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
-        float mn = M;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) mn = fmaxf(mn, mm[j]);   // finite: segment s0 exists
-        const float a = __builtin_amdgcn_exp2f(M - mn);        // 0 while M is -inf
-        L *= a;
-        A *= a;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const float wj = __builtin_amdgcn_exp2f(mm[j] - mn);   // 0 for absent segments
-            L = __builtin_fmaf(wj, ll[j], L);
-            A = __builtin_fmaf(wj, xx[j], A);
-        }
-        M = mn;
-    }
-    if (d == 0) {
-        part_m[part] = M;
-        part_l[part] = L;
-    }
-    part_acc[part][d] = A;
-    __syncthreads();
-    if (tid < D) {
-        float Mt = part_m[0];
-#pragma unroll
-        for (int p = 1; p < NP; ++p) Mt = fmaxf(Mt, part_m[p]);
-        float Lt = 0.f, t = 0.f;
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const float wp = __builtin_amdgcn_exp2f(part_m[p] - Mt);   // 0 for a part with no segment
-            Lt = __builtin_fmaf(wp, part_l[p], Lt);
-            t = __builtin_fmaf(wp, part_acc[p][tid], t);
-        }
-        out[tid] = (T)(t / Lt);
     }
 }
 
 template <typename T, int D>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
-    hipExtLaunchKernelGGL((decode_split_kernel<T, D>), dim3(kDecodeSplitWGs), dim3(kDecodeThreads), 0, stream,
-                          a.ev_start, nullptr, 0, (const T*)a.q, (const T*)a.kcache, (const T*)a.vcache, a.seqlens,
-                          a.workspace, a.B, a.H, a.S_cap, a.scale_log2);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipExtLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)(a.H * a.B)), dim3(kCombineThreads), 0,
-                          stream, nullptr, a.ev_stop, 0, (const float*)a.workspace, a.seqlens, (T*)a.o, a.B, a.H,
-                          a.S_cap, kDecodeSplitWGs);
+    char* ws = (char*)a.workspace;
+    unsigned long long* flags = (unsigned long long*)(ws + decode_records_bytes(a.B, a.H, a.D));
+    // merging workgroups: one per (sequence, head group) pair, at most kDecodeMergeWGs
+    const long long pairs = (long long)a.B * ((a.H + DecCfg<T, D>::HPI - 1) / DecCfg<T, D>::HPI);
+    const unsigned grid = kDecodeSplitWGs + (unsigned)(pairs < kDecodeMergeWGs ? pairs : kDecodeMergeWGs);
+    if (a.ev_start || a.ev_stop)   // timed: events on the kernel itself
+        hipExtLaunchKernelGGL((decode_kernel<T, D>), dim3(grid), dim3(kDecodeThreads), 0, stream,
+                              a.ev_start, a.ev_stop, 0, (const T*)a.q, (const T*)a.kcache, (const T*)a.vcache,
+                              a.seqlens, (T*)a.o, (float*)ws, flags, a.B, a.H, a.S_cap, a.scale_log2, a.tag);
+    else   // the plain launch, which stream capture records
+        hipLaunchKernelGGL((decode_kernel<T, D>), dim3(grid), dim3(kDecodeThreads), 0, stream,
+                           (const T*)a.q, (const T*)a.kcache, (const T*)a.vcache, a.seqlens, (T*)a.o, (float*)ws,
+                           flags, a.B, a.H, a.S_cap, a.scale_log2, a.tag);
     return hipGetLastError();
 }
 

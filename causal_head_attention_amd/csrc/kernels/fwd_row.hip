@@ -1,8 +1,9 @@
 // fwd_row.hip -- one wave per query row: the per-query mapping.
 //
-// Serves the fp32 forward (gfx950 has no reduced-precision fp32 matrix
-// path, and fp32 inputs are held to a 1e-4 absolute bound) and, under
-// ATTN_ALGO=row, a bf16 / fp16 cross-check of the tile kernel. Each iteration takes
+// The independent cross-check path: under ATTN_ALGO=row every forward entry
+// point (all three storage types, key mask and KV-cache forms) runs here
+// instead of the matrix-core kernels, so tests can compare two kernels that
+// share no tiling. Each iteration takes
 // 64 keys: lane j computes the score of key j0+j (one K row, read in
 // 16-byte pieces), the wave reduces max and sum with cross-lane shuffles, and the
 // lanes switch to owning head dims to accumulate p_j * V[j0+j, :] with

@@ -40,9 +40,12 @@ struct DecodeArgs {
     void* o;
     int B, H, S_cap, D;
     float scale_log2;
-    float* workspace;   // decode_workspace_floats(B, H, S_cap, D) floats
-    hipEvent_t ev_start;   // optional: recorded when the split kernel starts
-    hipEvent_t ev_stop;    // optional: recorded when the combine kernel ends
+    void* workspace;   // decode_workspace_bytes(B, H, S_cap, D) bytes
+    hipEvent_t ev_start;   // optional: recorded when the kernel starts
+    hipEvent_t ev_stop;    // optional: recorded when the kernel ends
+    // nonzero value that marks this call's flags in the workspace; flags
+    // left by earlier calls are zero, and garbage matches it with odds 2^-64
+    unsigned long long tag;
 };
 
 struct QkvArgs {
@@ -74,7 +77,7 @@ hipError_t launch_fwd_prefill(const FwdArgs& a, Elt t, hipStream_t stream);
 hipError_t launch_fwd_row(const FwdArgs& a, Elt t, hipStream_t stream);
 // fp32 kernel on the fp32 matrix cores; D in {32, 64, 128}.
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
-// Split-KV decode (split + combine kernels), any storage type.
+// Split-KV decode (one kernel: split, then the merge by the last finisher), any storage type.
 hipError_t launch_decode(const DecodeArgs& a, Elt t, hipStream_t stream);
 // Q/K/V projection GEMM, 16-bit storage.
 hipError_t launch_qkv_proj(const QkvArgs& a, Elt t, hipStream_t stream);

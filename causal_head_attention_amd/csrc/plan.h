@@ -134,24 +134,29 @@ constexpr int kF32N = 32;
 constexpr int kF32Threads = 512;
 
 // ---------------------------------------------------------------------------
-// Split-KV decode.
+// Split-KV decode, one kernel.
 //   The valid keys of all sequences, laid end to end, form one token space
-//   of T = sum of the lengths. Split workgroup w (of kDecodeSplitWGs) takes
+//   of T = sum of the lengths. Workgroup w (of kDecodeSplitWGs) takes
 //   tokens [w*C, (w+1)*C) with C = ceil(T / kDecodeSplitWGs): every
 //   workgroup streams the same number of keys, and a range that crosses a
 //   sequence boundary is processed as one segment per sequence. Each
 //   workgroup covers ALL heads of its keys: each wave owns a group of heads,
 //   each load instruction reads one token's rows of those heads (contiguous
-//   bytes). A segment (w, b) leaves one partial record per head at record
-//   index w + b (unique: see decode.hip).
-//   Combine kernel: one workgroup per (b, h).
+//   bytes). A segment that holds a whole sequence writes its output rows
+//   directly; any other segment (w, b) leaves one partial record per head at
+//   record index w + b (unique: see decode.hip) and raises one flag per head
+//   group. Merging workgroups, launched after the streaming ones, take the
+//   (sequence, head group) pairs cut into several segments and merge their
+//   records once the segments' flags are raised.
 // ---------------------------------------------------------------------------
 constexpr int kDecodeWaves = 8;
 constexpr int kDecodeSplitWGs = 256;      // one per CU of the chip
 constexpr int kDecodeBatch = 16;          // keys whose loads are in flight together
 constexpr int kDecodeThreads = kDecodeWaves * 64;
-constexpr int kCombineThreads = 512;
 constexpr int kDecodeScanLds = 1024;      // length prefix sums kept in LDS up to this many sequences
+constexpr int kDecodeMergeWGs = 256;      // merging workgroups at most (one per (sequence, head group) pair)
+constexpr int kDecodeMergeBatch = 8;      // records whose loads are in flight together in a merge
+constexpr int kDecodeSpinLimit = 1 << 22;  // polls of the segments' flags before a merge gives up (seconds)
 
 // Partial records: segment (w, b) uses index w + b, so at most
 // kDecodeSplitWGs + B - 1 of them.
@@ -159,10 +164,18 @@ ATTN_HD inline long long decode_records(int B) {
     return (long long)kDecodeSplitWGs + B - 1;
 }
 
-// Workspace: per (record, h) one float max, one float sum, D float
-// accumulators. It does not depend on the cache capacity.
-ATTN_HD inline size_t decode_workspace_floats(int B, int H, int /*S_cap*/, int D) {
-    return (size_t)decode_records(B) * (size_t)H * (size_t)(D + 2);
+// One partial record per (record, h): max, sum, two pad floats, then D
+// accumulators, so the accumulators start 16-byte aligned.
+ATTN_HD constexpr int decode_record_floats(int D) { return D + 4; }
+
+// Workspace: the records, then one 64-bit flag per (record, h) (a head group
+// uses the slot of its group index, and there are never more groups than
+// heads). It does not depend on the cache capacity.
+ATTN_HD inline size_t decode_records_bytes(int B, int H, int D) {
+    return (size_t)decode_records(B) * (size_t)H * (size_t)decode_record_floats(D) * sizeof(float);
+}
+ATTN_HD inline size_t decode_workspace_bytes(int B, int H, int /*S_cap*/, int D) {
+    return decode_records_bytes(B, H, D) + (size_t)decode_records(B) * (size_t)H * sizeof(unsigned long long);
 }
 
 // ---------------------------------------------------------------------------

@@ -146,9 +146,11 @@ int attn_fwd_mask(const void* q, const void* k, const void* v, const uint8_t* ke
 
 /*
  * attn_decode_workspace_bytes -- device workspace attn_decode needs for
- * these sizes: (256 + B - 1) * H partial records of D + 2 floats (max, sum
- * and D accumulators). It does not depend on S_cap. Returns 0 for invalid
- * or empty sizes.
+ * these sizes: (256 + B - 1) * H partial records of D + 4 floats (max, sum,
+ * two pad floats, D accumulators), then (256 + B - 1) * H 64-bit flags. It
+ * does not depend on S_cap. Returns 0 for invalid or empty sizes. The size
+ * and the planning split follow the host-side shape checks of the
+ * depthwise-convolution page, section 6.2.
  */
 size_t attn_decode_workspace_bytes(int B, int H, int S_cap, int D);
 
@@ -159,7 +161,9 @@ size_t attn_decode_workspace_bytes(int B, int H, int S_cap, int D);
  * afterwards (rows spanning several blocks need one common normaliser:
  * "Week-4 CUDA notes" page, section 2.2). The valid keys of all sequences,
  * laid end to end, are cut into 256 equal ranges, one workgroup each, so
- * the work is balanced whatever the length mix.
+ * the work is balanced whatever the length mix. One kernel launch: a
+ * sequence cut into several ranges is merged by extra workgroups of the
+ * same launch once the ranges' flags in the workspace are raised.
  *
  *   q, o            : [B, 1, H, D]
  *   kcache, vcache  : [B, S_cap, H, D]
@@ -168,15 +172,21 @@ size_t attn_decode_workspace_bytes(int B, int H, int S_cap, int D);
  *                     causal mask admits all of them). It is read on the
  *                     device only: a value <= 0 produces an all-zero output
  *                     row and a value > S_cap is treated as S_cap. Slots at
- *                     or beyond the length are never read.
+ *                     or beyond the length are never read, so they may
+ *                     hold anything, NaN included.
  *   workspace       : DEVICE buffer of at least
  *                     attn_decode_workspace_bytes(B, H, S_cap, D) bytes,
- *                     16-byte aligned; contents on entry are ignored and on
- *                     return are unspecified. Calls that share a workspace
- *                     must be ordered on one stream.
+ *                     16-byte aligned; any contents on entry are fine (each
+ *                     call marks its flags with its own 64-bit value, and a
+ *                     stale word matches it with odds 2^-64). Every flag a
+ *                     call raises is zero again when it ends, so a captured
+ *                     launch replayed from a graph is also correct. Calls
+ *                     that share a workspace must be ordered on one stream:
+ *                     overlapping calls on one workspace race.
  *   dtype           : ATTN_F32, ATTN_BF16 or ATTN_F16 for q, caches and o.
  *   D must be 32, 64 or 128. B == 0 or H == 0 is a valid empty call;
- *   S_cap must be >= 1. o may not overlap any other argument.
+ *   S_cap must be >= 1 and B * S_cap below 2^31. o may not overlap any
+ *   other argument.
  * A too-small or NULL workspace returns ATTN_ERR_WORKSPACE.
  */
 int attn_decode(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens,
@@ -252,7 +262,11 @@ int attn_sinusoidal_pe(float* pe, int S, int d_model, int pos0);
 /*
  * attn_set_stream -- set the HIP stream (a hipStream_t passed as void*) that
  * later calls from THIS thread enqueue on; NULL selects the null stream.
- * attn_get_stream returns the current thread's stream.
+ * attn_get_stream returns the current thread's stream. The host side of a
+ * launch (arguments prepared, kernel enqueued, no copies on the path) is the
+ * host launch function of the depthwise-convolution page, section 3.2, with
+ * the data kept on the device as the "CUDA first principles" page, section
+ * 2.1 asks.
  */
 int attn_set_stream(void* hip_stream);
 void* attn_get_stream(void);
@@ -268,11 +282,14 @@ void* attn_get_stream(void);
  */
 int attn_set_timing_events(void* start, void* stop);
 
-/* Reason for the last non-OK status returned on this thread ("" if none).
+/* Reason for the last non-OK status returned on this thread ("" if none):
+ * a rejected shape or argument (the host-side checks of the
+ * depthwise-convolution page, section 6.2) or the runtime's message for a
+ * launch error read right after the launch (that page, section 3.2).
  * The pointer stays valid until the next call into the library on this thread. */
 const char* attn_last_error(void);
 
-/* Static name of a status code ("ATTN_OK", ...). */
+/* Static name of a status code ("ATTN_OK", ...), for the messages above. */
 const char* attn_status_string(int status);
 
 /*

@@ -158,8 +158,9 @@ def test_xcd_remap_is_a_bijection_with_contiguous_ranges(n):
 # Decode boundary
 # ---------------------------------------------------------------------------
 def test_decode_workspace_and_plan():
-    # one record per (workgroup, sequence) segment: at most 256 + B - 1, per head
-    assert attn.attn_decode_workspace_bytes(16, 32, 4096, 128) == (256 + 15) * 32 * 130 * 4
+    # one record per (workgroup, sequence) segment: at most 256 + B - 1, per
+    # head: max, sum, two pad floats, D accumulators; then a 64-bit flag each
+    assert attn.attn_decode_workspace_bytes(16, 32, 4096, 128) == (256 + 15) * 32 * (132 * 4 + 8)
     assert attn.attn_decode_workspace_bytes(16, 32, 1, 128) == attn.attn_decode_workspace_bytes(16, 32, 4096, 128)
     assert attn.attn_decode_workspace_bytes(0, 32, 4096, 128) == 0
     p = attn.attn_decode_plan(16, 32, 4096, 128, attn.ATTN_BF16)

@@ -293,6 +293,102 @@ def test_decode_workspace_reused_across_shapes_ignores_stale_contents(attn):
         assert torch.all(o.cpu()[sl <= 0] == 0)
 
 
+def _decode_case(seed, B, H, S_cap, D, dtype, lens):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, 1, H, D, generator=g).to(dtype)
+    kc = torch.randn(B, S_cap, H, D, generator=g).to(dtype)
+    vc = torch.randn(B, S_cap, H, D, generator=g).to(dtype)
+    return torch.tensor(lens, dtype=torch.int32), q, kc, vc
+
+
+def test_decode_leaves_every_merge_flag_zero(attn):
+    """A sequence cut into several segments is merged after its segments
+    raise per-call flags in the workspace; the merging workgroup resets them.
+    Garbage in flag words (here 0xFF bytes) is never taken for a raised flag,
+    and from a zeroed flag area every call leaves all flags zero again, so a
+    later call, or a replay of the same launch, never finds one left raised."""
+    B, H, S_cap, D = 6, 8, 3000, 128
+    lens = [3000, 1, 2999, 0, 1500, 2048]   # long ones span several workgroups each
+    sl, q, kc, vc = _decode_case(420, B, H, S_cap, D, torch.bfloat16, lens)
+    need = attn.attn_decode_workspace_bytes(B, H, S_cap, D)
+    records_bytes = (256 + B - 1) * H * (D + 4) * 4   # the flags follow the records
+    assert need == records_bytes + (256 + B - 1) * H * 8
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    ref = oracle.attn_decode(q, kc, vc, sl.numpy())
+    flags = ws[records_bytes:].view(torch.int64)
+    for it in range(4):
+        say(f"decode flags reset, call {it}")
+        o = attn.attn_decode(q.cuda(), kc.cuda(), vc.cuda(), sl.cuda(), workspace=ws)
+        torch.cuda.synchronize()
+        check(o, ref, torch.bfloat16, f"decode flags call {it}")
+        if it == 0:
+            flags.zero_()
+            torch.cuda.synchronize()
+        else:
+            assert int((flags != 0).sum()) == 0
+
+
+def test_decode_graph_replays_with_new_lengths(attn):
+    """The decode launch captured once in a HIP graph and replayed with new
+    lengths written into the same seqlens buffer between replays (the
+    per-call flag value is frozen into the graph): every replay matches the
+    eager call on the same lengths, bitwise."""
+    B, H, S_cap, D = 8, 8, 2048, 128
+    g = torch.Generator().manual_seed(421)
+    q = torch.randn(B, 1, H, D, generator=g).bfloat16().cuda()
+    kc = torch.randn(B, S_cap, H, D, generator=g).bfloat16().cuda()
+    vc = torch.randn(B, S_cap, H, D, generator=g).bfloat16().cuda()
+    sl = torch.zeros(B, dtype=torch.int32, device="cuda")
+    o = torch.empty_like(q)
+    ws = torch.zeros(attn.attn_decode_workspace_bytes(B, H, S_cap, D), dtype=torch.uint8, device="cuda")
+    sl.copy_(torch.randint(1, S_cap + 1, (B,), generator=g, dtype=torch.int32))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):   # warm-up outside capture
+        attn.attn_decode(q, kc, vc, sl, o=o, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        attn.attn_decode(q, kc, vc, sl, o=o, workspace=ws)
+    for it in range(4):
+        lens = torch.randint(1, S_cap + 1, (B,), generator=g, dtype=torch.int32)
+        if it == 2:
+            lens[:] = S_cap   # every sequence long: all cut into segments
+        say(f"decode graph replay {it}: lens {lens.tolist()}")
+        sl.copy_(lens)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = o.clone()
+        eager = attn.attn_decode(q, kc, vc, sl)
+        torch.cuda.synchronize()
+        assert torch.equal(got, eager), f"replay {it} differs from the eager call"
+
+
+def test_decode_binding_rejects_bad_output_and_workspace(attn):
+    """The Python binding checks a caller's o and workspace before any launch."""
+    B, H, S_cap, D = 2, 2, 64, 64
+    sl, q, kc, vc = _decode_case(422, B, H, S_cap, D, torch.bfloat16, [10, 64])
+    q, kc, vc, sl = q.cuda(), kc.cuda(), vc.cuda(), sl.cuda()
+    need = attn.attn_decode_workspace_bytes(B, H, S_cap, D)
+    with pytest.raises(ValueError):
+        attn.attn_decode(q, kc, vc, sl, o=torch.empty(B, 1, H, D, dtype=torch.bfloat16))   # CPU o
+    with pytest.raises(ValueError):
+        attn.attn_decode(q, kc, vc, sl, o=torch.empty(B, 1, H, D // 2, dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        attn.attn_decode(q, kc, vc, sl, o=torch.empty(B, 1, H, D, dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError):
+        attn.attn_decode(q, kc, vc, sl, workspace=torch.empty(need, dtype=torch.uint8))   # CPU workspace
+    with pytest.raises(ValueError):
+        attn.attn_decode(q, kc, vc, sl, workspace=torch.empty(need - 16, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError):
+        attn.attn_decode(q, kc, vc, sl, workspace=torch.empty(2, need, dtype=torch.uint8, device="cuda")[:, 0])
+    o = attn.attn_decode(q, kc, vc, sl, workspace=torch.empty(need, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    check(o, oracle.attn_decode(q.cpu(), kc.cpu(), vc.cpu(), sl.cpu().numpy()), torch.bfloat16, "binding")
+
+
 def test_decode_matches_forward_with_one_query(attn):
     """attn_decode row b equals attn_fwd(S_q = 1, S_kv = len_b) on the same data."""
     B, H, S_cap, D = 4, 4, 700, 128
