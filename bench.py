@@ -35,23 +35,45 @@ BF16_MFMA_PEAK_TFLOPS = 2516.6   # MI355X dense bf16: 256 CU x 4096 FLOP/clk x 2
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 FP32_MFMA_PEAK_TFLOPS = 157.3    # MI355X dense fp32 matrix (the same figure as the fp32 vector peak)
 FLUSH_BYTES = 512 << 20
-TILE_SRC = os.path.join(ROOT, "causal_head_attention_amd", "csrc", "kernels", "fwd_tile.hip")
-DECODE_SRC = os.path.join(ROOT, "causal_head_attention_amd", "csrc", "kernels", "decode.hip")
+CSRC = os.path.join(ROOT, "causal_head_attention_amd", "csrc")
+PREFILL_SRC = os.path.join(CSRC, "kernels", "fwd_prefill.hip")
+DECODE_SRC = os.path.join(CSRC, "kernels", "decode.hip")
+# headers every kernel source includes: their constants set tile sizes,
+# LDS layouts and the decode split, hence the kernels' traffic
+KERNEL_HEADERS = [os.path.join(CSRC, "plan.h"), os.path.join(CSRC, "launch.h"),
+                  os.path.join(ROOT, "include", "attn.h")]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+NOMINAL_CLOCK_GHZ = 2.4          # the clock the MI355X peaks are quoted at
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def build_sha256(path: str) -> str:
-    """Fingerprint of a kernel as built: its source text and the device flags
-    it is compiled with (include paths left out, as they differ per machine)."""
+def _hipcc_version() -> str:
+    import subprocess
+    from causal_head_attention_amd import build as B
+    try:
+        return subprocess.run([B.hipcc(), "--version"], capture_output=True, text=True).stdout
+    except (OSError, RuntimeError):
+        return "unknown"
+
+
+def build_sha256(path: str, headers=None) -> str:
+    """Fingerprint of a kernel as built: its source text, the local headers it
+    includes (plan.h, launch.h, attn.h), the device flags it is compiled with
+    (include paths left out, as they differ per machine) and the compiler's
+    version banner."""
     from causal_head_attention_amd import build as B
     name = os.path.basename(path)
     flags = [f for f in B.COMMON if f != "-I" and not os.path.isabs(f)]
     flags += B.DEVICE_FLAGS + B.PER_SOURCE_FLAGS.get(name, [])
-    return hashlib.sha256(open(path, "rb").read() + " ".join(flags).encode()).hexdigest()
+    h = hashlib.sha256(open(path, "rb").read())
+    for hdr in (KERNEL_HEADERS if headers is None else headers):
+        h.update(open(hdr, "rb").read())
+    h.update(" ".join(flags).encode())
+    h.update(_hipcc_version().encode())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel: str, src: str):
@@ -115,7 +137,7 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, copy_mib: int = 256) -
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            if "fwd_tile_kernel" in name and r["Grid_Size"] != prefill_grid:
+            if "prefill_kernel" in name and r["Grid_Size"] != prefill_grid:
                 name += " [kvcache]"   # the KV-cache launch of the same kernel
             vals.setdefault(name, []).append(float(r["Counter_Value"]))
         return vals
@@ -134,20 +156,16 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, copy_mib: int = 256) -
     out = {"note": (f"HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each "
                     f"scaled by what the counter reads for a {copy_mib} MiB device copy: FETCH_SIZE x {f_scale:.5f}, "
                     f"WRITE_SIZE x {w_scale:.5f}.")}
-    rows = []
-    prefill = {"fetch_kib": mean_of(fetch, "fwd_tile_kernelIDF16bLi128ELb0"),
-               "write_kib": mean_of(write, "fwd_tile_kernelIDF16bLi128ELb0")}
-    split = {"fetch_kib": mean_of(fetch, "decode_split_kernelIDF16bLi128"),
-             "write_kib": mean_of(write, "decode_split_kernelIDF16bLi128")}
-    comb = {"fetch_kib": mean_of(fetch, "decode_combine_kernelIDF16bLi128"),
-            "write_kib": mean_of(write, "decode_combine_kernelIDF16bLi128")}
+    prefill = {"fetch_kib": mean_of(fetch, "prefill_kernelIDF16bLi128"),
+               "write_kib": mean_of(write, "prefill_kernelIDF16bLi128")}
+    dec = {"fetch_kib": mean_of(fetch, "decode_kernelIDF16bLi128"),
+           "write_kib": mean_of(write, "decode_kernelIDF16bLi128")}
     pb = round((prefill["fetch_kib"] * f_scale + prefill["write_kib"] * w_scale) * 1024)
-    db = round(((split["fetch_kib"] + comb["fetch_kib"]) * f_scale + (split["write_kib"] + comb["write_kib"]) * w_scale)
-               * 1024)
-    out["fwd_tile"] = {"bytes_per_launch": pb, "algorithmic_bytes": 4 * 2048 * 32 * 128 * 2,
-                            "counters_kib": prefill, "build_sha256": build_sha256(TILE_SRC)}
-    out["decode"] = {"bytes_per_launch": db, "counters_kib": {"split": split, "combine": comb},
-                     "build_sha256": build_sha256(DECODE_SRC), "note": "one call = split + combine kernels"}
+    db = round((dec["fetch_kib"] * f_scale + dec["write_kib"] * w_scale) * 1024)
+    out["prefill"] = {"bytes_per_launch": pb, "algorithmic_bytes": 4 * 2048 * 32 * 128 * 2,
+                      "counters_kib": prefill, "build_sha256": build_sha256(PREFILL_SRC)}
+    out["decode"] = {"bytes_per_launch": db, "counters_kib": dec, "build_sha256": build_sha256(DECODE_SRC),
+                     "note": "one call = one kernel (streaming and merging workgroups)"}
     out["scales"] = {"fetch": f_scale, "write": w_scale}
     return out
 
@@ -166,9 +184,9 @@ def cpu_model() -> str:
 
 def main() -> int:
     if len(sys.argv) >= 2 and sys.argv[1] == "--traffic-from":
-        # bench.py --traffic-from FETCH_CSV WRITE_CSV: write profiles/traffic.json
+        # bench.py --traffic-from FETCH_CSV WRITE_CSV [OUT]: write profiles/traffic.json (or OUT)
         doc = traffic_from_counters(sys.argv[2], sys.argv[3])
-        json.dump(doc, open(TRAFFIC_JSON, "w"), indent=1)
+        json.dump(doc, open(sys.argv[4] if len(sys.argv) > 4 else TRAFFIC_JSON, "w"), indent=1)
         print(json.dumps(doc, indent=1))
         return 0
     ap = argparse.ArgumentParser()
@@ -217,12 +235,16 @@ def main() -> int:
     dec_bytes = workloads.decode_kv_bytes(seqlens_h.tolist(), dc.H, dc.D, 2, dc.S_cap)
 
     hev = HipEvents()
+    # one clock-probe row per timed step: the prefill kernel's workgroup 0
+    # writes (shader clock, 100 MHz real time) at its start and at its end
+    clk = torch.zeros(args.steps, 4, dtype=torch.int64, device=dev)
 
-    def step(evs):
+    def step(evs, probe=None):
         # events are attached to the kernels themselves (hipExtLaunchKernelGGL),
         # so each interval is the call's device time on its own stream
         flush.zero_()
         attn.attn_set_timing_events(evs[0], evs[1])
+        attn.attn_set_clock_probe(probe)
         attn.attn_fwd(q, k, v, o, causal=True)
         flush.zero_()
         attn.attn_set_timing_events(evs[2], evs[3])
@@ -239,14 +261,41 @@ def main() -> int:
     events = [hev.create(4) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for evs in events:
-        step(evs)
+    for i, evs in enumerate(events):
+        step(evs, clk[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     fwd_ms = [hev.ms(e[0], e[1]) for e in events]
     dec_ms = [hev.ms(e[2], e[3]) for e in events]
     for e in events:
         hev.destroy(e)
+    c = clk.cpu().numpy()
+    clock_ghz = [(c[i, 2] - c[i, 0]) / (c[i, 3] - c[i, 1]) * 0.1 for i in range(args.steps) if c[i, 3] > c[i, 1]]
+
+    # the read-only reference: a plain non-temporal read of as many bytes as
+    # one decode call reads, on this same GPU, cold like the decode
+    log("read-only stream reference")
+    import ctypes
+    probe_lib = ctypes.CDLL(os.path.join(ROOT, "causal_head_attention_amd", "libattn_probe.so"))
+    rs = probe_lib.attn_probe_read_stream
+    rs.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.c_void_p]
+    rs.restype = ctypes.c_int
+    rs_bytes = dec_bytes // 16 * 16
+    rs_buf = torch.ones(rs_bytes, dtype=torch.uint8, device=dev)
+    rs_out = torch.empty(256 * 512, dtype=torch.int32, device=dev)
+    rs_stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    rs_ms = []
+    for i in range(23):
+        e = hev.create(2)
+        flush.zero_()
+        if rs(rs_buf.data_ptr(), rs_bytes, rs_out.data_ptr(), rs_stream, e[0], e[1]) != 0:
+            raise RuntimeError("attn_probe_read_stream failed")
+        torch.cuda.synchronize()
+        if i >= 3:
+            rs_ms.append(hev.ms(e[0], e[1]))
+        hev.destroy(e)
+    del rs_buf, rs_out
 
     # warm-cache figures (no flush), for context only
     warm_f, warm_d = [], []
@@ -282,13 +331,13 @@ def main() -> int:
         return out
 
     def mfma_leg(ms, flop, workload):
-        mean = statistics.fmean(ms)
-        tf = flop / (mean * 1e-3) / 1e12
+        med = statistics.median(ms)
+        tf = flop / (med * 1e-3) / 1e12
         return {"value": round(tf, 2), "unit": "TFLOPS", "workload": workload,
                 "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                             "flop_per_launch": flop, "mean_launch_us": round(mean * 1e3, 2),
-                             "median_launch_us": round(statistics.median(ms) * 1e3, 2)}}
+                             "flop_per_launch": flop, "median_launch_us": round(med * 1e3, 2),
+                             "mean_launch_us": round(statistics.fmean(ms) * 1e3, 2)}}
 
     kv = f16 = kp = qp = pe_leg = sm_leg = f32 = nc = s4k = None
     if not args.skip_extras:
@@ -348,7 +397,7 @@ def main() -> int:
         log("position encoding table")
         pe_t = torch.empty(workloads.PE_S, workloads.PE_D, dtype=torch.float32, device=dev)
         pe_ms = cold_ms(lambda: attn.sinusoidal_pe(workloads.PE_S, workloads.PE_D, 0, out=pe_t))
-        pe_mean = statistics.fmean(pe_ms)
+        pe_mean = statistics.median(pe_ms)
         pe_bytes = workloads.PE_S * workloads.PE_D * 4
         pe_gbs = pe_bytes / (pe_mean * 1e-3) / 1e9
         pe_leg = {"value": round(pe_gbs, 1), "unit": "GB/s",
@@ -356,7 +405,7 @@ def main() -> int:
                               f"cold, 20 calls",
                   "roofline": {"bound": "hbm", "achieved": round(pe_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                "frac": round(pe_gbs / HBM_PEAK_GBS, 4), "bytes_per_call": pe_bytes,
-                               "mean_launch_us": round(pe_mean * 1e3, 2)}}
+                               "median_launch_us": round(pe_mean * 1e3, 2)}}
         del pe_t
 
         # the standalone masked softmax over the bf16_s2048 layer's score
@@ -366,7 +415,7 @@ def main() -> int:
         s_sm = workloads.make_scores(sc).to(dev)
         p_sm = torch.empty_like(s_sm)
         sm_ms = cold_ms(lambda: attn.masked_softmax(s_sm, sc.scale, sc.causal, out=p_sm))
-        sm_mean = statistics.fmean(sm_ms)
+        sm_mean = statistics.median(sm_ms)
         sm_bytes = sc.algorithmic_bytes()
         sm_gbs = sm_bytes / (sm_mean * 1e-3) / 1e9
         sm_leg = {"value": round(sm_gbs, 1), "unit": "GB/s",
@@ -374,7 +423,7 @@ def main() -> int:
                               f"scale 1/sqrt(128) (seed {sc.seed}); cold, 20 calls",
                   "roofline": {"bound": "hbm", "achieved": round(sm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                "frac": round(sm_gbs / HBM_PEAK_GBS, 4), "bytes_per_call": sm_bytes,
-                               "mean_launch_us": round(sm_mean * 1e3, 2)}}
+                               "median_launch_us": round(sm_mean * 1e3, 2)}}
         del s_sm, p_sm
 
         # the bf16_s2048 data without the causal rule: every query block walks
@@ -405,7 +454,7 @@ def main() -> int:
         q32, k32, v32 = (t.to(dev) for t in workloads.make_prefill(c32))
         o32 = torch.empty_like(q32)
         f32_ms = cold_ms(lambda: attn.attn_fwd(q32, k32, v32, o32, causal=True))
-        f32_mean = statistics.fmean(f32_ms)
+        f32_mean = statistics.median(f32_ms)
         f32_tf = c32.flops() / (f32_mean * 1e-3) / 1e12
         f32 = {"value": round(f32_tf, 3), "unit": "TFLOPS",
                "workload": f"fp32 causal prefill B={c32.B} H={c32.H} S={c32.S_q} D={c32.D} (seed {c32.seed}), "
@@ -413,7 +462,7 @@ def main() -> int:
                "roofline": {"bound": "mfma", "achieved": round(f32_tf, 3), "peak": FP32_MFMA_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(f32_tf / FP32_MFMA_PEAK_TFLOPS, 4),
                             "kernel": "fwd_f32_kernel<64>",
-                            "flop_per_launch": c32.flops(), "mean_launch_us": round(f32_mean * 1e3, 2)}}
+                            "flop_per_launch": c32.flops(), "median_launch_us": round(f32_mean * 1e3, 2)}}
         del q32, k32, v32, o32
 
     if args.copy_calibration:
@@ -424,10 +473,13 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"copy calibration: {n} bytes read, {n} bytes written")
 
-    fwd_mean = statistics.fmean(fwd_ms)
-    dec_mean = statistics.fmean(dec_ms)
-    tflops = flops / (fwd_mean * 1e-3) / 1e12
-    dec_gbs = dec_bytes / (dec_mean * 1e-3) / 1e9
+    # headline rates from the median call (the mean is reported beside it)
+    fwd_med = statistics.median(fwd_ms)
+    dec_med = statistics.median(dec_ms)
+    tflops = flops / (fwd_med * 1e-3) / 1e12
+    dec_gbs = dec_bytes / (dec_med * 1e-3) / 1e9
+    clk_ghz = statistics.median(clock_ghz) if clock_ghz else None
+    rs_gbs = rs_bytes / (statistics.median(rs_ms) * 1e-3) / 1e9
 
     # quick parity sample on the benchmarked outputs
     o_h = o.float().cpu().double().numpy()
@@ -465,7 +517,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(fwd_mean + dec_mean, 4),
+        "ms_per_step": round(fwd_med + dec_med, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -477,20 +529,36 @@ def main() -> int:
                    "decode_tokens": int(sum(int(x) for x in seqlens_h))},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("fwd_tile", TILE_SRC),
-                     "kernel": "fwd_tile_kernel<bf16,128>", "flop_per_launch": flops,
-                     "mean_launch_us": round(fwd_mean * 1e3, 2),
-                     "median_launch_us": round(statistics.median(fwd_ms) * 1e3, 2),
-                     "p95_launch_us": round(float(np.percentile(fwd_ms, 95)) * 1e3, 2)},
+                     "traffic": measured_traffic("prefill", PREFILL_SRC),
+                     "kernel": "prefill_kernel<bf16,128>", "flop_per_launch": flops,
+                     "rate_from": "median launch",
+                     "median_launch_us": round(fwd_med * 1e3, 2),
+                     "mean_launch_us": round(statistics.fmean(fwd_ms) * 1e3, 2),
+                     "p95_launch_us": round(float(np.percentile(fwd_ms, 95)) * 1e3, 2),
+                     "clock_ghz": round(clk_ghz, 3) if clk_ghz else None,
+                     "clock_adjusted_frac": (round(tflops / (BF16_MFMA_PEAK_TFLOPS * clk_ghz / NOMINAL_CLOCK_GHZ), 4)
+                                             if clk_ghz else None),
+                     "clock_note": "shader clock over workgroup 0's run (s_memtime against the 100 MHz "
+                                   "s_memrealtime), median over the timed calls; clock_adjusted_frac divides "
+                                   f"by the peak scaled to that clock from {NOMINAL_CLOCK_GHZ} GHz"},
         "decode": {"value": round(dec_gbs, 1), "unit": "GB/s",
                    "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                                 "traffic": measured_traffic("decode", DECODE_SRC),
                                 "bytes_per_call": dec_bytes,
-                                "mean_call_us": round(dec_mean * 1e3, 2),
-                                "median_call_us": round(statistics.median(dec_ms) * 1e3, 2),
+                                "rate_from": "median call",
+                                "median_call_us": round(dec_med * 1e3, 2),
+                                "mean_call_us": round(statistics.fmean(dec_ms) * 1e3, 2),
                                 "p95_call_us": round(float(np.percentile(dec_ms, 95)) * 1e3, 2),
-                                "note": "one call = split kernel + combine kernel"}},
+                                "note": "one call = one kernel: 256 streaming workgroups and the merging "
+                                        "workgroups after them"},
+                   "read_stream_reference": {
+                       "gbs": round(rs_gbs, 1), "frac_of_peak": round(rs_gbs / HBM_PEAK_GBS, 4),
+                       "decode_over_reference": round(dec_gbs / rs_gbs, 4),
+                       "bytes": rs_bytes, "median_us": round(statistics.median(rs_ms) * 1e3, 2),
+                       "what": "libattn_probe.so read_stream_kernel: a plain non-temporal 16-byte-per-lane read "
+                               "of the same number of bytes on this GPU, 256x512 threads, 16 loads in flight, "
+                               "cold like the decode, median of 20"}},
         "warm_cache": ({"prefill_tflops": round(flops / (statistics.median(warm_f) * 1e-3) / 1e12, 2),
                         "decode_gbs": round(dec_bytes / (statistics.median(warm_d) * 1e-3) / 1e9, 1)}
                        if warm_f else None),

@@ -71,6 +71,8 @@ def _load() -> ctypes.CDLL:
     lib.attn_set_stream.restype = i
     lib.attn_set_timing_events.argtypes = [vp, vp]
     lib.attn_set_timing_events.restype = i
+    lib.attn_set_clock_probe.argtypes = [vp]
+    lib.attn_set_clock_probe.restype = i
     lib.attn_get_stream.argtypes = []
     lib.attn_get_stream.restype = vp
     lib.attn_last_error.argtypes = []
@@ -328,9 +330,7 @@ def attn_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, seq
             raise ValueError("workspace must be a GPU tensor on q's device")
         if not workspace.is_contiguous():
             raise ValueError("workspace must be contiguous")
-        if workspace.numel() * workspace.element_size() < need:
-            raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
-                             f"{need} needed")
+        # its size is checked by the library (ATTN_ERR_WORKSPACE)
     _set_stream(q.device)
     _check(load().attn_decode(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), seqlens.data_ptr(),
                            o.data_ptr(), B, H, S_cap, D, _dtype_code(q), workspace.data_ptr(),
@@ -341,6 +341,19 @@ def attn_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, seq
 def attn_set_timing_events(start: int | None, stop: int | None) -> None:
     """Arm two hipEvent_t handles for the next attn_fwd / attn_decode call on this thread."""
     _check(load().attn_set_timing_events(ctypes.c_void_p(start or 0), ctypes.c_void_p(stop or 0)))
+
+
+def attn_set_clock_probe(buf: torch.Tensor | None) -> None:
+    """Arm a device int64[4] buffer for the next attn_fwd call on this thread:
+    the prefill kernel's workgroup 0 writes (shader clock, 100 MHz real time)
+    at its start and at its end. None disarms."""
+    if buf is None:
+        _check(load().attn_set_clock_probe(ctypes.c_void_p(0)))
+        return
+    _dev_tensor("clock probe", buf, 1)
+    if buf.dtype != torch.int64 or buf.numel() < 4:
+        raise ValueError("clock probe must be an int64 GPU tensor of at least 4 elements")
+    _check(load().attn_set_clock_probe(ctypes.c_void_p(buf.data_ptr())))
 
 
 def attn_fwd_plan(B: int, H: int, S_q: int, S_kv: int, D: int, causal: bool, dtype: int) -> FwdPlan:
@@ -356,5 +369,5 @@ def attn_decode_plan(B: int, H: int, S_cap: int, D: int, dtype: int) -> DecodePl
 
 
 __all__ = ["attn_fwd", "attn_fwd_kvcache", "attn_fwd_mask", "attn_decode", "qkv_proj", "sinusoidal_pe", "masked_softmax", "attn_decode_workspace_bytes", "attn_fwd_plan", "attn_decode_plan",
-           "attn_set_timing_events",
+           "attn_set_timing_events", "attn_set_clock_probe",
            "AttnError", "ATTN_F32", "ATTN_BF16", "ATTN_F16", "lib", "LIB_PATH"]

@@ -32,6 +32,11 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "softmax.hip"),
 ]
 
+# The bench's read-only HBM reference: a separate library, not part of the
+# attention path or its C ABI.
+PROBE_SOURCES = [os.path.join(CSRC, "probe", "read_stream.hip")]
+PROBE_LIB = os.path.join(PKG, "libattn_probe.so")
+
 ARCH = "gfx950"
 # Packed fp32 VALU forms are switched off for every device pass. MFMA
 # accumulators are kept in ordinary VGPRs: the softmax rescale touches them
@@ -96,11 +101,13 @@ def _compile(src: str) -> tuple[str, dict]:
 
 
 def build(jobs: int = 4) -> str:
-    """Compile every HIP/C++ source for gfx950 and link ``libattn.so``."""
+    """Compile every HIP/C++ source for gfx950 and link ``libattn.so`` (and
+    the bench's ``libattn_probe.so``)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        done = list(ex.map(_compile, SOURCES))
-    objs = [o for o, _ in done]
+        done = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    objs = [o for o, _ in done[:len(SOURCES)]]
+    probe_objs = [o for o, _ in done[len(SOURCES):]]
     res = {}
     for _, r in done:
         res.update(r)
@@ -110,10 +117,11 @@ def build(jobs: int = 4) -> str:
         if r.get("ScratchSize", 0) or r.get("VGPRs Spill", 0):
             print(f"warning: {name} uses {r.get('ScratchSize')} B/lane of scratch "
                   f"({r.get('VGPRs Spill')} VGPRs spilled)", file=sys.stderr)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
-    subprocess.run(cmd, check=True, capture_output=True, text=True)
-    os.replace(tmp, LIB)
+    for lib, parts in ((LIB, objs), (PROBE_LIB, probe_objs)):
+        tmp = lib + ".tmp"
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + parts
+        subprocess.run(cmd, check=True, capture_output=True, text=True)
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -33,12 +33,20 @@ namespace {
 thread_local hipStream_t t_stream = nullptr;
 thread_local std::string t_error;
 thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;   // for the next call only
+thread_local unsigned long long* t_clock_probe = nullptr;             // for the next call only
 
 // Take (and clear) the timing events armed for this call.
 void take_events(hipEvent_t& start, hipEvent_t& stop) {
     start = t_ev_start;
     stop = t_ev_stop;
     t_ev_start = t_ev_stop = nullptr;
+}
+
+// Take (and clear) the clock probe armed for this call.
+unsigned long long* take_clock_probe() {
+    unsigned long long* p = t_clock_probe;
+    t_clock_probe = nullptr;
+    return p;
 }
 
 int fail(int status, const std::string& msg) {
@@ -155,6 +163,7 @@ int run_fwd(const char* fn, const void* q, const void* k, const void* v, const i
             int dtype, bool kvcache) {
     hipEvent_t ev_start, ev_stop;
     take_events(ev_start, ev_stop);
+    unsigned long long* const clk = take_clock_probe();
     const int st = check_fwd_sizes(B, H, S_q, S_kv, D, causal, dtype, kvcache, fn);
     if (st != ATTN_OK) return st;
     if ((long long)B * H * S_q == 0) return ok();
@@ -181,6 +190,7 @@ int run_fwd(const char* fn, const void* q, const void* k, const void* v, const i
     attn::FwdArgs a{q, k, v, o, B, H, S_q, S_kv, D, causal,
                     (float)(1.0f / std::sqrt((float)D)) * 1.4426950408889634f, ev_start, ev_stop, kv_lens, lse,
                     key_mask};
+    a.clock_probe = clk;
     const Algo algo = algo_from_env();
     hipError_t e;
     if (algo == kRow)
@@ -210,6 +220,13 @@ void* attn_get_stream(void) { return static_cast<void*>(t_stream); }
 int attn_set_timing_events(void* start, void* stop) {
     t_ev_start = static_cast<hipEvent_t>(start);
     t_ev_stop = static_cast<hipEvent_t>(stop);
+    return ok();
+}
+
+int attn_set_clock_probe(void* device_buf) {
+    if (device_buf && (reinterpret_cast<uintptr_t>(device_buf) & 7u) != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_set_clock_probe: buffer must be 8-byte aligned");
+    t_clock_probe = static_cast<unsigned long long*>(device_buf);
     return ok();
 }
 
@@ -359,6 +376,7 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
                 int H, int S_cap, int D, int dtype, void* workspace, size_t workspace_bytes) {
     hipEvent_t ev_start, ev_stop;
     take_events(ev_start, ev_stop);
+    take_clock_probe();   // armed for an attn_fwd call only
     attn_decode_plan_t plan;
     const int st = attn_decode_plan(B, H, S_cap, D, dtype, &plan);
     if (st != ATTN_OK) return st;
@@ -400,6 +418,7 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
 int attn_sinusoidal_pe(float* pe, int S, int d_model, int pos0) {
     hipEvent_t ev_start, ev_stop;
     take_events(ev_start, ev_stop);
+    take_clock_probe();   // armed for an attn_fwd call only
     if (S < 0 || d_model <= 0 || pos0 < 0)
         return fail(ATTN_ERR_INVALID_ARG, "attn_sinusoidal_pe: sizes must be S >= 0, d_model >= 1, pos0 >= 0");
     if (d_model & 1)
@@ -427,6 +446,7 @@ int attn_masked_softmax(const void* s, void* p, int B, int H, int S_q, int S_kv,
                         int dtype) {
     hipEvent_t ev_start, ev_stop;
     take_events(ev_start, ev_stop);
+    take_clock_probe();   // armed for an attn_fwd call only
     if (B < 0 || H < 0 || S_q < 0 || S_kv < 0)
         return fail(ATTN_ERR_INVALID_ARG, "attn_masked_softmax: negative size");
     if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "attn_masked_softmax: causal must be 0 or 1");
@@ -463,6 +483,7 @@ int attn_masked_softmax(const void* s, void* p, int B, int H, int S_q, int S_kv,
 int attn_qkv_proj(const void* x, const void* w, void* q, void* k, void* v, int M, int E, int H, int D, int dtype) {
     hipEvent_t ev_start, ev_stop;
     take_events(ev_start, ev_stop);
+    take_clock_probe();   // armed for an attn_fwd call only
     if (M < 0 || E <= 0 || H <= 0 || D <= 0)
         return fail(ATTN_ERR_INVALID_ARG, "attn_qkv_proj: sizes must be M >= 0 and E, H, D >= 1");
     if (dtype != ATTN_BF16 && dtype != ATTN_F16)
@@ -473,8 +494,8 @@ int attn_qkv_proj(const void* x, const void* w, void* q, void* k, void* v, int M
     const long long N = (long long)H * D;
     if (N % 32 != 0) return fail(ATTN_ERR_UNSUPPORTED, "attn_qkv_proj: H*D must be a multiple of 32");
     // per-tile descriptors span 256 rows of X or of an output, 384 rows of W
-    if ((long long)attn::kGemmBM * E * 2 > 0x7fffffffLL || (long long)attn::kGemmBM * N * 2 > 0x7fffffffLL ||
-        3 * N > 0x7fffffffLL)
+    if ((long long)attn::kGemmBM * E * 2 > 0x7fffffffLL || (long long)attn::kGemmBN * E * 2 > 0x7fffffffLL ||
+        (long long)attn::kGemmBM * N * 2 > 0x7fffffffLL || 3 * N > 0x7fffffffLL)
         return fail(ATTN_ERR_UNSUPPORTED, "attn_qkv_proj: E or H*D too large for 32-bit tile offsets");
     if (tensor_bytes(M, E, 1, 1, 2) < 0 || tensor_bytes(3, N, E, 1, 2) < 0 || tensor_bytes(M, N, 1, 1, 2) < 0 ||
         attn::qkv_grid(M, (int)N) > 0x7fffffffLL)

@@ -243,7 +243,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     T* __restrict__ O, int B, int H, int S_q, int S_cap, int causal, float c /* scale*log2e */, int n_qblk,
-    int items_per_bh, int paired, const int32_t* __restrict__ kv_lens, float* __restrict__ lse) {
+    int items_per_bh, int paired, const int32_t* __restrict__ kv_lens, float* __restrict__ lse,
+    unsigned long long* __restrict__ clk) {
     typedef typename Mma<T>::v8 v8;
     typedef typename Mma<T>::v2 v2;
     using C = Cfg<D>;
@@ -259,6 +260,12 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
     const int wq = wave & 3;     // query sub-block of this wave
     const int half = wave >> 2;  // key half of every tile
     const int HD2 = H * D * 2;   // bytes between consecutive tokens of a head
+    // optional clock probe: workgroup 0 records the shader-clock counter and
+    // the 100 MHz real-time counter when it starts and when it ends
+    if (clk && blockIdx.x == 0 && tid == 0) {
+        clk[0] = __builtin_amdgcn_s_memtime();
+        clk[1] = __builtin_amdgcn_s_memrealtime();
+    }
 
     // ---- work item
     int bh, p;
@@ -688,6 +695,10 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
         }
         j0 += nt;
     }
+    if (clk && blockIdx.x == 0 && tid == 0) {
+        clk[2] = __builtin_amdgcn_s_memtime();
+        clk[3] = __builtin_amdgcn_s_memrealtime();
+    }
 }
 
 template <typename T, int D>
@@ -696,7 +707,7 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
     hipExtLaunchKernelGGL((prefill_kernel<T, D>), dim3((unsigned)tg.n_items), dim3(kTileThreads), 0, stream,
                           a.ev_start, a.ev_stop, 0, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                           (T*)a.o, a.B, a.H, a.S_q, a.S_kv, a.causal, a.scale_log2, tg.n_qblk, tg.items_per_bh,
-                          tg.paired, a.kv_lens, a.lse);
+                          tg.paired, a.kv_lens, a.lse, a.clock_probe);
     return hipGetLastError();
 }
 

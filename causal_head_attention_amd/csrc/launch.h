@@ -27,6 +27,9 @@ struct FwdArgs {
     // optional device uint8 [B, S_kv]: 0 hides key j of entry b from all
     // its queries (key padding); nullptr means no key is hidden
     const uint8_t* key_mask;
+    // optional device uint64[4]: the prefill kernel's workgroup 0 writes the
+    // shader-clock and real-time counters at its start and at its end
+    unsigned long long* clock_probe;
 };
 
 // Storage type of q, k, v and o (arithmetic is fp32 throughout).

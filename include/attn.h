@@ -282,6 +282,20 @@ void* attn_get_stream(void);
  */
 int attn_set_timing_events(void* start, void* stop);
 
+/*
+ * attn_set_clock_probe -- arm a DEVICE buffer of four uint64 (8-byte
+ * aligned; NULL disarms) for the NEXT call on this thread. If that call is
+ * an attn_fwd, attn_fwd_kvcache or attn_fwd_mask that runs the 16-bit
+ * prefill kernel, that kernel's workgroup 0 writes the shader-clock counter
+ * (s_memtime) and the 100 MHz real-time counter (s_memrealtime) when it
+ * starts, then both again when it ends; the ratio of the differences
+ * times 100 MHz is the shader clock over that workgroup's run. Any other
+ * call leaves the buffer untouched. The probe is used once, like the timing
+ * events. Measurement plumbing, not part of the operation; it follows the
+ * timing practice of the depthwise-convolution page, section 4.1.
+ */
+int attn_set_clock_probe(void* device_buf);
+
 /* Reason for the last non-OK status returned on this thread ("" if none):
  * a rejected shape or argument (the host-side checks of the
  * depthwise-convolution page, section 6.2) or the runtime's message for a

@@ -217,6 +217,7 @@ def qkv(x=A, w=A + 0x1000000, q=A + 0x4000000, k=A + 0x5000000, v=A + 0x6000000,
     (dict(q=A + 0x100), attn.ATTN_ERR_INVALID_ARG, "overlaps an input"),          # q inside x
     (dict(k=A + 0x4000000), attn.ATTN_ERR_INVALID_ARG, "each other"),            # k on q
     (dict(E=1 << 23), attn.ATTN_ERR_UNSUPPORTED, "32-bit"),
+    (dict(E=3 << 20), attn.ATTN_ERR_UNSUPPORTED, "32-bit"),   # the 384-row W tile passes 2^31 bytes first
 ])
 def test_qkv_rejections(kw, status, needle):
     assert qkv(**kw) == status, L.attn_last_error()
@@ -306,7 +307,8 @@ def test_kernels_use_no_scratch():
     if not os.path.exists(path):
         pytest.skip("no build report (build the library first)")
     res = json.load(open(path))
-    assert any("fwd_tile_kernel" in k for k in res), "report lists the tile kernel"
+    for kern in ("prefill_kernel", "fwd_tile_kernel", "decode_kernel", "fwd_f32_kernel"):
+        assert any(kern in k for k in res), f"report lists {kern}"
     bad = {k: v for k, v in res.items() if v.get("ScratchSize", 0) or v.get("VGPRs Spill", 0)}
     assert not bad, bad
 
@@ -321,17 +323,33 @@ def _bench_module():
 
 
 def test_traffic_record_matches_the_current_build_and_goes_stale(monkeypatch, tmp_path):
-    """profiles/traffic.json is keyed by each kernel's source and device flags:
-    the committed record matches this build, and a changed flag or source nulls it."""
+    """profiles/traffic.json is keyed by each kernel's build: its source, the
+    headers it includes, the device flags and the compiler. The committed
+    record matches this build, and a changed flag, source or header nulls it."""
     from causal_head_attention_amd import build as B
     bench = _bench_module()
     import json
     doc = json.load(open(bench.TRAFFIC_JSON))
-    assert bench.measured_traffic("fwd_tile", bench.TILE_SRC) == doc["fwd_tile"]["bytes_per_launch"]
+    assert bench.measured_traffic("prefill", bench.PREFILL_SRC) == doc["prefill"]["bytes_per_launch"]
     assert bench.measured_traffic("decode", bench.DECODE_SRC) == doc["decode"]["bytes_per_launch"]
-    monkeypatch.setitem(B.PER_SOURCE_FLAGS, "fwd_tile.hip", [])
-    assert bench.measured_traffic("fwd_tile", bench.TILE_SRC) is None
+    monkeypatch.setitem(B.PER_SOURCE_FLAGS, "fwd_prefill.hip", ["-fno-honor-nans"])
+    assert bench.measured_traffic("prefill", bench.PREFILL_SRC) is None
     monkeypatch.undo()
     edited = tmp_path / "decode.hip"
     edited.write_bytes(open(bench.DECODE_SRC, "rb").read() + b"\n// edited\n")
     assert bench.measured_traffic("decode", str(edited)) is None
+    # an edit of plan.h (tile sizes, the decode split) changes every kernel's fingerprint
+    plan = tmp_path / "plan.h"
+    plan.write_bytes(open(bench.KERNEL_HEADERS[0], "rb").read() + b"\n// edited\n")
+    headers = [str(plan)] + bench.KERNEL_HEADERS[1:]
+    assert bench.build_sha256(bench.DECODE_SRC, headers) != bench.build_sha256(bench.DECODE_SRC)
+    assert bench.build_sha256(bench.PREFILL_SRC, headers) != doc["prefill"]["build_sha256"]
+
+
+def test_clock_probe_arming():
+    """attn_set_clock_probe accepts NULL and an 8-byte aligned pointer (nothing
+    is written until an attn_fwd runs) and rejects a misaligned one."""
+    assert L.attn_set_clock_probe(None) == attn.ATTN_OK
+    assert L.attn_set_clock_probe(A + 8) == attn.ATTN_OK
+    assert L.attn_set_clock_probe(A + 4) == attn.ATTN_ERR_INVALID_ARG
+    assert L.attn_set_clock_probe(None) == attn.ATTN_OK   # disarm: no call below may write through it

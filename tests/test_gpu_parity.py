@@ -380,8 +380,9 @@ def test_decode_binding_rejects_bad_output_and_workspace(attn):
         attn.attn_decode(q, kc, vc, sl, o=torch.empty(B, 1, H, D, dtype=torch.float16, device="cuda"))
     with pytest.raises(ValueError):
         attn.attn_decode(q, kc, vc, sl, workspace=torch.empty(need, dtype=torch.uint8))   # CPU workspace
-    with pytest.raises(ValueError):
+    with pytest.raises(attn.AttnError) as e:
         attn.attn_decode(q, kc, vc, sl, workspace=torch.empty(need - 16, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == attn.ATTN_ERR_WORKSPACE
     with pytest.raises(ValueError):
         attn.attn_decode(q, kc, vc, sl, workspace=torch.empty(2, need, dtype=torch.uint8, device="cuda")[:, 0])
     o = attn.attn_decode(q, kc, vc, sl, workspace=torch.empty(need, dtype=torch.uint8, device="cuda"))
