@@ -38,10 +38,9 @@ FLUSH_BYTES = 512 << 20
 CSRC = os.path.join(ROOT, "causal_head_attention_amd", "csrc")
 PREFILL_SRC = os.path.join(CSRC, "kernels", "fwd_prefill.hip")
 DECODE_SRC = os.path.join(CSRC, "kernels", "decode.hip")
-# headers every kernel source includes: their constants set tile sizes,
-# LDS layouts and the decode split, hence the kernels' traffic
-KERNEL_HEADERS = [os.path.join(CSRC, "plan.h"), os.path.join(CSRC, "launch.h"),
-                  os.path.join(ROOT, "include", "attn.h")]
+# the local headers every kernel source includes: their constants set tile
+# sizes, LDS layouts and the decode split, hence the kernels' traffic
+KERNEL_HEADERS = [os.path.join(CSRC, "plan.h"), os.path.join(CSRC, "launch.h")]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 NOMINAL_CLOCK_GHZ = 2.4          # the clock the MI355X peaks are quoted at
 
@@ -59,18 +58,29 @@ def _hipcc_version() -> str:
         return "unknown"
 
 
+def code_text(path: str) -> bytes:
+    """A C/C++ source without its comments and with runs of whitespace folded,
+    so that edits to comments and layout leave a fingerprint unchanged."""
+    import re
+    text = open(path, encoding="utf-8").read()
+    # string and character literals are kept whole; comments go
+    pat = re.compile(r'"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'|//[^\n]*|/\*.*?\*/', re.S)
+    text = pat.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", text)
+    return " ".join(text.split()).encode()
+
+
 def build_sha256(path: str, headers=None) -> str:
-    """Fingerprint of a kernel as built: its source text, the local headers it
-    includes (plan.h, launch.h, attn.h), the device flags it is compiled with
-    (include paths left out, as they differ per machine) and the compiler's
-    version banner."""
+    """Fingerprint of a kernel as built: its code (source and the local headers
+    it includes, plan.h and launch.h, comments left out), the device flags it
+    is compiled with (include paths left out, as they differ per machine) and
+    the compiler's version banner."""
     from causal_head_attention_amd import build as B
     name = os.path.basename(path)
     flags = [f for f in B.COMMON if f != "-I" and not os.path.isabs(f)]
     flags += B.DEVICE_FLAGS + B.PER_SOURCE_FLAGS.get(name, [])
-    h = hashlib.sha256(open(path, "rb").read())
+    h = hashlib.sha256(code_text(path))
     for hdr in (KERNEL_HEADERS if headers is None else headers):
-        h.update(open(hdr, "rb").read())
+        h.update(code_text(hdr))
     h.update(" ".join(flags).encode())
     h.update(_hipcc_version().encode())
     return h.hexdigest()

@@ -323,9 +323,10 @@ def _bench_module():
 
 
 def test_traffic_record_matches_the_current_build_and_goes_stale(monkeypatch, tmp_path):
-    """profiles/traffic.json is keyed by each kernel's build: its source, the
-    headers it includes, the device flags and the compiler. The committed
-    record matches this build, and a changed flag, source or header nulls it."""
+    """profiles/traffic.json is keyed by each kernel's build: its code (source
+    and the headers it includes, comments left out), the device flags and the
+    compiler. The committed record matches this build, and a changed flag, or
+    a code change in the source or a header, nulls it."""
     from causal_head_attention_amd import build as B
     bench = _bench_module()
     import json
@@ -335,12 +336,18 @@ def test_traffic_record_matches_the_current_build_and_goes_stale(monkeypatch, tm
     monkeypatch.setitem(B.PER_SOURCE_FLAGS, "fwd_prefill.hip", ["-fno-honor-nans"])
     assert bench.measured_traffic("prefill", bench.PREFILL_SRC) is None
     monkeypatch.undo()
-    edited = tmp_path / "decode.hip"
-    edited.write_bytes(open(bench.DECODE_SRC, "rb").read() + b"\n// edited\n")
+    src = open(bench.DECODE_SRC, "rb").read()
+    # a comment-only edit keeps the fingerprint; a code edit nulls the record
+    commented = tmp_path / "decode.hip"
+    commented.write_bytes(src.replace(b"\n", b"  // note\n", 3) + b"\n/* a remark */\n")
+    assert bench.measured_traffic("decode", str(commented)) == doc["decode"]["bytes_per_launch"]
+    edited = tmp_path / "decode_edited.hip"
+    edited.write_bytes(src + b"\nnamespace { constexpr int kEdited = 1; }\n")
     assert bench.measured_traffic("decode", str(edited)) is None
-    # an edit of plan.h (tile sizes, the decode split) changes every kernel's fingerprint
+    # a code edit of plan.h (tile sizes, the decode split) changes every kernel's fingerprint
     plan = tmp_path / "plan.h"
-    plan.write_bytes(open(bench.KERNEL_HEADERS[0], "rb").read() + b"\n// edited\n")
+    plan.write_bytes(open(bench.KERNEL_HEADERS[0], "rb").read().replace(
+        b"constexpr int kDecodeBatch = 16;", b"constexpr int kDecodeBatch = 8;"))
     headers = [str(plan)] + bench.KERNEL_HEADERS[1:]
     assert bench.build_sha256(bench.DECODE_SRC, headers) != bench.build_sha256(bench.DECODE_SRC)
     assert bench.build_sha256(bench.PREFILL_SRC, headers) != doc["prefill"]["build_sha256"]
