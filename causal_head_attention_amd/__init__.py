@@ -59,6 +59,8 @@ def _load() -> ctypes.CDLL:
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, sz]
     lib.attn_decode.restype = i
+    lib.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i]
+    lib.attn_decode_noalloc.restype = i
     lib.attn_fwd_mask.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i]
     lib.attn_fwd_mask.restype = i
     lib.attn_qkv_proj.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i]
@@ -338,6 +340,30 @@ def attn_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, seq
     return o
 
 
+def attn_decode_noalloc(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, seqlens: torch.Tensor,
+                        o: torch.Tensor) -> torch.Tensor:
+    """attn_decode without a workspace argument: the library's fixed per-GPU
+    scratch serves instead, and nothing is allocated (o must be given)."""
+    for n, t in (("q", q), ("kcache", kcache), ("vcache", vcache), ("o", o)):
+        _dev_tensor(n, t, 4)
+    _dev_tensor("seqlens", seqlens, 1)
+    B, one, H, D = q.shape
+    S_cap = kcache.shape[1]
+    if one != 1 or tuple(kcache.shape) != (B, S_cap, H, D) or tuple(vcache.shape) != tuple(kcache.shape):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, kcache {tuple(kcache.shape)}, "
+                         f"vcache {tuple(vcache.shape)}")
+    if seqlens.dtype != torch.int32 or seqlens.shape[0] != B:
+        raise ValueError("seqlens must be int32[B]")
+    if not (q.dtype == kcache.dtype == vcache.dtype):
+        raise TypeError("q and the caches must share one dtype")
+    if tuple(o.shape) != tuple(q.shape) or o.dtype != q.dtype or o.device != q.device:
+        raise ValueError("o must match q in shape, dtype and device")
+    _set_stream(q.device)
+    _check(load().attn_decode_noalloc(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), seqlens.data_ptr(),
+                                      o.data_ptr(), B, H, S_cap, D, _dtype_code(q)))
+    return o
+
+
 def attn_set_timing_events(start: int | None, stop: int | None) -> None:
     """Arm two hipEvent_t handles for the next attn_fwd / attn_decode call on this thread."""
     _check(load().attn_set_timing_events(ctypes.c_void_p(start or 0), ctypes.c_void_p(stop or 0)))
@@ -368,6 +394,6 @@ def attn_decode_plan(B: int, H: int, S_cap: int, D: int, dtype: int) -> DecodePl
     return plan
 
 
-__all__ = ["attn_fwd", "attn_fwd_kvcache", "attn_fwd_mask", "attn_decode", "qkv_proj", "sinusoidal_pe", "masked_softmax", "attn_decode_workspace_bytes", "attn_fwd_plan", "attn_decode_plan",
+__all__ = ["attn_fwd", "attn_fwd_kvcache", "attn_fwd_mask", "attn_decode", "attn_decode_noalloc", "qkv_proj", "sinusoidal_pe", "masked_softmax", "attn_decode_workspace_bytes", "attn_fwd_plan", "attn_decode_plan",
            "attn_set_timing_events", "attn_set_clock_probe",
            "AttnError", "ATTN_F32", "ATTN_BF16", "ATTN_F16", "lib", "LIB_PATH"]

@@ -372,8 +372,13 @@ int attn_decode_plan(int B, int H, int S_cap, int D, int dtype, attn_decode_plan
     return ok();
 }
 
-int attn_decode(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens, void* o, int B,
-                int H, int S_cap, int D, int dtype, void* workspace, size_t workspace_bytes) {
+namespace {
+
+// attn_decode and attn_decode_noalloc: validation and launch. A NULL
+// workspace with noalloc set means this GPU's fixed scratch array.
+int run_decode(const char* fn, const void* q, const void* kcache, const void* vcache, const int32_t* seqlens,
+               void* o, int B, int H, int S_cap, int D, int dtype, void* workspace, size_t workspace_bytes,
+               bool noalloc) {
     hipEvent_t ev_start, ev_stop;
     take_events(ev_start, ev_stop);
     take_clock_probe();   // armed for an attn_fwd call only
@@ -385,24 +390,35 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
     const long long nq = tensor_bytes(B, 1, H, D, es), nkv = tensor_bytes(B, S_cap, H, D, es);
     const long long nsl = (long long)B * 4;
     if (!q || !kcache || !vcache || !seqlens || !o)
-        return fail(ATTN_ERR_INVALID_ARG, "attn_decode: NULL tensor pointer");
+        return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + ": NULL tensor pointer");
     if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(o))
-        return fail(ATTN_ERR_INVALID_ARG, "attn_decode: tensor pointers must be 16-byte aligned");
+        return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + ": tensor pointers must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0)
-        return fail(ATTN_ERR_INVALID_ARG, "attn_decode: seqlens must be 4-byte aligned");
+        return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + ": seqlens must be 4-byte aligned");
+    if (noalloc) {
+        if (plan.workspace_bytes > attn::kDecodeScratchBytes)
+            return fail(ATTN_ERR_WORKSPACE, std::string(fn) + ": these sizes need " +
+                                                std::to_string(plan.workspace_bytes) +
+                                                " bytes of workspace, beyond the fixed " +
+                                                std::to_string(attn::kDecodeScratchBytes) + "-byte scratch");
+        const hipError_t se = attn::decode_scratch(&workspace);
+        if (se != hipSuccess)
+            return fail(ATTN_ERR_HIP, std::string(fn) + ": scratch lookup failed: " + hipGetErrorString(se));
+        workspace_bytes = attn::kDecodeScratchBytes;
+    }
     if (!workspace || workspace_bytes < plan.workspace_bytes)
-        return fail(ATTN_ERR_WORKSPACE, "attn_decode: workspace needs " + std::to_string(plan.workspace_bytes) +
+        return fail(ATTN_ERR_WORKSPACE, std::string(fn) + ": workspace needs " + std::to_string(plan.workspace_bytes) +
                                             " bytes, got " + std::to_string(workspace_bytes));
-    if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "attn_decode: workspace must be 16-byte aligned");
+    if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + ": workspace must be 16-byte aligned");
     const long long nws = (long long)plan.workspace_bytes;
     if (overlap(o, nq, q, nq) || overlap(o, nq, kcache, nkv) || overlap(o, nq, vcache, nkv) ||
         overlap(o, nq, seqlens, nsl) || overlap(o, nq, workspace, nws))
-        return fail(ATTN_ERR_INVALID_ARG, "attn_decode: output overlaps another argument");
+        return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + ": output overlaps another argument");
     if (overlap(workspace, nws, q, nq) || overlap(workspace, nws, kcache, nkv) ||
         overlap(workspace, nws, vcache, nkv) || overlap(workspace, nws, seqlens, nsl))
-        return fail(ATTN_ERR_INVALID_ARG, "attn_decode: workspace overlaps an input");
-    if (check_lengths_on()) {
-        const int cs = check_lengths("attn_decode", seqlens, B, S_cap);
+        return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + ": workspace overlaps an input");
+    if (!noalloc && check_lengths_on()) {   // (a host copy of the lengths)
+        const int cs = check_lengths(fn, seqlens, B, S_cap);
         if (cs != ATTN_OK) return cs;
     }
 
@@ -411,8 +427,22 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
                        ev_stop, next_decode_tag()};
     const hipError_t e = attn::launch_decode(a, elt_of(dtype), t_stream);
     if (e != hipSuccess)
-        return fail(ATTN_ERR_HIP, std::string("attn_decode: launch failed: ") + hipGetErrorString(e));
+        return fail(ATTN_ERR_HIP, std::string(std::string(fn) + ": launch failed: ") + hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+int attn_decode(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens, void* o, int B,
+                int H, int S_cap, int D, int dtype, void* workspace, size_t workspace_bytes) {
+    return run_decode("attn_decode", q, kcache, vcache, seqlens, o, B, H, S_cap, D, dtype, workspace,
+                      workspace_bytes, false);
+}
+
+int attn_decode_noalloc(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens, void* o,
+                        int B, int H, int S_cap, int D, int dtype) {
+    return run_decode("attn_decode_noalloc", q, kcache, vcache, seqlens, o, B, H, S_cap, D, dtype, nullptr, 0,
+                      true);
 }
 
 int attn_sinusoidal_pe(float* pe, int S, int d_model, int pos0) {

@@ -31,6 +31,8 @@
 // principles" page, section 3.2).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "../launch.h"
 #include "../plan.h"
 
@@ -622,6 +624,36 @@ hipError_t launch_decode(const DecodeArgs& a, Elt t, hipStream_t stream) {
         case Elt::F16: return launch_t<_Float16>(a, stream);
     }
     return hipErrorInvalidValue;
+}
+
+// The allocation-free decode's workspace: a file-scope device array, one copy
+// per GPU the library runs on, held until the process ends. It starts zeroed
+// (the flags' idle state) and every call leaves its flags zero again. In host
+// code the array's name is not a device address: the address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+namespace {
+__device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // per device, set once under the mutex
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+    *ptr = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace attn

@@ -82,6 +82,9 @@ hipError_t launch_fwd_row(const FwdArgs& a, Elt t, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 // Split-KV decode (one kernel: split, then the merge by the last finisher), any storage type.
 hipError_t launch_decode(const DecodeArgs& a, Elt t, hipStream_t stream);
+// Device address of this GPU's fixed decode workspace (kDecodeScratchBytes),
+// looked up once per device; no allocation.
+hipError_t decode_scratch(void** ptr);
 // Q/K/V projection GEMM, 16-bit storage.
 hipError_t launch_qkv_proj(const QkvArgs& a, Elt t, hipStream_t stream);
 // Row softmax of scale * s under the causal rule, any storage type.

@@ -178,6 +178,10 @@ ATTN_HD inline size_t decode_workspace_bytes(int B, int H, int /*S_cap*/, int D)
     return decode_records_bytes(B, H, D) + (size_t)decode_records(B) * (size_t)H * sizeof(unsigned long long);
 }
 
+// The allocation-free decode's fixed workspace (one per GPU): at most this
+// many bytes of records and flags, e.g. B <= 722 sequences at H = 32, D = 128.
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+
 // ---------------------------------------------------------------------------
 // Q/K/V projection GEMM: 256 x 384 tiles of C = X W^T, 32-wide K steps,
 // eight waves in a 2 x 4 grid (128 x 96 outputs each).

@@ -194,6 +194,22 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
                 size_t workspace_bytes);
 
 /*
+ * attn_decode_noalloc -- attn_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernel and results, with no workspace argument.
+ * Its workspace is the library's own fixed array in device memory, 16 MiB per
+ * GPU (kDecodeScratchBytes), looked up once per device and kept until the
+ * process ends; the call allocates nothing. Sizes whose workspace
+ * (attn_decode_workspace_bytes) exceeds it return ATTN_ERR_WORKSPACE (about
+ * B <= 722 sequences at H = 32, D = 128). Every call on a GPU shares that
+ * GPU's array: calls that overlap on one GPU (two streams, two threads) race
+ * and must be ordered by the caller. Arguments and errors otherwise as
+ * attn_decode (the ATTN_CHECK length copy is not made here).
+ */
+int attn_decode_noalloc(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens,
+                        void* o, int B, int H, int S_cap, int D, int dtype);
+
+/*
  * attn_qkv_proj -- the Q, K and V projections of the input rows as one GEMM
  * over the stacked weights: Q = X W_Q, K = X W_K, V = X W_V (MMHA page,
  * section 2), concatenated into a single GEMM ("Week-4 CUDA notes" page,
