@@ -136,8 +136,7 @@ int check_fwd_sizes(int B, int H, int S_q, int S_kv, int D, int causal, int dtyp
     if (D != 32 && D != 64 && D != 128)
         return fail(ATTN_ERR_UNSUPPORTED, std::string(fn) + ": head dim D=" + std::to_string(D) +
                                               " not built (32, 64 or 128)");
-    const long long out_elems = (long long)B * H * S_q;
-    if (out_elems == 0) return ATTN_OK;
+    if (B == 0 || H == 0 || S_q == 0) return ATTN_OK;   // an empty call (no product formed before the checks below)
     if (S_kv == 0)
         return fail(ATTN_ERR_INVALID_ARG, std::string(fn) + (kvcache ? ": S_cap == 0 leaves no cache rows"
                                                                      : ": S_kv == 0 leaves the softmax without keys"));
@@ -339,7 +338,8 @@ static unsigned long long next_decode_tag() {
 }
 
 size_t attn_decode_workspace_bytes(int B, int H, int S_cap, int D) {
-    if (B <= 0 || H <= 0 || S_cap <= 0 || D <= 0) return 0;
+    if (B <= 0 || H <= 0 || S_cap <= 0 || (D != 32 && D != 64 && D != 128)) return 0;
+    if (attn::decode_records(B) * H > 0x7fffffffLL) return 0;   // beyond what attn_decode_plan accepts
     return attn::decode_workspace_bytes(B, H, S_cap, D);
 }
 
@@ -354,7 +354,8 @@ int attn_decode_plan(int B, int H, int S_cap, int D, int dtype, attn_decode_plan
         return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: head dim D=" + std::to_string(D) + " not built");
     // key offsets inside one sequence are 32-bit (a load batch may reach
     // kDecodeBatch keys past the last valid one)
-    if (((long long)S_cap + attn::kDecodeBatch) * H * D * elem_size(dtype) > 0x7fffffffLL)
+    const long long seq_bytes = tensor_bytes(1, (long long)S_cap + attn::kDecodeBatch, H, D, elem_size(dtype));
+    if (seq_bytes < 0 || seq_bytes > 0x7fffffffLL)
         return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: one sequence's cache spans more than 2 GiB");
     if (tensor_bytes(B, S_cap, H, D, elem_size(dtype)) < 0 || attn::decode_records(B) * H > 0x7fffffffLL)
         return fail(ATTN_ERR_INVALID_ARG, "attn_decode: sizes overflow");
