@@ -9,7 +9,7 @@
 // section 4.1). An environment switch picks the implementation, as the
 // depthwise-convolution page's section 6.2 suggests for bisecting:
 //   ATTN_ALGO=auto (default) | tile | row
-// (auto and tile: the MFMA kernels -- the 16-bit tile kernel or the fp32
+// (auto and tile: the MFMA kernels -- the 16-bit prefill kernel or the fp32
 // kernel; row: the per-query row kernel for every storage type)
 // and ATTN_CHECK=1 turns on a debug check of the device-side lengths (a
 // synchronous copy to the host before the launch).
@@ -196,8 +196,6 @@ int run_fwd(const char* fn, const void* q, const void* k, const void* v, const i
         e = attn::launch_fwd_row(a, elt_of(dtype), t_stream);
     else if (dtype == ATTN_F32)
         e = attn::launch_fwd_f32(a, t_stream);
-    else if (key_mask)
-        e = attn::launch_fwd_tile(a, elt_of(dtype), t_stream);
     else
         e = attn::launch_fwd_prefill(a, elt_of(dtype), t_stream);
     if (e != hipSuccess)

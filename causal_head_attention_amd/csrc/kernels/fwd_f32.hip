@@ -197,10 +197,16 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __res
             for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
 
         // O^T += V^T . P^T; k-step j: key k0 + 8*(j/4) + 4g + j%4, dim 32*db + l32
+        // (the key of mask byte j: a hidden key's V is replaced by 0, so
+        // whatever its padding slot holds never reaches the sum)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) acc[db] = mfma_f32(cur.v[db][j], x[j], acc[db]);
+            for (int j = 0; j < 16; ++j) {
+                float vj = cur.v[db][j];
+                if constexpr (KMASK) vj = mb[j] == 0u ? 0.f : vj;
+                acc[db] = mfma_f32(vj, x[j], acc[db]);
+            }
         if constexpr (kPrefetch) cur = nxt;
     }
 

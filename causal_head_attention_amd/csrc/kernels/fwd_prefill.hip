@@ -108,6 +108,11 @@ __device__ __forceinline__ int swap_bits23(int x) {
 //            register plus an immediate.
 //   merge  : the partial softmax states of the key-half-1 waves, exchanged
 //            in rounds of kMdb accumulator blocks.
+//   masks  : (with a key-padding mask) 4 stages of 256 bytes: the tile's
+//            mask bytes as loaded from a 4-byte aligned address, so the byte
+//            of key k sits at msh + k (msh: the mask row's address mod 4);
+//            then one bit per key tile of the entry: the tile holds a key
+//            the mask hides.
 template <int D>
 struct Cfg {
     static constexpr int KS = D / 16;      // MFMA k-steps of S^T
@@ -128,6 +133,9 @@ struct Cfg {
     static constexpr int MREC = prefill_merge_rec_floats(D);
     static constexpr int ROUNDS = DB / MDB;
     static constexpr int LDS = prefill_lds_bytes(D);
+    // (masked instantiation only) the key-mask stages, then the tile bits
+    static constexpr int MASKS = LDS;
+    static constexpr int TBITS = MASKS + kPrefillMaskStages * kPrefillMaskStageBytes;
     static constexpr int ROWS_PER_256 = 256 / VROW;   // V rows sharing one 256-byte bank span
     static_assert(K_STAGE % 1024 == 0 && V_STAGE % 1024 == 0, "stages are whole wave loads");
     static_assert(MERGE + 4 * 64 * MREC * 4 <= LDS, "layout fits");
@@ -175,6 +183,21 @@ __device__ __forceinline__ void lds_dma16(u32x4_t dv, unsigned voff, unsigned ld
     asm volatile(
         "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
         "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_addr), "v"(voff), "s"(d)
+        : "memory");
+}
+
+// 4 bytes per lane from global memory into LDS at lds_addr + 4*lane (the
+// dword form of the same path); out of range: 0.
+__device__ __forceinline__ void lds_dma4(u32x4_t dv, unsigned voff, unsigned lds_addr_v) {
+    const u32x4_t d = {(unsigned)__builtin_amdgcn_readfirstlane(dv[0]), (unsigned)__builtin_amdgcn_readfirstlane(dv[1]),
+                       (unsigned)__builtin_amdgcn_readfirstlane(dv[2]), (unsigned)__builtin_amdgcn_readfirstlane(dv[3])};
+    const unsigned lds_addr = (unsigned)__builtin_amdgcn_readfirstlane(lds_addr_v);
+    unsigned saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
         : "=&s"(saved)
         : "s"(lds_addr), "v"(voff), "s"(d)
         : "memory");
@@ -239,17 +262,23 @@ constexpr float kLazy = 8.0f;
 template <bool B>
 using Flag = std::integral_constant<bool, B>;
 
-template <typename T, int D>
+// The wave that loads the key-mask bytes: the last one, which has the
+// fewest K and V loads for every head dim.
+constexpr int kMaskWave = kTileWaves - 1;
+
+// KMASK: a key-padding mask is given (attn_fwd_mask; a separate
+// instantiation, so the unmasked kernel carries none of its work).
+template <typename T, int D, bool KMASK>
 __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     T* __restrict__ O, int B, int H, int S_q, int S_cap, int causal, float c /* scale*log2e */, int n_qblk,
     int items_per_bh, int paired, const int32_t* __restrict__ kv_lens, float* __restrict__ lse,
-    unsigned long long* __restrict__ clk) {
+    unsigned long long* __restrict__ clk, const uint8_t* __restrict__ key_mask) {
     typedef typename Mma<T>::v8 v8;
     typedef typename Mma<T>::v2 v2;
     using C = Cfg<D>;
     const v2 kOnes2 = {(T)1.0f, (T)1.0f};
-    __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
+    __shared__ __attribute__((aligned(1024))) char lds[KMASK ? prefill_lds_bytes_kmask(D) : C::LDS];
     const unsigned lds_u = (unsigned)(size_t)(lds_void_t*)lds;
 
     const int tid = threadIdx.x;
@@ -269,7 +298,12 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
 
     // ---- work item
     int bh, p;
-    if (!kv_lens) {
+    if (KMASK) {
+        // entries differ in the tiles their masks leave visible; kv_order
+        // spreads the heads of every entry over all XCDs, so no XCD is left
+        // with the longest entries alone
+        kv_order(blockIdx.x, gridDim.x, items_per_bh, bh, p);
+    } else if (!kv_lens) {
         const int item = xcd_remap(blockIdx.x, gridDim.x);
         bh = item / items_per_bh;
         p = item % items_per_bh;
@@ -297,27 +331,102 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
     const int qb_first = n_qblk - 1 - p;
     const int nblk = (paired && p != qb_first) ? 2 : 1;
     const int qbs[2] = {qb_first, p};
+    // the entry's row of the key mask, and its address mod 4
+    const uint8_t* const mrow = KMASK ? key_mask + (size_t)b * S_cap : nullptr;
+    const int msh = (int)((unsigned long long)mrow & 3u);
 
-    // tiles [0, hi) of each block (walked from hi-1 down), and how many of
+    // With a key mask, the tiles before the entry's first visible key and
+    // after its last one are skipped: [vis_lo, vis_hi) bounds the visible
+    // keys (empty when none is). The row is read in 16-byte pieces through a
+    // descriptor rounded out to 16-byte boundaries (a piece never reaches a
+    // page the row does not touch); bytes outside the row are ignored.
+    // The same pass marks the tiles that hold a hidden key; only their steps
+    // apply the mask to the scores.
+    int vis_lo = 0, vis_hi = S_kv;
+    if constexpr (KMASK) {
+        unsigned* tbits = (unsigned*)(lds + C::TBITS);
+        for (int i = tid; i < kPrefillMaskTileBits / 32; i += kTileThreads) tbits[i] = 0u;
+        __syncthreads();
+        const unsigned long long ra = (unsigned long long)mrow;
+        const int sh = (int)(ra & 15u);
+        const int n_ch = (sh + S_kv + 15) >> 4;
+        const __amdgpu_buffer_rsrc_t dm =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(mrow - sh), (short)0, n_ch * 16, 0x00020000);
+        int lo_t = S_kv, hi_t = 0;
+        for (int ch = tid; ch < n_ch; ch += kTileThreads) {
+            const u32x4_t w =
+                __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(dm, 16u * (unsigned)ch, 0, 0));
+            const int k0 = 16 * ch - sh;   // row index of the piece's first byte
+            int hid_first = S_kv, hid_last = -1;   // hidden keys of the piece
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                const int k = k0 + x;
+                if (k >= 0 && k < S_kv) {
+                    if (((w[x >> 2] >> (8 * (x & 3))) & 0xFFu) != 0u) {
+                        lo_t = min(lo_t, k);
+                        hi_t = k + 1;
+                    } else {
+                        hid_first = min(hid_first, k);
+                        hid_last = k;
+                    }
+                }
+            }
+            // a piece spans at most two tiles
+            if (hid_last >= 0) {
+                const int t0 = hid_first / kTileN, t1 = hid_last / kTileN;
+                if (t0 < kPrefillMaskTileBits) atomicOr(&tbits[t0 >> 5], 1u << (t0 & 31));
+                if (t1 != t0 && t1 < kPrefillMaskTileBits) atomicOr(&tbits[t1 >> 5], 1u << (t1 & 31));
+            }
+        }
+#pragma unroll
+        for (int x = 32; x >= 1; x >>= 1) {
+            lo_t = min(lo_t, __shfl_xor(lo_t, x));
+            hi_t = max(hi_t, __shfl_xor(hi_t, x));
+        }
+        // across the waves through the merge region (first used at the
+        // first block's end)
+        int* sv = (int*)(lds + C::MERGE);
+        if (lane == 0) {
+            sv[2 * wave] = lo_t;
+            sv[2 * wave + 1] = hi_t;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kTileWaves; ++w) {
+            lo_t = min(lo_t, sv[2 * w]);
+            hi_t = max(hi_t, sv[2 * w + 1]);
+        }
+        vis_lo = __builtin_amdgcn_readfirstlane(lo_t);
+        vis_hi = __builtin_amdgcn_readfirstlane(hi_t);
+    }
+
+    // tiles [lo, hi) of each block (walked from hi-1 down), and how many of
     // the top ones cross the diagonal or the key end
-    int hi_[2] = {0, 0}, nedge_[2] = {0, 0};
+    int hi_[2] = {0, 0}, lo_[2] = {0, 0}, nedge_[2] = {0, 0};
 #pragma unroll
     for (int ph = 0; ph < 2; ++ph) {
         if (ph < nblk) {
             const int qb = qbs[ph];
-            const int hi = tiles_for_block(qb, S_q, S_kv, causal);
+            int hi = tiles_for_block(qb, S_q, S_kv, causal);
             int full = S_kv / kTileN;   // tiles wholly inside the valid keys
             if (causal) {
                 const int lim = qb * kTileM + off + 1;   // keys the block's first query sees
                 full = min(full, lim > 0 ? lim / kTileN : 0);
             }
+            if constexpr (KMASK) {
+                hi = min(hi, (vis_hi + kTileN - 1) / kTileN);
+                lo_[ph] = min(vis_lo / kTileN, hi);
+            }
             hi_[ph] = hi;
             nedge_[ph] = hi - min(max(full, 0), hi);
         }
     }
-    const int nt0 = hi_[0];
-    const int N = nt0 + hi_[1];   // tiles in the item's stream
-    auto stream_tile = [&](int j) __attribute__((always_inline)) { return j < nt0 ? nt0 - 1 - j : hi_[1] - 1 - (j - nt0); };
+    const int nt0 = hi_[0] - lo_[0];
+    const int N = nt0 + hi_[1] - lo_[1];   // tiles in the item's stream
+    auto stream_tile = [&](int j) __attribute__((always_inline)) {
+        if constexpr (KMASK) return j < nt0 ? hi_[0] - 1 - j : hi_[1] - 1 - (j - nt0);
+        return j < nt0 ? nt0 - 1 - j : hi_[1] - 1 - (j - nt0);
+    };
 
     // ---- per-lane load offsets (loop-invariant; the tile moves the descriptor)
     unsigned k_voff[C::K_SLOTS], v_voff[C::V_SLOTS];
@@ -358,6 +467,10 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
         const unsigned range = (in && rem > 0) ? (unsigned)rem : 0u;
         return (u32x4_t){(unsigned)a, (unsigned)(a >> 32) & 0xFFFFu, range, 0x00020000u};
     };
+    // with a key mask, the mask bytes of stream tile j go with its K rows
+    // into mask stage j % 4: one wave loads 256 bytes from the 4-byte
+    // boundary at or below the tile's first byte (the range is rounded up to
+    // 4 bytes, so no load reaches a page the row does not touch)
     auto issue_k = [&](int j) __attribute__((always_inline)) {
         const u32x4_t d = tile_desc(k_head, j);
         const unsigned base = lds_u + C::K_RING + (unsigned)(j % kPrefillStages) * C::K_STAGE + 1024u * wave;
@@ -366,17 +479,54 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
             if (s < C::K_LOADS / kTileWaves || wave < C::K_LOADS % kTileWaves)
                 lds_dma16(d, k_voff[s], base + 1024u * kTileWaves * s);
         }
+        if constexpr (KMASK) {
+            if (wave == kMaskWave) {
+                const bool in = j < N;
+                const int t = in ? stream_tile(j) : 0;
+                const unsigned long long a = (unsigned long long)(mrow - msh + (size_t)t * kTileN);
+                const int rem = msh + S_kv - t * kTileN;   // bytes from a to the row's end
+                const u32x4_t dm = {(unsigned)a, (unsigned)(a >> 32) & 0xFFFFu,
+                                    (in && rem > 0) ? (unsigned)(rem + 3) & ~3u : 0u, 0x00020000u};
+                lds_dma4(dm, 4u * (unsigned)lane, lds_u + C::MASKS + (unsigned)(j & 3) * kPrefillMaskStageBytes);
+            }
+        }
     };
-    auto issue_v = [&](int j) __attribute__((always_inline)) {
+    // whether stream tile j holds a key the mask hides (wave-uniform): the
+    // LDS word of its bit, and the bit's position (32: a tile past the
+    // bits, taken as holding one)
+    auto tile_word = [&](int j, int& bit) __attribute__((always_inline)) {
+        const int t = j < N ? stream_tile(j) : 0;
+        bit = t < kPrefillMaskTileBits ? (t & 31) : 32;
+        return *(const unsigned*)(lds + C::TBITS + 4 * ((t < kPrefillMaskTileBits ? t : 0) >> 5));
+    };
+    auto tile_hides = [&](unsigned w, int bit) __attribute__((always_inline)) {
+        return bit >= 32 ? 1 : (int)(((unsigned)__builtin_amdgcn_readfirstlane(w) >> bit) & 1u);
+    };
+    // the mask bytes of the V rows this lane loads for stream tile j (read
+    // from LDS ahead of issue_v, so the read's latency is hidden)
+    auto v_mask_words = [&](int j, unsigned (&mw)[C::V_SLOTS]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < C::V_SLOTS; ++s) {
+            const int r = (64 * (wave + kTileWaves * s) + lane) / C::KCH;   // key row of the tile
+            // (a lane with no load in this slot reads a byte it ignores)
+            mw[s] = *(const unsigned char*)(lds + C::MASKS + (j & 3) * kPrefillMaskStageBytes + msh + (r & (kTileN - 1)));
+        }
+    };
+    // V rows of hidden keys get an out-of-range offset and land as zeros, so
+    // whatever a padding slot holds never reaches P.V
+    auto issue_v = [&](int j, const unsigned (&mw)[C::V_SLOTS]) __attribute__((always_inline)) {
         const u32x4_t d = tile_desc(v_head, j);
         const unsigned base = lds_u + C::V_RING + (unsigned)(j % kPrefillStages) * C::V_STAGE + 1024u * wave;
 #pragma unroll
         for (int s = 0; s < C::V_SLOTS; ++s) {
-            if (s < C::V_LOADS / kTileWaves || wave < C::V_LOADS % kTileWaves)
-                lds_dma16(d, v_voff[s], base + 1024u * kTileWaves * s);
+            if (s < C::V_LOADS / kTileWaves || wave < C::V_LOADS % kTileWaves) {
+                unsigned vo = v_voff[s];
+                if constexpr (KMASK) vo = (mw[s] & 0xFFu) != 0u ? vo : 0x80000000u;
+                lds_dma16(d, vo, base + 1024u * kTileWaves * s);
+            }
         }
     };
-    const int nld = nk_w + nv_w;   // this wave's loads per step
+    const int nld = nk_w + nv_w + (KMASK && wave == kMaskWave ? 1 : 0);   // this wave's loads per step
 
     // ---- per-lane operand offsets inside a stage
     const int k_lane = C::K_RING + (32 * half + l32) * C::KROW + 16 * g;
@@ -430,18 +580,36 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
         *(u32x4_t*)(lds + C::V_RING + (kPrefillStages - 1) * C::V_STAGE + 16 * i) = (u32x4_t){0u, 0u, 0u, 0u};
 
     // ---- opening loads: Q of the first block, K of stream tiles 0..2, V of 0
+    int hides_cur = 0;   // (key mask) the current step's tile holds a hidden key
+    if constexpr (KMASK) {
+        int bit;
+        const unsigned w = tile_word(0, bit);
+        hides_cur = tile_hides(w, bit);
+    }
+    unsigned vmw[C::V_SLOTS];
+#pragma unroll
+    for (int s = 0; s < C::V_SLOTS; ++s) vmw[s] = 1u;
     issue_q(qbs[0]);
     issue_k(0);
     issue_k(1);
-    issue_v(0);
-    issue_k(2);
-    // K(0) and K(1) must be in before the first scores and the first step
-    wait_vm_barrier(nld);
+    if constexpr (KMASK) {
+        // V(0) needs tile 0's mask bytes in LDS first
+        wait_vm_barrier(0);
+        v_mask_words(0, vmw);
+        issue_v(0, vmw);
+        issue_k(2);
+    } else {
+        issue_v(0, vmw);
+        issue_k(2);
+        // K(0) and K(1) must be in before the first scores and the first step
+        wait_vm_barrier(nld);
+    }
 
     int j0 = 0;   // stream index of the block's first tile
     for (int ph = 0; ph < nblk; ++ph) {
         const int qb = qbs[ph];
-        const int nt = hi_[ph];
+        const int lo = lo_[ph];
+        const int nt = hi_[ph] - lo;   // the block's steps
         const int n_edge = nedge_[ph];
         const int q0 = qb * kTileM + 32 * wq;    // first query of this wave
         const int qi = q0 + l32;                 // this lane's query
@@ -516,8 +684,33 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
                 for (int db = 0; db < C::DB; ++db) vaddr[db] = v_lane[db] + vs;
             }
             // (b) the diagonal and the key end: -inf past this lane's last key
-            const int kbase = (nt - 1 - u) * kTileN + 32 * half;   // first key of this wave's half tile
-            if (u < n_edge && ((causal && kbase + 31 > q0 + off) || (kbase + 32 > S_kv))) {
+            const int kbase = (lo + nt - 1 - u) * kTileN + 32 * half;   // first key of this wave's half tile
+            // (key mask) the next tile's flag and V rows' mask bytes, read now
+            // and used at the end of the step
+            unsigned hw_next = 0u;
+            int hbit_next = 0;
+            if constexpr (KMASK) {
+                hw_next = tile_word(j + 1, hbit_next);
+                v_mask_words(j + 1, vmw);
+            }
+            if (KMASK && hides_cur) {
+                // a tile with hidden keys: -inf for them too, by a select, so
+                // a NaN score of a padding slot is dropped (this lane's keys
+                // are 32*half + 16*(r/8) + 8*g + r%8: two runs of 8 bytes,
+                // each read as 12 aligned bytes and shifted by msh)
+                const char* mp = lds + C::MASKS + (j & 3) * kPrefillMaskStageBytes + 32 * half + 8 * g;
+                const u32x2_t m0 = *(const u32x2_t*)mp, m1 = *(const u32x2_t*)(mp + 16);
+                const unsigned e0 = *(const unsigned*)(mp + 8), e1 = *(const unsigned*)(mp + 24);
+                const unsigned x0 = m0[0], x1 = m0[1], y0 = m1[0], y1 = m1[1];
+                const unsigned mb[4] = {__builtin_amdgcn_alignbyte(x1, x0, msh), __builtin_amdgcn_alignbyte(e0, x1, msh),
+                                        __builtin_amdgcn_alignbyte(y1, y0, msh), __builtin_amdgcn_alignbyte(e1, y1, msh)};
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kbase + 16 * (r >> 3) + 8 * g + (r & 7);
+                    const bool hide = (key > lane_key_limit) | (key >= S_kv) | (((mb[r >> 2] >> (8 * (r & 3))) & 0xFFu) == 0u);
+                    s_c[r] = hide ? -INFINITY : s_c[r];
+                }
+            } else if (u < n_edge && ((causal && kbase + 31 > q0 + off) || (kbase + 32 > S_kv))) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = kbase + 16 * (r >> 3) + 8 * g + (r & 7);
@@ -542,11 +735,15 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
 #pragma unroll
                     for (int ks = 0; ks < C::KS; ++ks) ka[ks] = *(const v8*)(kp + 32 * ks);
                 }
-                // row max (one exchange with the partner lane l^32), lazy re-base
+                // row max (one exchange with the partner lane l^32), lazy
+                // re-base. IEEE maximum: a NaN score gives a NaN maximum (and
+                // no re-base) rather than being skipped, and on gfx950 it is
+                // one three-input instruction per two scores, with no quieting
+                // of the matrix cores' results first
                 float mx = s_c[0];
 #pragma unroll
-                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_c[r]);
-                mx = fmaxf(mx, partner_lane(mx)) * c;
+                for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, s_c[r]);
+                mx = __builtin_elementwise_maximum(mx, partner_lane(mx)) * c;
                 const bool rebase = __builtin_amdgcn_ballot_w64(mx > m_ref + kLazy) != 0;
                 const float m_new = rebase ? fmaxf(m_ref, mx) : m_ref;
                 const float alpha =
@@ -597,7 +794,8 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
             // (d) loads for later steps, issued once this step's MFMAs are
             // queued: K two steps ahead, V of the next tile
             issue_k(j + 3);
-            issue_v(j + 1);
+            issue_v(j + 1, vmw);
+            if constexpr (KMASK) hides_cur = tile_hides(hw_next, hbit_next);
             // (e) this wave's loads of the previous step have landed; publish
             wait_vm_barrier(nld);
         };
@@ -661,7 +859,9 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
                     const float mu = (m == -INFINITY) ? 0.f : m;
                     a0 = __builtin_amdgcn_exp2f(m_ref - mu);
                     a1 = __builtin_amdgcn_exp2f(m1 - mu);
-                    float l = a0 * l_run + a1 * l1;
+                    // (both weighted sums are written as one explicit fma, so
+                    // every instantiation rounds them the same way)
+                    float l = __builtin_fmaf(a0, l_run, a1 * l1);
                     l += partner_lane(l);
                     // a row that sees no key (a cache entry shorter than the chunk) is 0
                     inv = l > 0.f ? 1.0f / l : 0.f;
@@ -683,7 +883,7 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
                         T ob[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            ob[e] = (T)((a0 * acc[db][4 * q4 + e] + a1 * part[x][q4][e]) * inv);
+                            ob[e] = (T)(__builtin_fmaf(a0, acc[db][4 * q4 + e], a1 * part[x][q4][e]) * inv);
                         // lane holds head dims 32*db + 8*q4 + 4*g .. +3 of its
                         // query; rows past S_q fall outside the descriptor
                         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, ob), d_o,
@@ -701,14 +901,21 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
     }
 }
 
-template <typename T, int D>
-hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
+template <typename T, int D, bool KMASK>
+hipError_t launch_m(const FwdArgs& a, hipStream_t stream) {
     const TileGrid tg = tile_grid(a.B, a.H, a.S_q, a.causal, a.kv_lens != nullptr);
-    hipExtLaunchKernelGGL((prefill_kernel<T, D>), dim3((unsigned)tg.n_items), dim3(kTileThreads), 0, stream,
+    hipExtLaunchKernelGGL((prefill_kernel<T, D, KMASK>), dim3((unsigned)tg.n_items), dim3(kTileThreads), 0, stream,
                           a.ev_start, a.ev_stop, 0, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                           (T*)a.o, a.B, a.H, a.S_q, a.S_kv, a.causal, a.scale_log2, tg.n_qblk, tg.items_per_bh,
-                          tg.paired, a.kv_lens, a.lse, a.clock_probe);
+                          tg.paired, a.kv_lens, a.lse, a.clock_probe, a.key_mask);
     return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
+    // the mask comes without per-entry lengths (attn_fwd_mask)
+    if (a.key_mask) return a.kv_lens ? hipErrorInvalidValue : launch_m<T, D, true>(a, stream);
+    return launch_m<T, D, false>(a, stream);
 }
 
 template <typename T>

@@ -139,8 +139,10 @@ __global__ __launch_bounds__(kRowThreads) void fwd_row_kernel(const T* __restric
 #pragma unroll
                 for (int u = 0; u < kRowVBatch; ++u) {
                     const float p = __shfl(pj, jb + u);
+                    // a weight of exactly 0 (a hidden key) adds nothing, also
+                    // when that key's padding slot holds a NaN
 #pragma unroll
-                    for (int e = 0; e < DPL; ++e) acc[e] = __builtin_fmaf(p, vv[u][e], acc[e]);
+                    for (int e = 0; e < DPL; ++e) acc[e] = __builtin_fmaf(p, p != 0.f ? vv[u][e] : 0.f, acc[e]);
                 }
             }
         } else {
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(kRowThreads) void fwd_row_kernel(const T* __restric
 #pragma unroll
                 for (int e = 0; e < DPL; ++e) {
                     const int d = lane + 64 * e;
-                    if (d < D) acc[e] = __builtin_fmaf(p, to_f32(vrow[d]), acc[e]);
+                    if (d < D) acc[e] = __builtin_fmaf(p, p != 0.f ? to_f32(vrow[d]) : 0.f, acc[e]);
                 }
             }
         }

@@ -72,15 +72,14 @@ struct SoftmaxArgs {
     hipEvent_t ev_stop;
 };
 
-// MFMA tile kernel for 16-bit storage (BF16 or F16); D in {32, 64, 128}.
-hipError_t launch_fwd_tile(const FwdArgs& a, Elt t, hipStream_t stream);
-// MFMA prefill kernel for 16-bit storage without a key mask; D in {32, 64, 128}.
+// MFMA prefill kernel for 16-bit storage (BF16 or F16), with or without a
+// key mask; D in {32, 64, 128}.
 hipError_t launch_fwd_prefill(const FwdArgs& a, Elt t, hipStream_t stream);
 // Row kernel: one wave per query row, any storage type.
 hipError_t launch_fwd_row(const FwdArgs& a, Elt t, hipStream_t stream);
 // fp32 kernel on the fp32 matrix cores; D in {32, 64, 128}.
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
-// Split-KV decode (one kernel: split, then the merge by the last finisher), any storage type.
+// Split-KV decode (one kernel: streaming workgroups, then merging workgroups), any storage type.
 hipError_t launch_decode(const DecodeArgs& a, Elt t, hipStream_t stream);
 // Device address of this GPU's fixed decode workspace (kDecodeScratchBytes),
 // looked up once per device; no allocation.

@@ -16,7 +16,7 @@
 namespace attn {
 
 // ---------------------------------------------------------------------------
-// MFMA bf16 tile kernel (prefill).
+// MFMA prefill kernel (bf16 or fp16 storage): work items and tiles.
 //   A work item is one (b, h, query block of BM rows); with the causal mask,
 //   query blocks r and n-1-r share one workgroup so every workgroup visits
 //   the same number of KV tiles (the causal triangle folded in half).
@@ -44,27 +44,7 @@ ATTN_HD inline int xcd_remap(int x, int n) {
     return tall * per + (xcd - tall) * (per - 1) + local;
 }
 
-// Key-mask stages of the tile kernel: four tiles of kTileN bytes.
-constexpr int kMaskStageBytes = 4 * kTileN;
-
-// Row stride of a V tile in LDS (key rows of D 16-bit values): 64 or 192
-// bytes past a multiple of 256, so the 4 rows one half-wave's transposing
-// read touches fall in distinct 64-byte bank windows.
-ATTN_HD constexpr int tile_vrow_bytes(int D) { return 2 * D == 64 ? 64 : 2 * D + 64; }
-
-// LDS bytes of the tile kernel for head dim D: two stages of (K tile with
-// rows padded to 2*D+16 bytes, V tile with rows of tile_vrow_bytes(D)), or
-// the end-of-block exchange of the partial softmax states of four waves
-// (64 lanes x (2 + D/2) floats each), whichever is larger; then the
-// key-mask stages.
-ATTN_HD constexpr int tile_stage_bytes(int D) {
-    return (2 * kTileN * ((2 * D + 16) + tile_vrow_bytes(D))) > (4 * 64 * (2 + D / 2) * 4)
-               ? (2 * kTileN * ((2 * D + 16) + tile_vrow_bytes(D)))
-               : (4 * 64 * (2 + D / 2) * 4);
-}
-ATTN_HD constexpr int tile_lds_bytes(int D) { return tile_stage_bytes(D) + kMaskStageBytes; }
-
-// Prefill kernel (attn_fwd, attn_fwd_kvcache; fwd_prefill.hip): the same
+// Prefill kernel (attn_fwd, attn_fwd_kvcache, attn_fwd_mask; fwd_prefill.hip):
 // items, waves and tiles as above, with K and V tiles loaded straight into a
 // ring of kPrefillStages LDS stages. K rows are padded by 16 bytes; V rows are
 // unpadded (their 16-byte chunks swizzled instead). The key-half merge goes
@@ -79,6 +59,18 @@ ATTN_HD constexpr int prefill_merge_rec_floats(int D) { return 16 * prefill_merg
 ATTN_HD constexpr int prefill_lds_bytes(int D) {
     return kPrefillStages * (prefill_k_stage_bytes(D) + prefill_v_stage_bytes(D)) +
            4 * 64 * prefill_merge_rec_floats(D) * 4;
+}
+
+// With a key-padding mask (attn_fwd_mask) the prefill kernel adds four
+// key-mask stages of 256 bytes (64 lanes x 4 bytes, of which a tile's 64
+// mask bytes and up to 3 bytes of alignment are used) and one bit per key
+// tile of the entry, set where the tile holds a hidden key, for the first
+// kPrefillMaskTileBits tiles (later tiles count as holding one).
+constexpr int kPrefillMaskStages = 4;
+constexpr int kPrefillMaskStageBytes = 4 * kTileN;
+constexpr int kPrefillMaskTileBits = 16384;
+ATTN_HD constexpr int prefill_lds_bytes_kmask(int D) {
+    return prefill_lds_bytes(D) + kPrefillMaskStages * kPrefillMaskStageBytes + kPrefillMaskTileBits / 8;
 }
 
 // Number of KV tiles query block qb must visit.

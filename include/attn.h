@@ -43,11 +43,12 @@
  *  - Arithmetic: scores, softmax and accumulation in fp32 whatever the
  *    storage type (MMHA page, section 3.3); the scale 1/sqrt(D) is an fp32
  *    value. bf16 results are rounded to nearest even.
- *  - Inputs are finite numbers. The bf16 / fp16 forward kernel assumes no
- *    NaN (its row maximum skips NaN handling): a NaN in the visible part of
- *    Q, K or V gives an unspecified output row. Memory past the valid rows
- *    (cache rows past a length, padded tails) is never used and may hold
- *    anything, NaN included.
+ *  - Memory a call does not use -- cache rows past a length, padded tails,
+ *    the K and V rows of keys a key mask hides -- never reaches a result and
+ *    may hold anything, NaN and infinities included. Non-finite values in
+ *    the data a call does use are not screened: they propagate into the
+ *    affected output rows as IEEE arithmetic has it (a NaN score or value
+ *    gives a NaN row).
  */
 #ifndef ATTN_GFX950_H
 #define ATTN_GFX950_H
@@ -137,9 +138,10 @@ int attn_fwd_kvcache(const void* q, const void* kcache, const void* vcache, cons
  *              required.
  *   lse      : DEVICE float [B, H, S_q] or NULL, as attn_fwd_kvcache.
  * A query row left with no visible key gets an all-zero output row and a
- * log-sum-exp of -inf. Hidden keys' K and V rows are read and their values
- * enter P.V with weight 0, so they must hold finite numbers. o may not
- * overlap any other argument, nor lse any input.
+ * log-sum-exp of -inf. Hidden keys' K and V rows never reach the result
+ * (their scores are replaced by -inf by selection, and their V rows are
+ * loaded as zeros or skipped), so padding slots may hold anything, NaN
+ * included. o may not overlap any other argument, nor lse any input.
  */
 int attn_fwd_mask(const void* q, const void* k, const void* v, const uint8_t* key_mask, void* o,
                   float* lse, int B, int H, int S_q, int S_kv, int D, int causal, int dtype);

@@ -10,7 +10,6 @@
 
 namespace attn {
 int g_launches = 0;
-hipError_t launch_fwd_tile(const FwdArgs&, Elt, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_fwd_prefill(const FwdArgs&, Elt, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_fwd_row(const FwdArgs&, Elt, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_fwd_f32(const FwdArgs&, hipStream_t) { ++g_launches; return hipSuccess; }

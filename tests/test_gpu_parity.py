@@ -549,18 +549,89 @@ def test_key_mask_against_oracle(attn, case, dtype):
 
 @pytest.mark.parametrize("dtype", ALL_DTYPES, ids=DTYPE_IDS)
 def test_key_mask_absent_or_all_visible_is_attn_fwd(attn, dtype):
-    """No mask is the attn_fwd kernel itself (bitwise). An all-visible mask runs
-    the key-mask kernel, whose fp32 rounding order may differ: it must agree
-    with attn_fwd to within two units of the storage type's last place."""
-    q, k, v = (t.cuda() for t in workloads.make_prefill_shape(610, dtype, 2, 3, 300, 300, 128))
-    for causal in (True, False):
-        ref = attn.attn_fwd(q, k, v, causal=causal)
-        o1 = attn.attn_fwd_mask(q, k, v, None, causal=causal)
-        o2 = attn.attn_fwd_mask(q, k, v, torch.ones(2, 300, dtype=torch.bool, device="cuda"), causal=causal)
-        assert torch.equal(o1, ref)
-        ulp = {torch.float32: 2.0 ** -23, torch.bfloat16: 2.0 ** -7, torch.float16: 2.0 ** -10}[dtype]
-        tol = 2 * ulp * torch.clamp(ref.float().abs(), min=2.0 ** -6)
-        assert torch.all((o2.float() - ref.float()).abs() <= tol)
+    """No mask is the attn_fwd kernel itself, and an all-visible mask runs the
+    key-mask instantiation of the same kernel, which takes the same steps in
+    the same order: both bitwise equal to attn_fwd."""
+    for D in (128, 64, 32):
+        q, k, v = (t.cuda() for t in workloads.make_prefill_shape(610 + D, dtype, 2, 3, 300, 300, D))
+        for causal in (True, False):
+            ref = attn.attn_fwd(q, k, v, causal=causal)
+            o1 = attn.attn_fwd_mask(q, k, v, None, causal=causal)
+            o2 = attn.attn_fwd_mask(q, k, v, torch.ones(2, 300, dtype=torch.bool, device="cuda"), causal=causal)
+            assert torch.equal(o1, ref)
+            assert torch.equal(o2, ref), f"all-visible mask D={D} causal={causal}"
+
+
+NAN_PAD_CASES = [  # (B, H, S_q, S_kv, D, causal, pattern)
+    (3, 2, 200, 200, 128, True, "random"),
+    (2, 3, 129, 300, 64, False, "right_pad"),
+    (2, 2, 65, 131, 32, True, "left_pad"),     # odd S_kv: mask rows start at every address mod 4
+    (2, 2, 300, 300, 128, False, "right_pad"),
+]
+
+
+def _poison_hidden(t, m):
+    """K or V with every row of a hidden key (all heads) set to NaN, +inf or
+    -inf in turn: the contents of an unwritten padding slot."""
+    t = t.clone()
+    bad = torch.tensor([float("nan"), float("inf"), float("-inf")], dtype=t.dtype)
+    idx = (~m).nonzero()
+    for n, (b, j) in enumerate(idx.tolist()):
+        t[b, j] = bad[n % 3]
+    return t
+
+
+@pytest.mark.parametrize("dtype", ALL_DTYPES, ids=DTYPE_IDS)
+@pytest.mark.parametrize("case", NAN_PAD_CASES, ids=lambda c: "x".join(map(str, c[:6])) + "_" + c[6])
+def test_key_mask_ignores_nan_in_padding(attn, case, dtype):
+    """Hidden keys' K and V rows never reach the result: with NaN and +-inf in
+    every padding slot the output and log-sum-exp are bitwise those of the
+    same call on finite padding, and match the oracle on the finite data."""
+    B, H, S_q, S_kv, D, causal, pattern = case
+    say(f"NaN padding {case} {dtype}")
+    q, k, v = workloads.make_prefill_shape(640 + D, dtype, B, H, S_q, S_kv, D)
+    m = _make_mask(pattern, B, S_kv, 650 + S_kv)
+    kp, vp = _poison_hidden(k, m), _poison_hidden(v, m)
+    assert torch.isnan(kp.float()).any() and torch.isinf(vp.float()).any()
+    o, lse = attn.attn_fwd_mask(q.cuda(), k.cuda(), v.cuda(), m.cuda(), causal=causal, return_lse=True)
+    op, lsep = attn.attn_fwd_mask(q.cuda(), kp.cuda(), vp.cuda(), m.cuda(), causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(op, o) and torch.equal(lsep, lse)
+    ro, rlse = oracle.attn_fwd_mask(q, k, v, m.numpy(), causal)
+    check(op, ro, dtype, f"NaN padding {case}")
+    check_lse(lsep, rlse, dtype, f"NaN padding {case}")
+
+
+def test_key_mask_ignores_nan_in_padding_row_kernel(attn, monkeypatch):
+    """The same for the per-query row kernel (the cross-check path)."""
+    B, H, S, D = 2, 2, 150, 64
+    q, k, v = workloads.make_prefill_shape(660, torch.bfloat16, B, H, S, S, D)
+    m = _make_mask("right_pad", B, S, 661)
+    kp, vp = _poison_hidden(k, m), _poison_hidden(v, m)
+    monkeypatch.setenv("ATTN_ALGO", "row")
+    o = attn.attn_fwd_mask(q.cuda(), kp.cuda(), vp.cuda(), m.cuda(), causal=True)
+    torch.cuda.synchronize()
+    check(o, oracle.attn_fwd_mask(q, k, v, m.numpy(), True)[0], torch.bfloat16, "NaN padding row kernel")
+
+
+def test_key_mask_unaligned_rows_and_long_rows(attn):
+    """A mask that starts 3 bytes past an aligned address, and rows longer
+    than one pass of the kernel's visibility scan (16 bytes per thread)."""
+    for (B, H, S_q, S_kv, D, causal, pattern, off) in [(3, 2, 130, 257, 128, True, "random", 3),
+                                                       (1, 2, 64, 9001, 64, False, "left_pad", 1),
+                                                       (2, 1, 40, 8500, 32, False, "right_pad", 2)]:
+        say(f"mask at offset {off}: {(B, H, S_q, S_kv, D, causal, pattern)}")
+        q, k, v = workloads.make_prefill_shape(670 + D, torch.bfloat16, B, H, S_q, S_kv, D)
+        m = _make_mask(pattern, B, S_kv, 671 + S_kv)
+        buf = torch.zeros(off + B * S_kv + 5, dtype=torch.uint8, device="cuda")
+        mv = buf[off:off + B * S_kv].view(B, S_kv)
+        mv.copy_(m.to(torch.uint8).cuda())
+        assert mv.data_ptr() % 4 == off % 4
+        o, lse = attn.attn_fwd_mask(q.cuda(), k.cuda(), v.cuda(), mv, causal=causal, return_lse=True)
+        torch.cuda.synchronize()
+        ro, rlse = oracle.attn_fwd_mask(q, k, v, m.numpy(), causal)
+        check(o, ro, torch.bfloat16, f"mask offset {off}")
+        check_lse(lse, rlse, torch.bfloat16, f"mask offset {off}")
 
 
 def test_key_mask_row_kernel_cross_check(attn, monkeypatch):
