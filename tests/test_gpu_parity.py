@@ -615,11 +615,14 @@ def test_key_mask_ignores_nan_in_padding_row_kernel(attn, monkeypatch):
 
 
 def test_key_mask_unaligned_rows_and_long_rows(attn):
-    """A mask that starts 3 bytes past an aligned address, and rows longer
-    than one pass of the kernel's visibility scan (16 bytes per thread)."""
+    """A mask that starts 1-3 bytes past an aligned address, rows longer than
+    one pass of the kernel's visibility scan (16 bytes per thread, up to
+    40,000 keys), and 300 entries of a ragged 65-key row."""
     for (B, H, S_q, S_kv, D, causal, pattern, off) in [(3, 2, 130, 257, 128, True, "random", 3),
                                                        (1, 2, 64, 9001, 64, False, "left_pad", 1),
-                                                       (2, 1, 40, 8500, 32, False, "right_pad", 2)]:
+                                                       (2, 1, 40, 8500, 32, False, "right_pad", 2),
+                                                       (2, 1, 32, 40000, 64, False, "right_pad", 1),
+                                                       (300, 1, 16, 65, 32, True, "random", 2)]:
         say(f"mask at offset {off}: {(B, H, S_q, S_kv, D, causal, pattern)}")
         q, k, v = workloads.make_prefill_shape(670 + D, torch.bfloat16, B, H, S_q, S_kv, D)
         m = _make_mask(pattern, B, S_kv, 671 + S_kv)
