@@ -87,6 +87,10 @@ def _load() -> ctypes.CDLL:
     lib.attn_decode_plan.restype = i
     lib.attn_xcd_remap.argtypes = [i, i]
     lib.attn_xcd_remap.restype = i
+    lib.attn_decode_range_start.argtypes = [i, i]
+    lib.attn_decode_range_start.restype = i
+    lib.attn_decode_range_of.argtypes = [i, i]
+    lib.attn_decode_range_of.restype = i
     return lib
 
 

@@ -245,6 +245,16 @@ int attn_xcd_remap(int x, int n) {
     return attn::xcd_remap(x, n);
 }
 
+int attn_decode_range_start(int w, int T) {
+    if (T < 0 || w < 0 || w > attn::kDecodeSplitWGs) return -1;
+    return attn::decode_range_start(w, T);
+}
+
+int attn_decode_range_of(int t, int T) {
+    if (T <= 0 || t < 0 || t >= T) return -1;
+    return attn::decode_range_of(t, T);
+}
+
 int attn_fwd_plan(int B, int H, int S_q, int S_kv, int D, int causal, int dtype, attn_fwd_plan_t* plan) {
     if (!plan) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_plan: plan is NULL");
     std::memset(plan, 0, sizeof(*plan));

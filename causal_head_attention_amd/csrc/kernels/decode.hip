@@ -1,16 +1,17 @@
 // decode.hip -- single-query attention against a KV cache, split along the keys.
 //
 // One kernel. The valid keys of all sequences, laid end to end, form one
-// token space; workgroup w of kDecodeSplitWGs (one per CU) streams an equal
-// share of it, for ALL heads, one segment per sequence its share touches.
+// token space; workgroup w of kDecodeSplitWGs (one per CU) streams one
+// contiguous share of it (the shares are sized to the XCD the workgroup
+// runs on), for ALL heads, one segment per sequence its share touches.
 // The cache is [B, S_cap, H, D], so one token's H head rows are one
 // contiguous span: each wave owns a group of heads whose rows for one token
 // are read by one 16-byte-per-lane load instruction, and the eight waves of
 // the workgroup together sweep whole token rows. A head's D elements sit in
 // one group of D*sizeof(T)/16 lanes ("a row"), so the dot product reduces
 // with DPP inside the row and the head's softmax state (max, sum, D
-// accumulators) lives in that row. Equal shares keep every CU streaming
-// until the end (a fixed number of keys per workgroup left a partly idle
+// accumulators) lives in that row. Shares of the whole token space keep
+// every CU streaming until the end (a fixed number of keys per workgroup left a partly idle
 // second wave of workgroups and many that only found their sequence
 // already ended).
 // A segment that holds a whole sequence divides by its sum and writes the
@@ -248,6 +249,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const T* __restr
     constexpr bool k16 = sizeof(T) == 2;   // bf16 or fp16: packed v_dot2 paths
     __shared__ int red[kDecodeWaves];
     __shared__ int incl_s[kDecodeScanLds];   // inclusive prefix sums of the lengths
+    __shared__ int batches_s[kDecodeWaves];  // load batches each wave has started
 
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     const int w = blockIdx.x;
@@ -287,7 +289,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const T* __restr
         __shared__ float part_acc[kDecodeWaves][64 * E];
         __shared__ float part_ml[kDecodeWaves][64][2];
         __shared__ int part_ok[kDecodeWaves];
-        const int Ct = (Ttot + G - 1) / G;
         const int m = w - G, GM = gridDim.x - G;
         for (int p = m; p < B * n_groups; p += GM) {
             const int b = p / n_groups, grp = p % n_groups;
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const T* __restr
             Pb = uni(Pb);
             len = uni(len);
             if (len == 0) continue;   // uniform
-            const int w0 = (int)(Pb / Ct), ns = (int)((Pb + len - 1) / Ct) - w0 + 1;
+            const int w0 = decode_range_of(Pb, Ttot), ns = decode_range_of(Pb + len - 1, Ttot) - w0 + 1;
             if (ns == 1) continue;   // uniform: one workgroup held it whole
             // this wave's segments: wave, wave + kDecodeWaves, ...
             bool ready = false;
@@ -376,9 +377,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const T* __restr
         }
     }
     if (Ttot == 0) return;   // uniform
-    const int Ct = (Ttot + G - 1) / G;
-    const int lo = w * Ct;
-    const int hi = lo + Ct < Ttot ? lo + Ct : Ttot;
+    const int lo = decode_range_start(w, Ttot);
+    const int hi = decode_range_start(w + 1, Ttot);
     if (lo >= hi) return;   // uniform
 
     // (2) first sequence reaching into [lo, hi): the number of sequences
@@ -438,6 +438,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const T* __restr
     const int key_bytes = H * D * (int)sizeof(T);
     const int P0 = P;   // where sequence b_first starts
     int last_b = b_first;
+    // Waves w and w ^ 4 share a SIMD and stream the same keys for different
+    // heads. Issue arbitration favours the older wave: left alone, waves 0-3
+    // finished their keys well before waves 4-7, which then streamed on with
+    // half the loads in flight per SIMD. So before each batch a wave compares
+    // its batch count with its partner's (a relaxed read; a stale value only
+    // delays the correction) and, while behind, takes the highest priority.
+    static_assert(kDecodeWaves == 8, "waves w and w ^ 4 share a SIMD");
+    if (lane == 0) __hip_atomic_store(&batches_s[wave], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __syncthreads();
+    int batches = 0;
     for (int b = b_first; b < B && P < hi; ++b) {
         const int len = uni(scan_in_lds ? incl_s[b] - P : clamp_len(seqlens[b], S_cap));
         if (len > 0) {
@@ -469,6 +479,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const T* __restr
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[e] = 0.f;
                 for (int kb = k0; kb < k1; kb += NB) {
+                    const int partner = uni(
+                        __hip_atomic_load(&batches_s[wave ^ 4], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+                    if (batches < partner) __builtin_amdgcn_s_setprio(3);
+                    else if (batches > partner) __builtin_amdgcn_s_setprio(0);
+                    ++batches;
+                    if (lane == 0)
+                        __hip_atomic_store(&batches_s[wave], batches, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                     u32x4_t kr[NB], vr[NB];
                     // read-once stream: non-temporal, so the loads do not allocate in
                     // the caches (and do not evict whatever is resident there); K
@@ -567,6 +584,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const T* __restr
         }
         P += len;
     }
+    __builtin_amdgcn_s_setprio(0);
 
     // (4) flags. Only the first and the last segment of the range can be
     // part of a longer sequence: the first when that sequence starts before

@@ -128,10 +128,10 @@ constexpr int kF32Threads = 512;
 // ---------------------------------------------------------------------------
 // Split-KV decode, one kernel.
 //   The valid keys of all sequences, laid end to end, form one token space
-//   of T = sum of the lengths. Workgroup w (of kDecodeSplitWGs) takes
-//   tokens [w*C, (w+1)*C) with C = ceil(T / kDecodeSplitWGs): every
-//   workgroup streams the same number of keys, and a range that crosses a
-//   sequence boundary is processed as one segment per sequence. Each
+//   of T = sum of the lengths. Workgroup w (of kDecodeSplitWGs) takes one
+//   contiguous range of it (decode_range_start below), in order, and a
+//   range that crosses a sequence boundary is processed as one segment per
+//   sequence. Each
 //   workgroup covers ALL heads of its keys: each wave owns a group of heads,
 //   each load instruction reads one token's rows of those heads (contiguous
 //   bytes). A segment that holds a whole sequence writes its output rows
@@ -143,12 +143,47 @@ constexpr int kF32Threads = 512;
 // ---------------------------------------------------------------------------
 constexpr int kDecodeWaves = 8;
 constexpr int kDecodeSplitWGs = 256;      // one per CU of the chip
-constexpr int kDecodeBatch = 16;          // keys whose loads are in flight together
+constexpr int kDecodeBatch = 8;           // keys whose loads are in flight together
 constexpr int kDecodeThreads = kDecodeWaves * 64;
 constexpr int kDecodeScanLds = 1024;      // length prefix sums kept in LDS up to this many sequences
 constexpr int kDecodeMergeWGs = 256;      // merging workgroups at most (one per (sequence, head group) pair)
 constexpr int kDecodeMergeBatch = 8;      // records whose loads are in flight together in a merge
 constexpr int kDecodeSpinLimit = 1 << 22;  // polls of the segments' flags before a merge gives up (seconds)
+
+// The streaming workgroups' ranges. Workgroups are dealt to the XCDs
+// round-robin, so workgroup w runs on XCD w % 8, and on MI355X the odd XCDs
+// stream about 8% slower than the even ones (a plain read in the decode's
+// pattern shows it, and it stays with the XCD when every workgroup's range
+// is moved to its neighbour). So each pair of workgroups (2p, 2p+1) shares
+// a span of decode_pair_span(T) tokens unequally: the even one takes
+// kDecodeEvenPermille / 1000 of it, rounded up, the odd one the rest. With
+// T <= kDecodeSplitWGs tokens, workgroup w takes token w alone.
+// The ranges tile [0, T) in workgroup order, and the empty ones come last
+// (the spans are then at least 3 tokens, of which each side takes one or
+// more): every workgroup between the first and the last of a sequence holds
+// some of its keys, as the merge assumes.
+constexpr int kDecodeEvenPermille = 530;
+ATTN_HD inline int decode_pair_span(int T) {
+    return (int)(((long long)T + kDecodeSplitWGs / 2 - 1) / (kDecodeSplitWGs / 2));
+}
+ATTN_HD inline int decode_even_part(int span) {   // for span >= 3: in [1, span - 1]
+    return (int)(((long long)span * kDecodeEvenPermille + 999) / 1000);
+}
+// First token of workgroup w's range, for 0 <= w <= kDecodeSplitWGs (w =
+// kDecodeSplitWGs gives T, the end of the last range).
+ATTN_HD inline int decode_range_start(int w, int T) {
+    if (T <= kDecodeSplitWGs) return w < T ? w : T;
+    const int span = decode_pair_span(T);
+    const long long s = (long long)(w >> 1) * span + ((w & 1) ? decode_even_part(span) : 0);
+    return s < T ? (int)s : T;
+}
+// The workgroup whose range holds token t, for 0 <= t < T.
+ATTN_HD inline int decode_range_of(int t, int T) {
+    if (T <= kDecodeSplitWGs) return t;
+    const int span = decode_pair_span(T);
+    const int p = t / span;
+    return 2 * p + (t - p * span >= decode_even_part(span) ? 1 : 0);
+}
 
 // Partial records: segment (w, b) uses index w + b, so at most
 // kDecodeSplitWGs + B - 1 of them.

@@ -356,7 +356,7 @@ int attn_fwd_plan(int B, int H, int S_q, int S_kv, int D, int causal, int dtype,
                   attn_fwd_plan_t* plan);
 
 /*
- * Decode plan: split workgroups (each streams an equal share of the
+ * Decode plan: split workgroups (each streams one contiguous share of the
  * sequences' valid keys), the partial records the workspace holds per head
  * (one per workgroup-sequence segment), threads per workgroup, and the
  * workspace size. Host only.
@@ -371,12 +371,26 @@ typedef struct {
 int attn_decode_plan(int B, int H, int S_cap, int D, int dtype, attn_decode_plan_t* plan);
 
 /*
- * Workgroup-id remap used by the tile kernel: hardware workgroup x of n runs
- * on XCD x % 8; the remap gives each XCD a contiguous range of logical work
- * items so the items of one head share that XCD's L2. A bijection on
- * [0, n). Exposed so the host tests can check it.
+ * Workgroup-id remap used by the prefill, fp32 and projection kernels:
+ * hardware workgroup x of n runs on XCD x % 8; the remap gives each XCD a
+ * contiguous range of logical work items so the items of one head share
+ * that XCD's L2. A bijection on [0, n). Exposed so the host tests can check
+ * it.
  */
 int attn_xcd_remap(int x, int n);
+
+/*
+ * The decode's split of a token space of T valid keys (all sequences laid
+ * end to end) over its split workgroups: attn_decode_range_start(w, T) is
+ * the first token of workgroup w's range (0 <= w <= split_workgroups; w =
+ * split_workgroups gives T), attn_decode_range_of(t, T) the workgroup whose
+ * range holds token t (0 <= t < T). Workgroup w runs on XCD w % 8, and each
+ * pair (2p, 2p+1) shares its span unequally, the even one taking 53%, since
+ * MI355X's odd XCDs stream about 8% slower. Both return -1 for arguments
+ * out of range. Exposed so the host tests can check them.
+ */
+int attn_decode_range_start(int w, int T);
+int attn_decode_range_of(int t, int T);
 
 #ifdef __cplusplus
 }

@@ -8,6 +8,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 import torch
 
@@ -168,6 +169,62 @@ def test_decode_workspace_and_plan():
     assert p.workspace_bytes == attn.attn_decode_workspace_bytes(16, 32, 4096, 128)
     with pytest.raises(attn.AttnError):   # one sequence's cache beyond 32-bit offsets
         attn.attn_decode_plan(1, 32, 1 << 18, 128, attn.ATTN_BF16)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 13, 127, 128, 129, 255, 256, 257, 258, 300, 383, 384, 385, 1000, 24304,
+                               65535, 1 << 20, (1 << 31) - 1])
+def test_decode_ranges_tile_the_token_space(T):
+    G = attn.attn_decode_plan(16, 32, 4096, 128, attn.ATTN_BF16).split_workgroups
+    starts = [L.attn_decode_range_start(w, T) for w in range(G + 1)]
+    assert starts[0] == 0 and starts[G] == T
+    assert all(a <= b for a, b in zip(starts, starts[1:]))
+    # the empty ranges come last: a sequence's keys never skip a workgroup
+    sizes = [b - a for a, b in zip(starts, starts[1:])]
+    n_full = sum(1 for x in sizes if x > 0)
+    assert all(x > 0 for x in sizes[:n_full]) and not any(sizes[n_full:])
+    probes = {0, T - 1} | {min(T - 1, s) for s in starts} | {max(0, s - 1) for s in starts}
+    probes |= set(range(0, T, max(1, T // 509)))
+    for t in sorted(probes):
+        w = L.attn_decode_range_of(t, T)
+        assert 0 <= w < G and starts[w] <= t < starts[w + 1], (t, w)
+    assert L.attn_decode_range_start(G + 1, T) == -1 and L.attn_decode_range_start(-1, T) == -1
+    assert L.attn_decode_range_of(T, T) == -1 and L.attn_decode_range_of(0, 0) == -1
+
+
+def test_decode_ranges_favour_even_xcds():
+    # 24,304 keys (the 16-sequence decode workload): spans of 190 keys per
+    # pair of workgroups, 101 for the even one (53%, rounded up), 89 for the odd
+    starts = [L.attn_decode_range_start(w, 24304) for w in range(257)]
+    sizes = [b - a for a, b in zip(starts, starts[1:])]
+    assert sizes[:4] == [101, 89, 101, 89]
+    assert sum(sizes) == 24304 and max(sizes) == 101
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_record_index_is_unique(seed):
+    # segment (w, b) -- workgroup w's part of sequence b -- writes record w + b;
+    # for any lengths (zeros included) no two segments share a record, and all
+    # fall below the plan's record count
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 300))
+    lens = rng.integers(0, (3, 5000, 40)[seed % 3], size=B)
+    lens[rng.random(B) < 0.2] = 0
+    T = int(lens.sum())
+    if T == 0:
+        return
+    G = 256
+    starts = [L.attn_decode_range_start(w, T) for w in range(G + 1)]
+    seen = set()
+    P = 0
+    for b, n in enumerate(lens.tolist()):
+        if n:
+            w0, w1 = L.attn_decode_range_of(P, T), L.attn_decode_range_of(P + n - 1, T)
+            for w in range(w0, w1 + 1):   # every one of them holds keys of b
+                assert max(starts[w], P) < min(starts[w + 1], P + n), (w, b)
+                assert w + b not in seen
+                seen.add(w + b)
+        P += n
+    assert max(seen) < attn.attn_decode_plan(B, 8, 64, 64, attn.ATTN_BF16).records
 
 
 def dec(q=A, kc=A + 0x100000, vc=A + 0x200000, sl=A + 0x300000, o=A + 0x310000, B=2, H=2, S_cap=100,
