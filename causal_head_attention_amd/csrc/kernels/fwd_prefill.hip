@@ -106,8 +106,9 @@ __device__ __forceinline__ int swap_bits23(int x) {
 //            consecutive lanes then read 8 (16) consecutive padded rows,
 //            which fall in distinct banks. Every operand read is a base
 //            register plus an immediate.
-//   merge  : the partial softmax states of the key-half-1 waves, exchanged
-//            in rounds of kMdb accumulator blocks.
+//   merge  : the two key halves' partial accumulators, exchanged one block
+//            per half and round, and their (m, l); with D = 32, the
+//            key-half-1 waves' one block and (m, l).
 //   masks  : (with a key-padding mask) 4 stages of 256 bytes: the tile's
 //            mask bytes as loaded from a 4-byte aligned address, so the byte
 //            of key k sits at msh + k (msh: the mask row's address mod 4);
@@ -214,6 +215,16 @@ __device__ __forceinline__ void wait_vm_barrier(int n) {
         case 4: asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
         case 5: asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
         case 6: asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+        case 7: asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+        case 8: asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+        case 9: asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+        case 10: asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+        case 11: asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+        case 12: asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+        case 13: asm volatile("s_waitcnt vmcnt(13) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+        case 14: asm volatile("s_waitcnt vmcnt(14) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+        case 15: asm volatile("s_waitcnt vmcnt(15) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+        case 16: asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
         default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
     }
 }
@@ -675,6 +686,12 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
         auto step = [&](auto mfma_first_f, auto last_f, int u, f32x16_t& s_c, f32x16_t& s_n) __attribute__((always_inline)) {
             constexpr bool LAST = decltype(last_f)::value;   // no next tile in this block
             const int j = j0 + u;
+            // the next block's Q: no MFMA of a block's last step reads Q, so
+            // its loads go out a step before the merge (the step's barrier
+            // lets them run on)
+            if constexpr (LAST) {
+                if (next_block) issue_q(qbs[ph + 1]);
+            }
             // this step's operand addresses: K of tile u+1, V of tile u-1
             const char* kp = lds + k_lane + ((j + 1) % kPrefillStages) * C::K_STAGE;
             int vaddr[C::DB];
@@ -797,7 +814,7 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
             issue_v(j + 1, vmw);
             if constexpr (KMASK) hides_cur = tile_hides(hw_next, hbit_next);
             // (e) this wave's loads of the previous step have landed; publish
-            wait_vm_barrier(nld);
+            wait_vm_barrier(LAST && next_block ? nld + C::KS : nld);
         };
 
         // two steps per iteration, so S(u) and S(u+1) swap registers without
@@ -829,69 +846,130 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
                     acc[db] = Mma<T>::mfma(vt_operand(v_lane[db] + vs + 16 * s2 * C::VROW), pb_prev[s2], acc[db]);
         }
 
-        // the next block's Q, under the merge
-        if (next_block) issue_q(qbs[ph + 1]);
-
-        // ---- merge the two key halves (waves wq and wq+4) through LDS, in
-        // rounds of MDB accumulator blocks; half 0 writes the block's rows
-        float* rec = (float*)(lds + C::MERGE) + (wq * 64 + lane) * C::MREC;
-        float a0 = 1.f, a1 = 0.f, inv = 0.f;
+        // ---- merge the two key halves (waves wq and wq+4) through LDS.
+        // With an even number of accumulator blocks both halves finalize:
+        // in round rd half 0 writes O block rd and half 1 block DB/2 + rd,
+        // each sending its partner the other one. Both compute the same
+        // weights from the two (m, l) and the same fma(a0, x0, a1 * x1) with
+        // x0 from half 0 and x1 from half 1, so which half finalizes a block
+        // does not change its bits. (One 32-row block, D = 32: half 1 sends,
+        // half 0 finalizes.)
+        if constexpr (C::DB % 2 == 0) {
+            constexpr int HB = C::DB / 2;
+            // [half][wq][q4][lane] float4 parts of a block, then [half][wq][lane] (m, l)
+            f32x4_t* const xs = (f32x4_t*)(lds + C::MERGE);
+            f32x2_t* const mls = (f32x2_t*)(lds + C::MERGE + 2 * 4 * 4 * 64 * 16);
+            static_assert(2 * 4 * 4 * 64 * 16 + 2 * 4 * 64 * 8 <= 4 * 64 * C::MREC * 4, "merge region fits");
+            const int mine = half * 4 + wq, theirs = (1 - half) * 4 + wq;
+            auto merge = [&](auto hf) __attribute__((always_inline)) {
+                constexpr int HF = decltype(hf)::value ? 1 : 0;   // this wave's key half
+                float a0 = 1.f, a1 = 0.f, inv = 0.f;
 #pragma unroll
-        for (int rd = 0; rd < C::ROUNDS; ++rd) {
-            if (half == 1) {
+                for (int rd = 0; rd < HB; ++rd) {
+                    const int send = (1 - HF) * HB + rd, fin = HF * HB + rd;
 #pragma unroll
-                for (int x = 0; x < C::MDB; ++x)
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const f32x4_t w = {acc[rd * C::MDB + x][4 * q4], acc[rd * C::MDB + x][4 * q4 + 1],
-                                           acc[rd * C::MDB + x][4 * q4 + 2], acc[rd * C::MDB + x][4 * q4 + 3]};
-                        *(f32x4_t*)(rec + 16 * x + 4 * q4) = w;
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        xs[(mine * 4 + q4) * 64 + lane] = (f32x4_t){acc[send][4 * q4], acc[send][4 * q4 + 1],
+                                                                    acc[send][4 * q4 + 2], acc[send][4 * q4 + 3]};
+                    if (rd == 0) mls[mine * 64 + lane] = (f32x2_t){m_ref, l_run};
+                    lds_barrier();
+                    if (rd == 0) {
+                        const f32x2_t ml = mls[theirs * 64 + lane];
+                        const float m0 = HF == 0 ? m_ref : ml[0], l0 = HF == 0 ? l_run : ml[1];
+                        const float m1 = HF == 0 ? ml[0] : m_ref, l1 = HF == 0 ? ml[1] : l_run;
+                        const float m = fmaxf(m0, m1);
+                        const float mu = (m == -INFINITY) ? 0.f : m;
+                        a0 = __builtin_amdgcn_exp2f(m0 - mu);
+                        a1 = __builtin_amdgcn_exp2f(m1 - mu);
+                        float l = __builtin_fmaf(a0, l0, a1 * l1);
+                        l += partner_lane(l);
+                        inv = l > 0.f ? 1.0f / l : 0.f;
+                        if (HF == 0 && lse && g == 0 && qi < S_q)
+                            lse[((size_t)b * H + h) * S_q + qi] =
+                                l > 0.f ? (mu + __builtin_log2f(l)) * 0.69314718055994531f : -INFINITY;
                     }
-                if (rd == 0) *(f32x2_t*)(rec + 16 * C::MDB) = (f32x2_t){m_ref, l_run};
-            }
-            lds_barrier();
-            if (half == 0) {
-                if (rd == 0) {
-                    const f32x2_t ml = *(const f32x2_t*)(rec + 16 * C::MDB);
-                    const float m1 = ml[0];
-                    const float l1 = ml[1];
-                    const float m = fmaxf(m_ref, m1);
-                    const float mu = (m == -INFINITY) ? 0.f : m;
-                    a0 = __builtin_amdgcn_exp2f(m_ref - mu);
-                    a1 = __builtin_amdgcn_exp2f(m1 - mu);
-                    // (both weighted sums are written as one explicit fma, so
-                    // every instantiation rounds them the same way)
-                    float l = __builtin_fmaf(a0, l_run, a1 * l1);
-                    l += partner_lane(l);
-                    // a row that sees no key (a cache entry shorter than the chunk) is 0
-                    inv = l > 0.f ? 1.0f / l : 0.f;
-                    // log of the softmax denominator in natural units: ln 2 * (m + log2 l)
-                    if (lse && g == 0 && qi < S_q)
-                        lse[((size_t)b * H + h) * S_q + qi] =
-                            l > 0.f ? (mu + __builtin_log2f(l)) * 0.69314718055994531f : -INFINITY;
-                }
-                f32x4_t part[C::MDB][4];
+                    f32x4_t part[4];
 #pragma unroll
-                for (int x = 0; x < C::MDB; ++x)
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) part[x][q4] = *(const f32x4_t*)(rec + 16 * x + 4 * q4);
-#pragma unroll
-                for (int x = 0; x < C::MDB; ++x) {
-                    const int db = rd * C::MDB + x;
+                    for (int q4 = 0; q4 < 4; ++q4) part[q4] = xs[(theirs * 4 + q4) * 64 + lane];
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
                         T ob[4];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            ob[e] = (T)(__builtin_fmaf(a0, acc[db][4 * q4 + e], a1 * part[x][q4][e]) * inv);
-                        // lane holds head dims 32*db + 8*q4 + 4*g .. +3 of its
-                        // query; rows past S_q fall outside the descriptor
+                        for (int e = 0; e < 4; ++e) {
+                            const float x0 = HF == 0 ? acc[fin][4 * q4 + e] : part[q4][e];
+                            const float x1 = HF == 0 ? part[q4][e] : acc[fin][4 * q4 + e];
+                            ob[e] = (T)(__builtin_fmaf(a0, x0, a1 * x1) * inv);
+                        }
                         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, ob), d_o,
-                                                              (unsigned)(qi * HD2 + (32 * db + 8 * q4 + 4 * g) * 2), 0, 0);
+                                                              (unsigned)(qi * HD2 + (32 * fin + 8 * q4 + 4 * g) * 2), 0, 0);
+                    }
+                    if (rd + 1 < HB) lds_barrier();   // the parts are rewritten by the next round
+                }
+            };
+            if (half == 0) merge(Flag<false>());
+            else merge(Flag<true>());
+        } else {
+            // ---- merge the two key halves (waves wq and wq+4) through LDS, in
+            // rounds of MDB accumulator blocks; half 0 writes the block's rows
+            float* rec = (float*)(lds + C::MERGE) + (wq * 64 + lane) * C::MREC;
+            float a0 = 1.f, a1 = 0.f, inv = 0.f;
+    #pragma unroll
+            for (int rd = 0; rd < C::ROUNDS; ++rd) {
+                if (half == 1) {
+    #pragma unroll
+                    for (int x = 0; x < C::MDB; ++x)
+    #pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            const f32x4_t w = {acc[rd * C::MDB + x][4 * q4], acc[rd * C::MDB + x][4 * q4 + 1],
+                                               acc[rd * C::MDB + x][4 * q4 + 2], acc[rd * C::MDB + x][4 * q4 + 3]};
+                            *(f32x4_t*)(rec + 16 * x + 4 * q4) = w;
+                        }
+                    if (rd == 0) *(f32x2_t*)(rec + 16 * C::MDB) = (f32x2_t){m_ref, l_run};
+                }
+                lds_barrier();
+                if (half == 0) {
+                    if (rd == 0) {
+                        const f32x2_t ml = *(const f32x2_t*)(rec + 16 * C::MDB);
+                        const float m1 = ml[0];
+                        const float l1 = ml[1];
+                        const float m = fmaxf(m_ref, m1);
+                        const float mu = (m == -INFINITY) ? 0.f : m;
+                        a0 = __builtin_amdgcn_exp2f(m_ref - mu);
+                        a1 = __builtin_amdgcn_exp2f(m1 - mu);
+                        // (both weighted sums are written as one explicit fma, so
+                        // every instantiation rounds them the same way)
+                        float l = __builtin_fmaf(a0, l_run, a1 * l1);
+                        l += partner_lane(l);
+                        // a row that sees no key (a cache entry shorter than the chunk) is 0
+                        inv = l > 0.f ? 1.0f / l : 0.f;
+                        // log of the softmax denominator in natural units: ln 2 * (m + log2 l)
+                        if (lse && g == 0 && qi < S_q)
+                            lse[((size_t)b * H + h) * S_q + qi] =
+                                l > 0.f ? (mu + __builtin_log2f(l)) * 0.69314718055994531f : -INFINITY;
+                    }
+                    f32x4_t part[C::MDB][4];
+    #pragma unroll
+                    for (int x = 0; x < C::MDB; ++x)
+    #pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4) part[x][q4] = *(const f32x4_t*)(rec + 16 * x + 4 * q4);
+    #pragma unroll
+                    for (int x = 0; x < C::MDB; ++x) {
+                        const int db = rd * C::MDB + x;
+    #pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            T ob[4];
+    #pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                ob[e] = (T)(__builtin_fmaf(a0, acc[db][4 * q4 + e], a1 * part[x][q4][e]) * inv);
+                            // lane holds head dims 32*db + 8*q4 + 4*g .. +3 of its
+                            // query; rows past S_q fall outside the descriptor
+                            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, ob), d_o,
+                                                                  (unsigned)(qi * HD2 + (32 * db + 8 * q4 + 4 * g) * 2), 0, 0);
+                        }
                     }
                 }
+                if (rd + 1 < C::ROUNDS) lds_barrier();   // the record is rewritten by the next round
             }
-            if (rd + 1 < C::ROUNDS) lds_barrier();   // the record is rewritten by the next round
         }
         j0 += nt;
     }

@@ -48,8 +48,10 @@ ATTN_HD inline int xcd_remap(int x, int n) {
 // items, waves and tiles as above, with K and V tiles loaded straight into a
 // ring of kPrefillStages LDS stages. K rows are padded by 16 bytes; V rows are
 // unpadded (their 16-byte chunks swizzled instead). The key-half merge goes
-// through its own region in rounds of prefill_merge_db(D) 32-row blocks of
-// the accumulator, one record of prefill_merge_rec_floats(D) floats per lane.
+// through its own region of 4 * 64 * prefill_merge_rec_floats(D) floats:
+// with D >= 64 each half sends its partner one 32-row block of the
+// accumulator per round (2 * 4 waves * 64 lanes * 16 floats) plus (m, l);
+// with D = 32 one record of 16 + 4 floats per lane of the key-half-1 waves.
 constexpr int kPrefillStages = 3;
 ATTN_HD constexpr int prefill_krow_bytes(int D) { return 2 * D + 16; }
 ATTN_HD constexpr int prefill_k_stage_bytes(int D) { return kTileN * (2 * D + 16); }
