@@ -403,8 +403,11 @@ def test_traffic_record_matches_the_current_build_and_goes_stale(monkeypatch, tm
     assert bench.measured_traffic("decode", str(edited)) is None
     # a code edit of plan.h (tile sizes, the decode split) changes every kernel's fingerprint
     plan = tmp_path / "plan.h"
-    plan.write_bytes(open(bench.KERNEL_HEADERS[0], "rb").read().replace(
-        b"constexpr int kDecodeBatch = 16;", b"constexpr int kDecodeBatch = 8;"))
+    text = open(bench.KERNEL_HEADERS[0], "rb").read()
+    edited_plan = re.sub(rb"constexpr int kDecodeBatch = (\d+);",
+                         lambda m: b"constexpr int kDecodeBatch = %d;" % (int(m.group(1)) + 2), text)
+    assert edited_plan != text
+    plan.write_bytes(edited_plan)
     headers = [str(plan)] + bench.KERNEL_HEADERS[1:]
     assert bench.build_sha256(bench.DECODE_SRC, headers) != bench.build_sha256(bench.DECODE_SRC)
     assert bench.build_sha256(bench.PREFILL_SRC, headers) != doc["prefill"]["build_sha256"]
