@@ -3,27 +3,31 @@
 // path.
 //
 // Work item: one workgroup of 8 waves. With the causal rule (or without it)
-// an item is two 128-query blocks of one (b, h), r and n-1-r, so every item
-// walks the same number of 64-key tiles; with per-entry cache lengths it is
-// one block. Wave w holds queries 32*(w%4) .. +31 of the block and key half
+// an item is two 128-query blocks of one (b, h), r and n-1-r (the smaller
+// one first), so every item walks the same number of 64-key tiles; with
+// per-entry cache lengths it is one block. Wave w holds queries 32*(w%4) .. +31 of the block and key half
 // w/4 of every tile; the two halves merge at the end of the block.
 //
 // The blocks of an item form ONE stream of key tiles, each block's tiles
-// walked from its diagonal down to tile 0. K and V tiles go from HBM
+// walked from tile 0 (or the first visible one) up to its diagonal: the
+// items of one head, which run on one XCD, start on the same tiles, so
+// those come from HBM once and from L2 for the rest (walking down from
+// each block's own diagonal, every item started on tiles of its own, and
+// the opening read all of them from HBM at once). K and V tiles go from HBM
 // straight into a ring of three LDS stages through the LDS path of the
 // buffer loads (no staging registers, no LDS store instructions), issued two
 // steps before their use; a step ends with one wait for the previous step's
 // loads and one barrier. The second block's Q and first tiles arrive during
 // the first block's last steps, so a block change costs only the merge.
 //
-// Step u of a block, tile t_u (the u-th from the top), key half of a wave:
+// Step u of a block, tile t_u (the u-th from the bottom), key half of a wave:
 //   matrix cores : O^T += V^T(t_{u-1}) . P(t_{u-1})^T   (one step late)
 //                  S^T(t_{u+1}) = K(t_{u+1}) . Q^T       (one step early)
 //   vector ALUs  : row max of S(t_u) with a lazy re-base, P(t_u) =
 //                  2^(S*c - m) rounded to the storage type, row sums of the
 //                  rounded P
 // so no MFMA of a step waits for that step's vector work. The steps whose
-// tile crosses the diagonal or the ragged key end (the first one or two of a
+// tile crosses the diagonal or the ragged key end (the last one or two of a
 // block) run a separate masked copy of the step; the remaining loop has no
 // branch but the rare re-base.
 //
@@ -339,9 +343,14 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
     const int b = bh / H, h = bh % H;
     const int S_kv = kv_lens ? min(max(kv_lens[b], 0), S_cap) : S_cap;   // valid keys of this entry
     const int off = S_kv - S_q;   // absolute position of query i is i + off (may be < 0)
-    const int qb_first = n_qblk - 1 - p;
-    const int nblk = (paired && p != qb_first) ? 2 : 1;
-    const int qbs[2] = {qb_first, p};
+    const int qb_big = n_qblk - 1 - p;   // the item's only block when unpaired
+    const int nblk = (paired && p != qb_big) ? 2 : 1;
+    // the smaller block first: every item of a head then starts on tile 0,
+    // and the larger blocks walk up behind one another (at most 14 tiles
+    // apart at S = 2048), so they still find their tiles in L2 (with the
+    // larger block first, the items that reached their smaller block last
+    // re-read its low tiles from HBM)
+    const int qbs[2] = {nblk == 2 ? p : qb_big, qb_big};
     // the entry's row of the key mask, and its address mod 4
     const uint8_t* const mrow = KMASK ? key_mask + (size_t)b * S_cap : nullptr;
     const int msh = (int)((unsigned long long)mrow & 3u);
@@ -411,8 +420,8 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
         vis_hi = __builtin_amdgcn_readfirstlane(hi_t);
     }
 
-    // tiles [lo, hi) of each block (walked from hi-1 down), and how many of
-    // the top ones cross the diagonal or the key end
+    // tiles [lo, hi) of each block (walked from lo up), and how many of the
+    // top ones cross the diagonal or the key end
     int hi_[2] = {0, 0}, lo_[2] = {0, 0}, nedge_[2] = {0, 0};
 #pragma unroll
     for (int ph = 0; ph < 2; ++ph) {
@@ -435,8 +444,8 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
     const int nt0 = hi_[0] - lo_[0];
     const int N = nt0 + hi_[1] - lo_[1];   // tiles in the item's stream
     auto stream_tile = [&](int j) __attribute__((always_inline)) {
-        if constexpr (KMASK) return j < nt0 ? hi_[0] - 1 - j : hi_[1] - 1 - (j - nt0);
-        return j < nt0 ? nt0 - 1 - j : hi_[1] - 1 - (j - nt0);
+        if constexpr (KMASK) return j < nt0 ? lo_[0] + j : lo_[1] + (j - nt0);
+        return j < nt0 ? j : j - nt0;
     };
 
     // ---- per-lane load offsets (loop-invariant; the tile moves the descriptor)
@@ -701,7 +710,7 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
                 for (int db = 0; db < C::DB; ++db) vaddr[db] = v_lane[db] + vs;
             }
             // (b) the diagonal and the key end: -inf past this lane's last key
-            const int kbase = (lo + nt - 1 - u) * kTileN + 32 * half;   // first key of this wave's half tile
+            const int kbase = (lo + u) * kTileN + 32 * half;   // first key of this wave's half tile
             // (key mask) the next tile's flag and V rows' mask bytes, read now
             // and used at the end of the step
             unsigned hw_next = 0u;
@@ -727,7 +736,7 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
                     const bool hide = (key > lane_key_limit) | (key >= S_kv) | (((mb[r >> 2] >> (8 * (r & 3))) & 0xFFu) == 0u);
                     s_c[r] = hide ? -INFINITY : s_c[r];
                 }
-            } else if (u < n_edge && ((causal && kbase + 31 > q0 + off) || (kbase + 32 > S_kv))) {
+            } else if (u >= nt - n_edge && ((causal && kbase + 31 > q0 + off) || (kbase + 32 > S_kv))) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = kbase + 16 * (r >> 3) + 8 * g + (r & 7);
@@ -1017,3 +1026,4 @@ hipError_t launch_fwd_prefill(const FwdArgs& a, Elt t, hipStream_t stream) {
 }
 
 }  // namespace attn
+
