@@ -238,6 +238,8 @@ DECODE_SEGMENTS = [
     (402, 300, 2, 8, 64, (-1, 4)),        # about 2 keys per sequence: ranges span many sequences
     (403, 1100, 2, 40, 32, (-2, 45)),     # beyond the LDS length scan
     (404, 3, 4, 3000, 128, (2500, 3000)), # long sequences: several ranges each
+    (405, 4, 2, 80, 32, (64, 70)),        # 257-280 keys: pair spans of 3 (2 for the even workgroup, 1 for the odd)
+    (406, 130, 2, 4, 64, (1, 3)),         # ~260 keys over many sequences, spans of 3 crossing sequences
 ]
 
 
