@@ -466,10 +466,10 @@ int attn_sinusoidal_pe(float* pe, int S, int d_model, int pos0) {
         return fail(ATTN_ERR_INVALID_ARG, "attn_sinusoidal_pe: positions pos0 + S exceed 2^31 - 1");
     if (tensor_bytes(S, d_model, 1, 1, 4) < 0)
         return fail(ATTN_ERR_INVALID_ARG, "attn_sinusoidal_pe: size overflows");
-    // launch grid: (S / kPeRows) x (d_model / 2 / kPeThreads) workgroups of kPeThreads
+    // launch grid: (S / kPeRows) x pe_grid_chunks(d_model) workgroups of kPeThreads
     if ((long long)(S + attn::kPeRows - 1) / attn::kPeRows * attn::kPeThreads > 0xffffffffLL)
         return fail(ATTN_ERR_UNSUPPORTED, "attn_sinusoidal_pe: S exceeds the launch grid");
-    if ((long long)(d_model / 2 + attn::kPeThreads - 1) / attn::kPeThreads > 65535)
+    if (attn::pe_grid_chunks(d_model) > 65535)
         return fail(ATTN_ERR_UNSUPPORTED, "attn_sinusoidal_pe: d_model exceeds the launch grid");
     if (S == 0) return ok();
     if (!pe) return fail(ATTN_ERR_INVALID_ARG, "attn_sinusoidal_pe: NULL output pointer");

@@ -222,11 +222,14 @@ constexpr int kGemmWavesM = 2;
 constexpr int kGemmWavesN = 4;
 constexpr int kGemmThreads = kGemmWavesM * kGemmWavesN * 64;
 
-// Sinusoidal position encoding: 256 threads over the frequency pairs, 4
-// positions per workgroup (a 4096-position table is 1,024 workgroups: 16
-// positions each left one wave per SIMD and the sin/cos latency exposed).
+// Sinusoidal position encoding: 256 threads, two frequency pairs each, and 4
+// positions per workgroup (a 4096 x 4096 table is 1,024 x 4 workgroups; 8 or
+// 16 positions per workgroup measured slower).
 constexpr int kPeThreads = 256;
 constexpr int kPeRows = 4;
+ATTN_HD inline long long pe_grid_chunks(int d_model) {
+    return ((long long)d_model / 2 + 2 * kPeThreads - 1) / (2 * kPeThreads);
+}
 
 // Masked softmax: one wave per row, kSmRowsPerBlock rows per workgroup. A
 // lane holds up to kSmChunksMax 16-byte chunks of its row in registers, so a

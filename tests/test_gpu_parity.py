@@ -759,6 +759,8 @@ PE_CASES = [  # (S, d_model, pos0)
     (300, 4096, 0),          # the model width of the bf16_s2048 layer
     (17, 128, 100_000),      # an offset block of positions (decode steps)
     (6, 8, (1 << 31) - 6),   # the largest positions the interface allows
+    (9, 6, 5),               # an odd number of pairs: the last thread has one
+    (5, 10, 3),              # rows not 16-byte aligned: 8-byte stores
 ]
 
 
@@ -782,6 +784,20 @@ def test_sinusoidal_pe_full_size(attn):
     bar = 3e-7 + 2.5e-16 * S
     err = float(np.abs(pe - ref).max())
     assert err <= bar, f"pe full size: max abs err {err:.3e} > {bar:.3e}"
+
+
+def test_sinusoidal_pe_output_aligned_to_8_bytes_only(attn):
+    """A d_model that allows 16-byte row stores, written into a buffer that
+    is only 8-byte aligned: the kernel takes its 8-byte store path."""
+    S, d = 7, 64
+    buf = torch.full((S * d + 2,), float("nan"), dtype=torch.float32, device="cuda")
+    view = buf[2:].view(S, d)
+    assert view.data_ptr() % 16 == 8
+    attn.sinusoidal_pe(S, d, 11, out=view)
+    torch.cuda.synchronize()
+    ref = oracle.sinusoidal_pe(S, d, 11)
+    assert float(np.abs(view.cpu().double().numpy() - ref).max()) <= 3e-7 + 2.5e-16 * (11 + S)
+    assert torch.isnan(buf[:2].cpu()).all()   # nothing written before the table
 
 
 def test_sinusoidal_pe_position_zero_is_exact(attn):
