@@ -512,6 +512,9 @@ MASK_CASES = [  # (B, H, S_q, S_kv, D, causal, pattern)
     (2, 1, 33, 513, 128, False, "random"),
     (2, 2, 300, 300, 64, True, "right_pad"),      # causal, paired blocks, trailing tiles skipped
     (3, 2, 300, 300, 128, True, "left_pad"),      # causal, leading tiles skipped
+    (2, 2, 200, 256, 64, True, "tile_pad"),       # visible keys end on a tile boundary
+    (2, 3, 150, 300, 128, False, "right_pad_hole"),   # right padding and one hidden key inside
+    (2, 2, 129, 300, 128, True, "right_pad_hole"),
 ]
 
 
@@ -522,6 +525,13 @@ def _make_mask(pattern, B, S_kv, seed):
     elif pattern == "right_pad":
         n = torch.randint(1, S_kv + 1, (B,), generator=g)
         m = torch.arange(S_kv)[None, :] < n[:, None]
+    elif pattern == "tile_pad":
+        n = 64 * torch.randint(1, S_kv // 64 + 1, (B,), generator=g)
+        m = torch.arange(S_kv)[None, :] < n[:, None]
+    elif pattern == "right_pad_hole":
+        n = torch.randint(2, S_kv + 1, (B,), generator=g)
+        m = torch.arange(S_kv)[None, :] < n[:, None]
+        m[torch.arange(B), n // 2] = False
     elif pattern == "left_pad":
         n = torch.randint(0, S_kv, (B,), generator=g)
         m = torch.arange(S_kv)[None, :] >= n[:, None]
@@ -551,9 +561,9 @@ def test_key_mask_against_oracle(attn, case, dtype):
 
 @pytest.mark.parametrize("dtype", ALL_DTYPES, ids=DTYPE_IDS)
 def test_key_mask_absent_or_all_visible_is_attn_fwd(attn, dtype):
-    """No mask is the attn_fwd kernel itself, and an all-visible mask runs the
-    key-mask instantiation of the same kernel, which takes the same steps in
-    the same order: both bitwise equal to attn_fwd."""
+    """No mask is the attn_fwd kernel itself, and an all-visible mask hides no
+    key, so the key-mask instantiation runs the same unmasked steps in the
+    same order: both bitwise equal to attn_fwd."""
     for D in (128, 64, 32):
         q, k, v = (t.cuda() for t in workloads.make_prefill_shape(610 + D, dtype, 2, 3, 300, 300, D))
         for causal in (True, False):
@@ -562,6 +572,23 @@ def test_key_mask_absent_or_all_visible_is_attn_fwd(attn, dtype):
             o2 = attn.attn_fwd_mask(q, k, v, torch.ones(2, 300, dtype=torch.bool, device="cuda"), causal=causal)
             assert torch.equal(o1, ref)
             assert torch.equal(o2, ref), f"all-visible mask D={D} causal={causal}"
+
+
+@pytest.mark.parametrize("dtype", ALL_DTYPES, ids=DTYPE_IDS)
+def test_key_mask_right_padding_is_a_key_length(attn, dtype):
+    """A mask that hides only a suffix of each entry is that entry's key
+    length: without the causal rule the result is bitwise that of
+    attn_fwd_kvcache with the same lengths (the same steps over keys [0, n)),
+    whatever the padding slots hold."""
+    B, H, S, D = 3, 2, 300, 128
+    q, k, v = workloads.make_prefill_shape(670, dtype, B, H, S, S, D)
+    n = torch.tensor([300, 1, 193], dtype=torch.int32)
+    m = torch.arange(S)[None, :] < n[:, None].long()
+    kp, vp = _poison_hidden(k, m), _poison_hidden(v, m)
+    o, lse = attn.attn_fwd_mask(q.cuda(), kp.cuda(), vp.cuda(), m.cuda(), causal=False, return_lse=True)
+    ok, lsek = attn.attn_fwd_kvcache(q.cuda(), kp.cuda(), vp.cuda(), n.cuda(), causal=False, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ok) and torch.equal(lse, lsek)
 
 
 NAN_PAD_CASES = [  # (B, H, S_q, S_kv, D, causal, pattern)
