@@ -247,8 +247,8 @@ __device__ __forceinline__ float partner_lane(float x) {
     return __builtin_bit_cast(float, (__lane_id() < 32) ? hi : lo);
 }
 
-// Entries whose lengths are ranked in LDS (2 ints each); above this the
-// longest-first order is skipped.
+// Entries, or (entry, block) classes, ranked in LDS (2 ints each); above
+// this the classes fall back to entries, and the entries to launch order.
 constexpr int kMaxRankedEntries = 256;
 static_assert(2 * kMaxRankedEntries * sizeof(int) <= prefill_lds_bytes(32), "rank table fits in LDS");
 
@@ -325,21 +325,50 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
         bh = item / items_per_bh;
         p = item % items_per_bh;
     } else {
-        // entries differ in length: the longest run first (ranked in LDS)
-        kv_order(blockIdx.x, gridDim.x, items_per_bh, bh, p);
-        if (B <= kMaxRankedEntries) {
-            int* lens = (int*)lds;
-            int* perm = lens + kMaxRankedEntries;
-            for (int e = tid; e < B; e += kTileThreads) lens[e] = min(max(kv_lens[e], 0), S_cap);
-            __syncthreads();
-            for (int e = tid; e < B; e += kTileThreads) {
-                int rank = 0;
-                for (int f = 0; f < B; ++f) rank += (lens[f] > lens[e]) || (lens[f] == lens[e] && f < e);
-                perm[rank] = e;
+        // entries differ in length, and the blocks of an entry in the tiles
+        // they walk: the (entry, block) classes run costliest first, ranked
+        // in LDS by their tile counts. Workgroups are dispatched in launch
+        // order, so a workgroup waits for the one before it to be placed:
+        // with costs that only fall, a CU that frees up finds the next item
+        // ready. The H heads of a class are consecutive workgroups, so head h
+        // of every class runs on XCD h % 8 (H a multiple of 8) and shares that
+        // head's K and V in one L2.
+        const int G = items_per_bh;
+        if (B * G <= kMaxRankedEntries && (long long)B * H * G == (long long)gridDim.x) {
+            int* cost = (int*)lds;
+            int* perm = cost + kMaxRankedEntries;
+            for (int c = tid; c < B * G; c += kTileThreads) {
+                const int len = min(max(kv_lens[c / G], 0), S_cap);
+                cost[c] = tiles_for_block(n_qblk - 1 - c % G, S_q, len, causal);
             }
             __syncthreads();
-            bh = perm[bh / H] * H + bh % H;
+            for (int c = tid; c < B * G; c += kTileThreads) {
+                int rank = 0;
+                for (int f = 0; f < B * G; ++f) rank += (cost[f] > cost[c]) || (cost[f] == cost[c] && f < c);
+                perm[rank] = c;
+            }
+            __syncthreads();
+            const int cls = perm[blockIdx.x / H];
+            bh = (cls / G) * H + blockIdx.x % H;
+            p = cls % G;
             __syncthreads();   // the table's LDS is reused by the first stages
+        } else {
+            // many entries: the longest entries first, their heads spread
+            kv_order(blockIdx.x, gridDim.x, items_per_bh, bh, p);
+            if (B <= kMaxRankedEntries) {
+                int* lens = (int*)lds;
+                int* perm = lens + kMaxRankedEntries;
+                for (int e = tid; e < B; e += kTileThreads) lens[e] = min(max(kv_lens[e], 0), S_cap);
+                __syncthreads();
+                for (int e = tid; e < B; e += kTileThreads) {
+                    int rank = 0;
+                    for (int f = 0; f < B; ++f) rank += (lens[f] > lens[e]) || (lens[f] == lens[e] && f < e);
+                    perm[rank] = e;
+                }
+                __syncthreads();
+                bh = perm[bh / H] * H + bh % H;
+                __syncthreads();   // the table's LDS is reused by the first stages
+            }
         }
     }
     const int b = bh / H, h = bh % H;

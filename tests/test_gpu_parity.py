@@ -488,6 +488,23 @@ def test_kvcache_edge_cases(attn, case, dtype):
 
 
 @pytest.mark.parametrize("dtype", ALL_DTYPES, ids=DTYPE_IDS)
+@pytest.mark.parametrize("B,H,S_q", [(70, 3, 200), (130, 1, 300)], ids=["140_classes", "390_classes"])
+def test_kvcache_many_entries(attn, B, H, S_q, dtype):
+    """Many entries: up to 256 (entry, block) classes are ranked by cost in
+    LDS, beyond that the entries keep the launch order; both orders place
+    every item once. H = 3 and 1 are not multiples of the 8 XCDs."""
+    S_cap, D = 320, 64
+    say(f"kvcache many entries B={B} H={H} S_q={S_q} {dtype}")
+    cfg = workloads.KVCachePrefill("many", dtype, B, H, S_q, S_cap, D, 450 + B, 1, S_cap, True)
+    lens = [int(x) for x in torch.randint(0, S_cap + 1, (B,), generator=torch.Generator().manual_seed(B))]
+    sl, q, kc, vc = workloads.make_kvcache_prefill(cfg, nan_fill=True, seqlens=lens)
+    o, lse = attn.attn_fwd_kvcache(q.cuda(), kc.cuda(), vc.cuda(), sl.cuda(), causal=True, return_lse=True)
+    ro, rlse = oracle.attn_fwd_kvcache(q, kc, vc, sl.numpy(), causal=True)
+    check(o, ro, dtype, f"kvcache many entries B={B}")
+    check_lse(lse, rlse, dtype, f"kvcache many entries B={B}")
+
+
+@pytest.mark.parametrize("dtype", ALL_DTYPES, ids=DTYPE_IDS)
 def test_kvcache_without_lengths_is_attn_fwd_bitwise(attn, dtype):
     q, k, v = workloads.make_prefill_shape(500, dtype, 2, 4, 200, 333, 128)
     q, k, v = q.cuda(), k.cuda(), v.cuda()
