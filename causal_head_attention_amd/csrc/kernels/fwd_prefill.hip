@@ -970,12 +970,12 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
                 // rounds of MDB accumulator blocks; half 0 writes the block's rows
                 float* rec = (float*)(lds + C::MERGE) + (wq * 64 + lane) * C::MREC;
                 float a0 = 1.f, a1 = 0.f, inv = 0.f;
-        #pragma unroll
+#pragma unroll
                 for (int rd = 0; rd < C::ROUNDS; ++rd) {
                     if (half == 1) {
-        #pragma unroll
+#pragma unroll
                         for (int x = 0; x < C::MDB; ++x)
-        #pragma unroll
+#pragma unroll
                             for (int q4 = 0; q4 < 4; ++q4) {
                                 const f32x4_t w = {acc[rd * C::MDB + x][4 * q4], acc[rd * C::MDB + x][4 * q4 + 1],
                                                    acc[rd * C::MDB + x][4 * q4 + 2], acc[rd * C::MDB + x][4 * q4 + 3]};
@@ -1005,17 +1005,17 @@ __global__ __launch_bounds__(kTileThreads) void prefill_kernel(
                                     l > 0.f ? (mu + __builtin_log2f(l)) * 0.69314718055994531f : -INFINITY;
                         }
                         f32x4_t part[C::MDB][4];
-        #pragma unroll
+#pragma unroll
                         for (int x = 0; x < C::MDB; ++x)
-        #pragma unroll
+#pragma unroll
                             for (int q4 = 0; q4 < 4; ++q4) part[x][q4] = *(const f32x4_t*)(rec + 16 * x + 4 * q4);
-        #pragma unroll
+#pragma unroll
                         for (int x = 0; x < C::MDB; ++x) {
                             const int db = rd * C::MDB + x;
-        #pragma unroll
+#pragma unroll
                             for (int q4 = 0; q4 < 4; ++q4) {
                                 T ob[4];
-        #pragma unroll
+#pragma unroll
                                 for (int e = 0; e < 4; ++e)
                                     ob[e] = (T)(__builtin_fmaf(a0, acc[db][4 * q4 + e], a1 * part[x][q4][e]) * inv);
                                 // lane holds head dims 32*db + 8*q4 + 4*g .. +3 of its
