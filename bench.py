@@ -26,6 +26,7 @@ import json
 import os
 import statistics
 import sys
+import subprocess
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -209,6 +210,9 @@ def main() -> int:
                     help="leave out the KV-cache, fp16, key-padding and Q/K/V projection measurements")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one device copy of MIB MiB (reference for HBM counters)")
+    ap.add_argument("--perf-log", default=None, metavar="PATH",
+                    help="append one JSON line per measured leg (workload, kernel, revision, median/p95, "
+                         "rate, fraction of roofline, parity) to PATH")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -588,7 +592,58 @@ def main() -> int:
         "parity": parity,
     }
     print(json.dumps(line), flush=True)
+    if args.perf_log:
+        append_perf_log(args.perf_log, line)
     return 0
+
+
+def _git_rev():
+    """The source revision: ATTN_GIT_REV if set (a copy of the tree without
+    its history), else `git rev-parse HEAD`, else None."""
+    rev = os.environ.get("ATTN_GIT_REV")
+    if rev:
+        return rev
+    try:
+        r = subprocess.run(["git", "rev-parse", "HEAD"], capture_output=True, text=True, cwd=ROOT, timeout=10)
+        return (r.stdout.strip() or None) if r.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        return None
+
+
+def perf_log_records(line: dict) -> list:
+    """One record per measured leg of a bench line: the per-version table of
+    timings (P50 and P95, rate, fraction of the roofline) keyed by workload,
+    kernel and source revision, so runs of different revisions line up."""
+    common = {"rev": _git_rev(), "utc": time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime()),
+              "build": {"prefill": build_sha256(PREFILL_SRC)[:16], "decode": build_sha256(DECODE_SRC)[:16]},
+              "algo": os.environ.get("ATTN_ALGO", "auto")}
+    cpu = line.get("cpu_baseline") or {}
+    parity = line.get("parity") or {}
+    roof = line["roofline"]
+    recs = [dict(common, leg="prefill", workload=line["config"]["workload"].split(" + ")[0],
+                 kernel=roof["kernel"], value=line["value"], unit=line["unit"], frac=roof["frac"],
+                 median_us=roof["median_launch_us"], p95_us=roof["p95_launch_us"],
+                 clock_ghz=roof.get("clock_ghz"), max_abs=parity.get("prefill_max_abs"),
+                 rel_l2=parity.get("prefill_rel_l2"),
+                 oracle_tflops=cpu.get("value"), host_cores=cpu.get("cores"))]
+    dr = line["decode"]["roofline"]
+    recs.append(dict(common, leg="decode", workload=line["config"]["workload"].split(" + ")[-1],
+                     kernel="decode_kernel<bf16,128>", value=line["decode"]["value"], unit="GB/s",
+                     frac=dr["frac"], median_us=dr["median_call_us"], p95_us=dr["p95_call_us"],
+                     max_abs=parity.get("decode_max_abs")))
+    for key, leg in line.items():
+        if isinstance(leg, dict) and "roofline" in leg and key != "decode" and "workload" in leg:
+            r = leg["roofline"]
+            recs.append(dict(common, leg=key, workload=leg["workload"], kernel=r.get("kernel"),
+                             value=leg["value"], unit=leg["unit"], frac=r.get("frac"),
+                             median_us=r.get("median_launch_us"), p95_us=r.get("p95_launch_us")))
+    return recs
+
+
+def append_perf_log(path: str, line: dict) -> None:
+    with open(path, "a") as f:
+        for rec in perf_log_records(line):
+            f.write(json.dumps(rec) + "\n")
 
 
 if __name__ == "__main__":

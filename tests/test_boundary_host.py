@@ -420,3 +420,28 @@ def test_clock_probe_arming():
     assert L.attn_set_clock_probe(A + 8) == attn.ATTN_OK
     assert L.attn_set_clock_probe(A + 4) == attn.ATTN_ERR_INVALID_ARG
     assert L.attn_set_clock_probe(None) == attn.ATTN_OK   # disarm: no call below may write through it
+
+
+def test_perf_log_has_one_record_per_leg(monkeypatch, tmp_path):
+    """bench.py --perf-log appends one JSON line per measured leg, keyed by
+    workload, kernel, source revision and kernel build, with P50/P95 and the
+    fraction of the roofline (the per-version timing table)."""
+    import json
+    bench = _bench_module()
+    monkeypatch.setenv("ATTN_GIT_REV", "0123abcd")
+    roof = {"kernel": "prefill_kernel<bf16,128>", "frac": 0.25, "median_launch_us": 56.0, "p95_launch_us": 58.0}
+    line = {"value": 613.9, "unit": "TFLOPS", "roofline": roof,
+            "config": {"workload": "bf16 causal prefill S=2048 + bf16 decode B=16"},
+            "decode": {"value": 5600.0, "roofline": {"frac": 0.7, "median_call_us": 71.0, "p95_call_us": 73.0}},
+            "fp16_prefill": {"value": 540.0, "unit": "TFLOPS", "workload": "fp16 causal prefill",
+                             "roofline": {"frac": 0.21, "median_launch_us": 64.0}},
+            "cpu_baseline": {"value": 0.04, "cores": 16}, "parity": {"prefill_max_abs": 8e-3}}
+    path = tmp_path / "perf.jsonl"
+    bench.append_perf_log(str(path), line)
+    bench.append_perf_log(str(path), line)
+    recs = [json.loads(x) for x in path.read_text().splitlines()]
+    assert [r["leg"] for r in recs] == ["prefill", "decode", "fp16_prefill"] * 2
+    assert all(r["rev"] == "0123abcd" and len(r["build"]["prefill"]) == 16 for r in recs)
+    assert recs[0]["median_us"] == 56.0 and recs[0]["p95_us"] == 58.0 and recs[0]["max_abs"] == 8e-3
+    assert recs[1]["workload"] == "bf16 decode B=16" and recs[1]["frac"] == 0.7
+    assert recs[2]["value"] == 540.0 and recs[2]["median_us"] == 64.0
